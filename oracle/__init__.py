@@ -1,0 +1,141 @@
+"""CPU oracle for the exact attention forward pass (float64).
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's
+CPU-baseline leg import this package. The product path (the HIP library and
+its binding) never imports, links or runs it, and shares no code with it.
+
+`attention()` decodes the stored inputs exactly to float64 (float16, bfloat16
+and E4M3FN values are all exactly representable; an e4m3 value is then
+multiplied by its fp32 descale in float64, which is exact too), then calls the
+plain C implementation in oracle.c of softmax(scale * Q K^T) V and the
+per-row log-sum-exp, with each softmax row materialised.
+
+Parity pins: tests/test_oracle_pins.py (closed forms, invariants, brute force
+at 50 significant digits, an independent library routine, planted mistakes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(out: str = _LIB, src: str = _SRC, extra=()) -> str:
+    """Compile oracle.c with gcc into a shared library."""
+    cmd = ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", *extra, "-o", out + ".tmp", src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load(path: str = _LIB):
+    lib = ctypes.CDLL(path)
+    fn = lib.oracle_attn_fwd
+    P = ctypes.c_void_p
+    L = ctypes.c_long
+    fn.argtypes = [P, P, P, P, P, L, L, L, L, L, ctypes.c_double, ctypes.c_int, L, P, L, ctypes.c_int]
+    fn.restype = ctypes.c_int
+    return lib
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = load()
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def decode(x: torch.Tensor, descale: float = 1.0) -> torch.Tensor:
+    """Exact float64 value of each stored element, times its descale."""
+    y = x.detach().to("cpu").to(torch.float64)
+    if descale != 1.0:
+        y = y * float(descale)
+    return y.contiguous()
+
+
+def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
+              rows=None, threads=None, lib=None):
+    """float64 O and LSE of softmax(scale * Q K^T) V.
+
+    q [B,H,Nq,D], k and v [B,H,Nk,D] (CPU or device tensors of any float dtype).
+    scale is used as float64(fp32(scale)) -- the fp32 value the kernel gets.
+    rows: None for every row (O [B,H,Nq,D], LSE [B,H,Nq]); otherwise an
+    iterable of flattened row ids (b*H + h)*Nq + i (O [n,D], LSE [n]).
+    """
+    lib = lib or _get()
+    threads = threads or default_threads()
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    scale64 = float(torch.tensor(scale, dtype=torch.float32))
+    if rows is None:
+        Q = decode(q, descales[0])
+        K = decode(k, descales[1])
+        V = decode(v, descales[2])
+        O = torch.empty((B, H, Nq, D), dtype=torch.float64)
+        LSE = torch.empty((B, H, Nq), dtype=torch.float64)
+        rc = lib.oracle_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), LSE.data_ptr(),
+                                 B, H, Nq, Nk, D, scale64, int(bool(causal)), int(window), None, 0, threads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_attn_fwd returned {rc}")
+        return O, LSE
+    # Sampled rows: decode one head at a time so full-size workloads fit.
+    rows = torch.as_tensor(list(rows) if not torch.is_tensor(rows) else rows, dtype=torch.int64)
+    O = torch.empty((rows.numel(), D), dtype=torch.float64)
+    LSE = torch.empty((rows.numel(),), dtype=torch.float64)
+    bh_of = rows // Nq
+    for bh in torch.unique(bh_of).tolist():
+        sel = (bh_of == bh).nonzero().flatten()
+        b, h = divmod(bh, H)
+        Q = decode(q[b, h], descales[0])
+        K = decode(k[b, h], descales[1])
+        V = decode(v[b, h], descales[2])
+        local = (rows[sel] % Nq).contiguous()
+        Oh = torch.empty((sel.numel(), D), dtype=torch.float64)
+        Lh = torch.empty((sel.numel(),), dtype=torch.float64)
+        rc = lib.oracle_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), Oh.data_ptr(), Lh.data_ptr(),
+                                 1, 1, Nq, Nk, D, scale64, int(bool(causal)), int(window),
+                                 local.data_ptr(), local.numel(), threads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_attn_fwd returned {rc}")
+        O[sel] = Oh
+        LSE[sel] = Lh
+    return O, LSE
+
+
+def visible_keys(i: int, Nq: int, Nk: int, causal: bool, window: int):
+    """[lo, hi) of the keys query row i sees (bottom-right causal alignment)."""
+    ip = i + (Nk - Nq)
+    lo, hi = 0, Nk
+    if causal:
+        hi = min(Nk, ip + 1)
+    if window > 0:
+        lo = max(0, ip - window + 1)
+    hi = max(hi, 0)
+    lo = min(lo, hi)
+    return lo, hi
+
+
+def pair_count(Nq: int, Nk: int, causal: bool, window: int) -> int:
+    """Number of (query, key) pairs the mask keeps, per (b, h)."""
+    total = 0
+    for i in range(Nq):
+        lo, hi = visible_keys(i, Nq, Nk, causal, window)
+        total += hi - lo
+    return total

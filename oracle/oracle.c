@@ -1,0 +1,160 @@
+/*
+ * CPU oracle for the exact attention forward pass. TEST INFRASTRUCTURE ONLY:
+ * the tests, the smoke check and the benchmark's CPU-baseline leg call it; the
+ * HIP library never does, and the two share no code.
+ *
+ * What it computes is the plain definition of scaled dot-product attention,
+ * Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V (aiinarabic.com
+ * "flash-attention" page, equation (1); inskillml course module 9, "Where n^2
+ * comes from"), written out in float64 with every softmax row materialised,
+ * i.e. the standard (unfused) attention the pages contrast the fused kernel
+ * with (aiinarabic.com page, Figure 3: S is formed, then softmax, then the
+ * product with V). The fused method reaches this same result up to rounding
+ * (inskillml module 9, "FlashAttention: compute without writing the
+ * weights": it is not an approximation).
+ *
+ * Per query row i of head (b, h):
+ *   i' = i + (Nk - Nq)                       (bottom-right causal alignment)
+ *   J  = { j < Nk : (!causal || j <= i') && (window == 0 || j > i' - window) }
+ *   s_j = scale * sum_d Q[i,d] K[j,d]        for j in J only
+ *   m = max_j s_j;  e_j = exp(s_j - m);  l = sum_j e_j
+ *   P_j = e_j / l                             (the materialised softmax row)
+ *   O[i,d] = sum_j P_j V[j,d];  LSE[i] = m + ln(l)
+ * An empty J gives O[i,:] = 0 and LSE[i] = -inf.
+ * The causal mask follows the SDPA call with is_causal=True in the inskillml
+ * module; the window keeps the w keys i-w < j <= i (a causal sliding window;
+ * the same module's "Sparse patterns" section names sliding windows).
+ *
+ * Inputs are float64 arrays the caller decoded exactly from the storage
+ * dtype. Layout: Q [B,H,Nq,D], K and V [B,H,Nk,D], contiguous.
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    const double *q, *k, *v;
+    double *o, *lse;
+    long B, H, Nq, Nk, D, window;
+    double scale;
+    int causal;
+    const long *rows;   /* flattened (b*H + h)*Nq + i, or NULL for every row */
+    long nrows;
+    long next;          /* work counter, shared */
+    pthread_mutex_t lock;
+    int bad;            /* set if a softmax row failed to sum to one */
+} job_t;
+
+/* One query row, following the definition above step by step. */
+static int one_row(const job_t *jb, long flat, double *s, double *o_row, double *lse_out)
+{
+    const long D = jb->D, Nq = jb->Nq, Nk = jb->Nk;
+    const long bh = flat / Nq, i = flat % Nq;
+    const double *qi = jb->q + flat * D;
+    const double *K = jb->k + bh * Nk * D;
+    const double *V = jb->v + bh * Nk * D;
+    const long ip = i + (Nk - Nq);
+
+    /* Visible keys J_i: j in [lo, hi). */
+    long lo = 0, hi = Nk;
+    if (jb->causal) hi = ip + 1 < Nk ? ip + 1 : Nk;
+    if (jb->window > 0) lo = ip - jb->window + 1 > 0 ? ip - jb->window + 1 : 0;
+    if (hi < 0) hi = 0;
+    if (lo > hi) lo = hi;
+
+    for (long d = 0; d < D; ++d) o_row[d] = 0.0;
+    if (hi == lo) {
+        *lse_out = -INFINITY;
+        return 0;
+    }
+
+    /* Scores s_j = scale * q_i . k_j */
+    for (long j = lo; j < hi; ++j) {
+        const double *kj = K + j * D;
+        double dot = 0.0;
+        for (long d = 0; d < D; ++d) dot += qi[d] * kj[d];
+        s[j - lo] = jb->scale * dot;
+    }
+    /* Softmax of the row: max, exponentials, sum, normalise. */
+    double m = s[0];
+    for (long j = 1; j < hi - lo; ++j) if (s[j] > m) m = s[j];
+    double l = 0.0;
+    for (long j = 0; j < hi - lo; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    double psum = 0.0;
+    for (long j = 0; j < hi - lo; ++j) {
+        s[j] = s[j] / l;
+        psum += s[j];
+    }
+    /* P times V */
+    for (long j = lo; j < hi; ++j) {
+        const double p = s[j - lo];
+        const double *vj = V + j * D;
+        for (long d = 0; d < D; ++d) o_row[d] += p * vj[d];
+    }
+    *lse_out = m + log(l);
+    return fabs(psum - 1.0) <= 1e-12 ? 0 : 1;
+}
+
+static void *worker(void *arg)
+{
+    job_t *jb = (job_t *)arg;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(jb->Nk > 0 ? jb->Nk : 1));
+    int bad = 0;
+    const long total = jb->rows ? jb->nrows : jb->B * jb->H * jb->Nq;
+    const long grab = 16;
+    for (;;) {
+        pthread_mutex_lock(&jb->lock);
+        long r0 = jb->next;
+        jb->next += grab;
+        pthread_mutex_unlock(&jb->lock);
+        if (r0 >= total) break;
+        long r1 = r0 + grab < total ? r0 + grab : total;
+        for (long r = r0; r < r1; ++r) {
+            long flat = jb->rows ? jb->rows[r] : r;
+            bad |= one_row(jb, flat, s, jb->o + r * jb->D, jb->lse + r);
+        }
+    }
+    free(s);
+    if (bad) {
+        pthread_mutex_lock(&jb->lock);
+        jb->bad = 1;
+        pthread_mutex_unlock(&jb->lock);
+    }
+    return NULL;
+}
+
+/*
+ * Computes O and LSE for the requested rows.
+ *   rows == NULL: every row; o is [B,H,Nq,D] and lse [B,H,Nq].
+ *   rows != NULL: nrows flattened row ids; o is [nrows,D] and lse [nrows].
+ * Returns 0 on success, 1 if some softmax row failed the sum-to-one check,
+ * -1 on bad arguments.
+ */
+int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o, double *lse,
+                    long B, long H, long Nq, long Nk, long D, double scale, int causal,
+                    long window, const long *rows, long nrows, int nthreads)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D <= 0 || window < 0 || nthreads <= 0) return -1;
+    job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.q = q; jb.k = k; jb.v = v; jb.o = o; jb.lse = lse;
+    jb.B = B; jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.D = D;
+    jb.window = window; jb.scale = scale; jb.causal = causal;
+    jb.rows = rows; jb.nrows = nrows;
+    pthread_mutex_init(&jb.lock, NULL);
+    if (nthreads > 256) nthreads = 256;
+    pthread_t tid[256];
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&tid[started], NULL, worker, &jb) == 0) ++started;
+    worker(&jb);
+    for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
+    pthread_mutex_destroy(&jb.lock);
+    return jb.bad ? 1 : 0;
+}
