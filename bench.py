@@ -1,0 +1,184 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+Default workload: causal self-attention forward, B=4 H=12 N=8192 D=64, bf16
+inputs and output, fp32 LSE -- the worked shape of the pages (inskillml course
+module 9). A step is one fa_fwd call over the whole batch, inputs resident in
+HBM. Prints one JSON line:
+
+  value      algorithmic TFLOP/s = 4*D*B*H*(visible query-key pairs) / time
+             (two products of 2*D flops per visible pair: Q K^T and P V)
+  roofline   the kernel against the dense bf16 MFMA peak (2516.6 TFLOP/s =
+             256 CU x 2.4 GHz x 4096 flop/CU/clk), timed with HIP events on
+             the launch stream; traffic = HBM bytes per launch from rocprofv3
+             FETCH_SIZE/WRITE_SIZE counters (profiles/), when the kernel source
+             is the one those counters were taken on
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same
+             workload's rows, on this host's cores (reported, not a target)
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}
+HBM_PEAK_GBS = 8000.0
+METRIC = "attention fwd TFLOPS + % MFMA peak, B4 H12 N8192 D64 causal bf16"
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_02_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def visible_pairs(Nq, Nk, causal, window):
+    """Visible (query, key) pairs per (batch, head)."""
+    import numpy as np
+    i = np.arange(Nq, dtype=np.int64) + (Nk - Nq)
+    hi = np.minimum(i + 1, Nk) if causal else np.full(Nq, Nk, dtype=np.int64)
+    lo = np.maximum(i - window + 1, 0) if window > 0 else np.zeros(Nq, dtype=np.int64)
+    return int(np.clip(hi - lo, 0, None).sum())
+
+
+def flops(w):
+    return 4.0 * w.D * w.B * w.H * visible_pairs(w.Nq, w.Nk, w.causal, w.window)
+
+
+def algorithmic_bytes(w):
+    eb = {"f16": 2, "bf16": 2, "e4m3": 1}[w.in_dtype]
+    ob = {"f32": 4, "f16": 2, "bf16": 2}[w.out_dtype]
+    n_bh = w.B * w.H
+    return n_bh * (w.Nq * w.D * eb + 2 * w.Nk * w.D * eb + w.Nq * w.D * ob + w.Nq * 4)
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for name in ("fa_fwd.hip", "fa_sched.h", "fa_launch.h"):
+        with open(os.path.join(ROOT, "exact_attention_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload_name):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload_name)
+    if not e or e.get("kernel_sha") != kernel_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, target_s=15.0):
+    """The oracle, as it is, on random rows of the workload, scaled to TFLOP/s."""
+    import torch
+    import oracle
+    threads = oracle.default_threads()
+    g = torch.Generator().manual_seed(1234)
+    n_rows_total = w.B * w.H * w.Nq
+
+    def row_pairs(rows):
+        i = rows % w.Nq + (w.Nk - w.Nq)
+        hi = torch.clamp(i + 1, max=w.Nk) if w.causal else torch.full_like(i, w.Nk)
+        lo = torch.clamp(i - w.window + 1, min=0) if w.window > 0 else torch.zeros_like(i)
+        return int(torch.clamp(hi - lo, min=0).sum())
+
+    n = 256
+    while True:
+        rows = torch.randint(0, n_rows_total, (n,), generator=g)
+        t0 = time.perf_counter()
+        oracle.attention(inp.q, inp.k, inp.v, w.scale, w.causal, w.window,
+                         descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or n >= n_rows_total:
+            fl = 4.0 * w.D * row_pairs(rows)
+            return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+                    "sample": f"{n} random query rows of the workload ({fl / 1e9:.1f} GFLOP), float64, "
+                              f"{dt:.1f} s wall"}
+        n = min(n_rows_total, max(2 * n, int(n * target_s / max(dt, 1e-3))))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(head-parallel sharding across GPUs is described, not built)"}))
+        sys.exit(2)
+
+    import torch
+    import exact_attention_02_amd as fa
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    out_t = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.out_dtype]
+    o = torch.empty((w.B, w.H, w.Nq, w.D), dtype=out_t, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    descales = (inp.descale_q, inp.descale_k, inp.descale_v) if w.in_dtype == "e4m3" else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window, out=o, lse=lse,
+                     descales=descales, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    fl = flops(w)
+    tflops = fl / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.in_dtype]
+    res = {
+        "metric": METRIC if args.workload == "c3" else f"attention fwd TFLOPS, {w.name}",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
+                   "causal": w.causal, "window": w.window, "in": w.in_dtype, "out": w.out_dtype,
+                   "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic_for(w.name),
+                     "kernel": "fa_fwd_kernel", "flop_per_launch": fl,
+                     "algorithmic_hbm_bytes": algorithmic_bytes(w),
+                     "timing": "HIP events on the launch stream, mean over the timed steps"},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+"""Python binding of libfa.so, the gfx950 fused exact-attention forward.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI in include/fa.h. The functions fa_fwd, fa_fwd_fp8 and
+fa_status_str carry the C names and arguments (device pointers as ints, the
+stream as an int handle). `attention()` is a convenience wrapper that takes
+torch tensors on a ROCm device, allocates the outputs with torch and calls
+fa_fwd / fa_fwd_fp8 on torch's current stream.
+
+There is no fallback: if libfa.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+# Mirrors of the enums in include/fa.h.
+FA_F16, FA_BF16, FA_F16_F32OUT, FA_E4M3, FA_BF16_F32OUT = 1, 2, 3, 4, 5
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE = 0, 1, 2, 3, 4
+FA_ERR_MASK, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_DEVICE, FA_ERR_LAUNCH = 5, 6, 7, 8, 9
+
+EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({fa_status_str(status)})")
+
+
+def load(path: str = LIB_PATH):
+    """Loads libfa.so and declares the C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(path)
+    P, I, F, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
+    pI, pLL = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_longlong)
+    lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P]
+    lib.fa_fwd.restype = I
+    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, F, F, F]
+    lib.fa_fwd_fp8.restype = I
+    lib.fa_status_str.argtypes = [I]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_plan_grid.argtypes = [I, I, I, I, I, I, I, I, pLL, pI, pI, pI]
+    lib.fa_plan_grid.restype = I
+    lib.fa_plan_tile.argtypes = [I, I, I, I, I, I, I, I, LL, pI, pI, pI, pI]
+    lib.fa_plan_tile.restype = I
+    lib.fa_plan_block_class.argtypes = [I, I, I, I, I, I, I, I]
+    lib.fa_plan_block_class.restype = I
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, dtype, stream=None) -> int:
+    """The C call, unchanged: pointers are ints (device addresses); returns the status."""
+    return load().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(causal), int(window), dtype, stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, dtype, stream,
+               descale_q, descale_k, descale_v) -> int:
+    return load().fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(causal), int(window), dtype, stream,
+                             descale_q, descale_k, descale_v)
+
+
+def fa_status_str(status: int) -> str:
+    return load().fa_status_str(status).decode()
+
+
+def plan_grid(B, H, Nq, Nk, D, causal, window, dtype):
+    """(n_wg, br, qw, bc) of the launch fa_fwd would make."""
+    n = ctypes.c_longlong()
+    br, qw, bc = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = load().fa_plan_grid(B, H, Nq, Nk, D, int(causal), int(window), dtype, ctypes.byref(n), ctypes.byref(br),
+                             ctypes.byref(qw), ctypes.byref(bc))
+    if st != FA_OK:
+        raise FaError(st, "fa_plan_grid")
+    return n.value, br.value, qw.value, bc.value
+
+
+def plan_tile(B, H, Nq, Nk, D, causal, window, dtype, wg):
+    """(bh, qtile, kv_lo, kv_hi) of workgroup wg."""
+    bh, qt, lo, hi = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = load().fa_plan_tile(B, H, Nq, Nk, D, int(causal), int(window), dtype, wg, ctypes.byref(bh),
+                             ctypes.byref(qt), ctypes.byref(lo), ctypes.byref(hi))
+    if st != FA_OK:
+        raise FaError(st, "fa_plan_tile")
+    return bh.value, qt.value, lo.value, hi.value
+
+
+def plan_block_class(w0, w1, c0, c1, Nq, Nk, causal, window) -> int:
+    return load().fa_plan_block_class(w0, w1, c0, c1, Nq, Nk, int(causal), int(window))
+
+
+def dtype_code(in_dtype, out_dtype) -> int:
+    import torch
+    table = {
+        (torch.float16, torch.float16): FA_F16,
+        (torch.bfloat16, torch.bfloat16): FA_BF16,
+        (torch.float16, torch.float32): FA_F16_F32OUT,
+        (torch.float8_e4m3fn, torch.bfloat16): FA_E4M3,
+        (torch.bfloat16, torch.float32): FA_BF16_F32OUT,
+    }
+    if (in_dtype, out_dtype) not in table:
+        raise ValueError(f"unsupported dtypes {in_dtype} -> {out_dtype}")
+    return table[(in_dtype, out_dtype)]
+
+
+def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, out_dtype=None,
+              descales=None, stream=None):
+    """O [B,H,Nq,D] and LSE [B,H,Nq] (float32) of softmax(scale Q K^T) V via libfa.
+
+    q [B,H,Nq,D], k and v [B,H,Nk,D]: contiguous device tensors of one dtype
+    (float16, bfloat16 or float8_e4m3fn). out_dtype defaults to the input dtype
+    (bfloat16 for e4m3). descales = (dq, dk, dv) for e4m3 inputs.
+    """
+    import torch
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
+        raise ValueError("k and v must be [B,H,Nk,D] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    code = dtype_code(q.dtype, out_dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, Nq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, H, Nq, Nk, D, float(scale), int(bool(causal)), int(window), code, stream)
+    if code == FA_E4M3 and descales is not None:
+        st = fa_fwd_fp8(*args, *[float(x) for x in descales])
+        where = "fa_fwd_fp8"
+    else:
+        st = fa_fwd(*args)
+        where = "fa_fwd"
+    if st != FA_OK:
+        raise FaError(st, where)
+    return out, lse

@@ -1,0 +1,179 @@
+// C-ABI entry points of libfa.so (declared in include/fa.h).
+//
+// Every argument is validated before the first HIP call, so argument errors
+// are reported (and testable) on a machine without a GPU. The library keeps
+// no state besides a per-device cache of "is this a gfx950".
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+#include "fa_sched.h"
+
+namespace {
+
+struct DtypeInfo {
+    int in, out;
+};
+
+bool dtype_info(int dtype, DtypeInfo* di) {
+    switch (dtype) {
+        case FA_F16: *di = {fa::IN_F16, fa::OUT_F16}; return true;
+        case FA_BF16: *di = {fa::IN_BF16, fa::OUT_BF16}; return true;
+        case FA_F16_F32OUT: *di = {fa::IN_F16, fa::OUT_F32}; return true;
+        case FA_E4M3: *di = {fa::IN_E4M3, fa::OUT_BF16}; return true;
+        case FA_BF16_F32OUT: *di = {fa::IN_BF16, fa::OUT_F32}; return true;
+        default: return false;
+    }
+}
+
+bool finite_positive(float x) { return std::isfinite(x) && x > 0.f; }
+
+// Argument checks shared by the entry points and the plan introspection.
+int check_shape(int B, int H, int Nq, int Nk, int D, int causal, int window, int dtype, DtypeInfo* di) {
+    (void)causal;
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+    if (D != 64 && D != 128) return FA_ERR_HEADDIM;
+    if (!dtype_info(dtype, di)) return FA_ERR_DTYPE;
+    if (window < 0 || (window > 0 && !causal)) return FA_ERR_MASK;
+    // element counts must fit 63 bits; the grid must fit 2^31 - 1 workgroups
+    const long long bh = (long long)B * H;
+    if (bh > (1LL << 31)) return FA_ERR_SHAPE;
+    const long long nmax = Nq > Nk ? Nq : Nk;
+    if (nmax > 0 && bh > (1LL << 62) / ((long long)nmax * D * 4)) return FA_ERR_SHAPE;
+    const fa::Plan pl = fa::make_plan(di->in, di->out, D, B, H, Nq);
+    if (pl.n_wg > 0x7fffffffLL) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_DEVICE;
+    if (dev < 64) {
+        const int known = g_dev_ok[dev].load(std::memory_order_relaxed);
+        if (known == 1) return FA_OK;
+        if (known == 2) return FA_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? FA_OK : FA_ERR_DEVICE;
+}
+
+int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
+        float scale, int causal, int window, int dtype, void* stream, float dq, float dk, float dv) {
+    DtypeInfo di;
+    const int st = check_shape(B, H, Nq, Nk, D, causal, window, dtype, &di);
+    if (st != FA_OK) return st;
+    if (!finite_positive(scale) || !finite_positive(dq) || !finite_positive(dk) || !finite_positive(dv))
+        return FA_ERR_SCALE;
+    const long long rows = (long long)B * H * Nq;
+    if (rows == 0) return FA_OK;  // empty problem: nothing to do
+    if (!q || !o || !lse) return FA_ERR_NULL;
+    if (Nk > 0 && (!k || !v)) return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    const int dst = check_device();
+    if (dst != FA_OK) return dst;
+
+    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq);
+    fa::Params p;
+    p.q = (const uint8_t*)q;
+    p.k = (const uint8_t*)k;
+    p.v = (const uint8_t*)v;
+    p.o = (uint8_t*)o;
+    p.lse = lse;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.causal = causal ? 1 : 0;
+    p.window = window;
+    p.n_bh = B * H;
+    p.n_qt = pl.n_qt;
+    p.c = scale * dq * dk * 1.44269504088896341f;
+    p.out_mul = dv;
+    if (std::getenv("FA_DEBUG"))
+        std::fprintf(stderr, "fa_fwd: in=%d out=%d D=%d qb=%d br=%d bc=%d n_qt=%d n_wg=%lld\n", pl.in, pl.out,
+                     pl.D, pl.qb, pl.br, pl.bc, pl.n_qt, pl.n_wg);
+    (void)hipGetLastError();  // clear a stale error left by the caller
+    const int err = fa::launch(pl, p, stream);
+    return err == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
+           float scale, int causal, int window, int dtype, void* stream) {
+    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, dtype, stream, 1.f, 1.f, 1.f);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+               int D, float scale, int causal, int window, int dtype, void* stream, float descale_q,
+               float descale_k, float descale_v) {
+    if (dtype != FA_E4M3) return FA_ERR_DTYPE;
+    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, dtype, stream, descale_q, descale_k,
+               descale_v);
+}
+
+const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "invalid or too large sizes";
+        case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
+        case FA_ERR_DTYPE: return "unsupported dtype";
+        case FA_ERR_MASK: return "window must be >= 0 and needs causal";
+        case FA_ERR_SCALE: return "scale and descales must be finite and positive";
+        case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+        case FA_ERR_DEVICE: return "no gfx950 HIP device is current";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int fa_plan_grid(int B, int H, int Nq, int Nk, int D, int causal, int window, int dtype, long long* n_wg, int* br,
+                 int* qw, int* bc) {
+    DtypeInfo di;
+    const int st = check_shape(B, H, Nq, Nk, D, causal, window, dtype, &di);
+    if (st != FA_OK) return st;
+    if (!n_wg || !br || !qw || !bc) return FA_ERR_NULL;
+    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq);
+    *n_wg = pl.n_wg;
+    *br = pl.br;
+    *qw = 32 * pl.qb;
+    *bc = pl.bc;
+    return FA_OK;
+}
+
+int fa_plan_tile(int B, int H, int Nq, int Nk, int D, int causal, int window, int dtype, long long wg, int* bh,
+                 int* qtile, int* kv_lo, int* kv_hi) {
+    DtypeInfo di;
+    const int st = check_shape(B, H, Nq, Nk, D, causal, window, dtype, &di);
+    if (st != FA_OK) return st;
+    if (!bh || !qtile || !kv_lo || !kv_hi) return FA_ERR_NULL;
+    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq);
+    if (wg < 0 || wg >= pl.n_wg) return FA_ERR_SHAPE;
+    fa::decode_wg(wg, B * H, pl.n_qt, bh, qtile);
+    const int r0 = *qtile * pl.br;
+    const int r1 = (r0 + pl.br < Nq) ? r0 + pl.br : Nq;
+    fa::kv_range(r0, r1, Nq, Nk, causal ? 1 : 0, window, kv_lo, kv_hi);
+    return FA_OK;
+}
+
+int fa_plan_block_class(int w0, int w1, int c0, int c1, int Nq, int Nk, int causal, int window) {
+    return fa::tile_class(w0, w1, c0, c1, Nq, Nk, causal ? 1 : 0, window);
+}
+
+}  // extern "C"

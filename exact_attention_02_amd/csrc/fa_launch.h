@@ -1,0 +1,43 @@
+// Internal interface between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+enum InKind { IN_F16 = 0, IN_BF16 = 1, IN_E4M3 = 2 };
+enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
+
+// Everything a workgroup needs; passed by value as the kernel argument.
+struct Params {
+    const uint8_t* q;
+    const uint8_t* k;
+    const uint8_t* v;
+    uint8_t* o;
+    float* lse;
+    int Nq, Nk;
+    int causal, window;
+    int n_bh;       // B * H
+    int n_qt;       // query tiles per head
+    float c;        // scale * descale_q * descale_k * log2(e): scores in base-2 units
+    float out_mul;  // descale_v (1 unless e4m3)
+};
+
+// Tile shape a launch uses.
+struct Plan {
+    int in, out, D;
+    int qb;         // 32-row query blocks per wave
+    int br;         // query rows per workgroup (4 waves)
+    int bc;         // key rows per tile
+    int n_qt;
+    long long n_wg;
+};
+
+// Picks the tile shape for a problem. Pure host arithmetic.
+Plan make_plan(int in, int out, int D, int B, int H, int Nq);
+
+// Enqueues the kernel chosen by `plan` on `stream`; returns the hipError_t
+// value of hipGetLastError() after the launch (0 on success).
+int launch(const Plan& plan, const Params& p, void* stream);
+
+}  // namespace fa

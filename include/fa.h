@@ -1,0 +1,134 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact-attention forward library.
+ *
+ * The operation is scaled dot-product attention,
+ *     O = softmax(scale * Q K^T) V,
+ * (aiinarabic.com "flash-attention" page, equation (1), with scale = 1/sqrt(d_k)
+ * there), computed tile by tile with an online softmax so the Nq x Nk score
+ * matrix is never written to device memory (same page, the kernel-fusion
+ * discussion and Figure 4; inskillml course module 9, "FlashAttention: compute
+ * without writing the weights"). Besides O the call writes each row's
+ * log-sum-exp, the softmax normaliser the pages say the forward keeps for the
+ * backward pass (aiinarabic.com page, the recomputation paragraph).
+ *
+ * Tensor layout follows the SDPA call in inskillml module 9: (batch, heads,
+ * sequence, head_dim), contiguous and row-major:
+ *     q   [B, H, Nq, D]      k, v [B, H, Nk, D]
+ *     o   [B, H, Nq, D]      lse  [B, H, Nq]  (float32)
+ * All of q, k, v, o, lse are device pointers; q, k, v, o 16-byte aligned and
+ * lse 4-byte aligned. The caller allocates and owns every buffer; the library
+ * allocates nothing, frees nothing and keeps no pointer after the call.
+ *
+ * Masks (is_causal in the SDPA call; sliding windows in module 9's "Sparse
+ * patterns" section):
+ *     causal != 0 : query row i sees keys j <= i + (Nk - Nq)
+ *                   (rows aligned at the bottom right when Nq != Nk).
+ *     window  > 0 : additionally j > i + (Nk - Nq) - window, i.e. the `window`
+ *                   most recent keys including the diagonal. Needs causal.
+ *     window == 0 : no window.
+ * A row that sees no key gets O = 0 and LSE = -inf.
+ *
+ * Streams: work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ * the default stream) and the call returns without synchronising. Faults inside
+ * the kernel surface at the caller's next synchronisation, as usual in HIP.
+ *
+ * Errors: every argument is checked before any HIP call; on an argument error
+ * the outputs are untouched and nothing is enqueued. No C++ exception or abort
+ * crosses this boundary. The functions are re-entrant and thread-safe.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtypes: inputs -> output. LSE is always float32. */
+enum {
+    FA_F16 = 1,          /* q, k, v float16  -> o float16  */
+    FA_BF16 = 2,         /* q, k, v bfloat16 -> o bfloat16 */
+    FA_F16_F32OUT = 3,   /* q, k, v float16  -> o float32  */
+    FA_E4M3 = 4,         /* q, k, v OCP E4M3FN (8-bit, bias 7, max 448) -> o bfloat16 */
+    FA_BF16_F32OUT = 5   /* q, k, v bfloat16 -> o float32  */
+};
+
+/* Status codes. */
+enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL */
+    FA_ERR_SHAPE = 2,     /* a negative size, or sizes whose products overflow */
+    FA_ERR_HEADDIM = 3,   /* D is not 64 or 128 */
+    FA_ERR_DTYPE = 4,     /* unknown dtype, or fa_fwd_fp8 with a non-e4m3 dtype */
+    FA_ERR_MASK = 5,      /* window < 0, or window > 0 without causal */
+    FA_ERR_SCALE = 6,     /* scale or a descale is not finite and positive */
+    FA_ERR_ALIGN = 7,     /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
+    FA_ERR_DEVICE = 8,    /* no HIP device, or the current device is not gfx950 */
+    FA_ERR_LAUNCH = 9     /* the kernel launch failed (hipGetLastError) */
+};
+
+/*
+ * fa_fwd: attention forward, O and LSE.
+ *   q, k, v : inputs in the layout above, in `dtype`'s input type.
+ *   o       : output [B,H,Nq,D] in `dtype`'s output type.
+ *   lse     : output [B,H,Nq] float32, natural-log log-sum-exp of the scaled
+ *             scores over the visible keys: ln sum_j exp(scale * q_i . k_j).
+ *   B, H, Nq, Nk, D : sizes; any of B, H, Nq equal to 0 is an empty problem
+ *             (FA_OK, nothing enqueued); Nk = 0 gives O = 0, LSE = -inf.
+ *   scale   : multiplier of the dot products (1/sqrt(D) in the pages).
+ *   causal, window : the masks above.
+ *   dtype   : one of the FA_* dtypes; FA_E4M3 behaves as fa_fwd_fp8 with all
+ *             descales 1.
+ *   stream  : hipStream_t or NULL.
+ * Returns FA_OK or an FA_ERR_* code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Nq, int Nk, int D, float scale,
+           int causal, int window, int dtype, void* stream);
+
+/*
+ * fa_fwd_fp8: as fa_fwd for FA_E4M3 inputs that were quantised per tensor.
+ * The real values are q8 * descale_q, k8 * descale_k and v8 * descale_v, so
+ * the scores are scale * descale_q * descale_k * (q8 . k8) and the output is
+ * descale_v * softmax(...) v8. FP8 inputs are the low-precision path of
+ * FlashAttention-3 (news.hamidun.com FlashAttention-3 item, "How the speedup
+ * works", third point). dtype must be FA_E4M3.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Nq, int Nk, int D, float scale,
+               int causal, int window, int dtype, void* stream,
+               float descale_q, float descale_k, float descale_v);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_status_str(int status);
+
+/*
+ * Launch-plan introspection (host only; no HIP call, usable without a GPU).
+ * These expose the logical-grid scheduler the kernel uses, so its coverage and
+ * bijection properties can be tested on the CPU.
+ *
+ * fa_plan_grid: for a problem, the workgroup count, the query rows per
+ *   workgroup (br), the query rows per wave (qw) and the key rows per tile (bc)
+ *   that fa_fwd would launch with. Returns FA_OK or an argument error code.
+ */
+int fa_plan_grid(int B, int H, int Nq, int Nk, int D, int causal, int window, int dtype,
+                 long long* n_wg, int* br, int* qw, int* bc);
+
+/*
+ * fa_plan_tile: for workgroup `wg` of that plan, its (batch*head) index, its
+ *   query tile, and the key range [kv_lo, kv_hi) it visits.
+ */
+int fa_plan_tile(int B, int H, int Nq, int Nk, int D, int causal, int window, int dtype,
+                 long long wg, int* bh, int* qtile, int* kv_lo, int* kv_hi);
+
+/*
+ * fa_plan_block_class: the class the kernel gives a block of query rows
+ *   [w0, w1) against keys [c0, c1): 0 skipped (no visible pair), 1 computed
+ *   without a mask (every pair visible), 2 computed with the mask.
+ */
+int fa_plan_block_class(int w0, int w1, int c0, int c1, int Nq, int Nk, int causal, int window);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

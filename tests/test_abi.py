@@ -1,0 +1,93 @@
+"""The C ABI on the host: the library loads, exports what include/fa.h
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import exact_attention_02_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTS), names
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_enums_match_header():
+    text = open(HEADER).read()
+    for name in ["FA_F16", "FA_BF16", "FA_F16_F32OUT", "FA_E4M3", "FA_BF16_F32OUT", "FA_OK", "FA_ERR_NULL",
+                 "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_DTYPE", "FA_ERR_MASK", "FA_ERR_SCALE",
+                 "FA_ERR_ALIGN", "FA_ERR_DEVICE", "FA_ERR_LAUNCH"]:
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(fa, name), name
+
+
+def test_status_strings():
+    for s in range(10):
+        assert fa.fa_status_str(s) and fa.fa_status_str(s) != "unknown status"
+    assert fa.fa_status_str(99) == "unknown status"
+
+
+P = 0x100000  # a 16-byte aligned dummy address; never dereferenced on these paths
+
+
+def call(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=64, Nk=64, D=64, scale=0.125, causal=0, window=0,
+             dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"],
+                     a["scale"], a["causal"], a["window"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), fa.FA_ERR_SHAPE), (dict(Nq=-3), fa.FA_ERR_SHAPE), (dict(Nk=-1), fa.FA_ERR_SHAPE),
+    (dict(D=96), fa.FA_ERR_HEADDIM), (dict(D=0), fa.FA_ERR_HEADDIM), (dict(D=256), fa.FA_ERR_HEADDIM),
+    (dict(dtype=0), fa.FA_ERR_DTYPE), (dict(dtype=6), fa.FA_ERR_DTYPE),
+    (dict(window=16), fa.FA_ERR_MASK), (dict(window=-1, causal=1), fa.FA_ERR_MASK),
+    (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-1.0), fa.FA_ERR_SCALE),
+    (dict(scale=float("inf")), fa.FA_ERR_SCALE), (dict(scale=float("nan")), fa.FA_ERR_SCALE),
+    (dict(q=0), fa.FA_ERR_NULL), (dict(o=0), fa.FA_ERR_NULL), (dict(lse=0), fa.FA_ERR_NULL),
+    (dict(k=0), fa.FA_ERR_NULL), (dict(v=0), fa.FA_ERR_NULL),
+    (dict(q=P + 8), fa.FA_ERR_ALIGN), (dict(v=P + 4), fa.FA_ERR_ALIGN), (dict(lse=P + 2), fa.FA_ERR_ALIGN),
+    (dict(B=1 << 20, H=1 << 12, Nq=1 << 20), fa.FA_ERR_SHAPE),
+])
+def test_argument_errors_before_any_device_work(kw, code):
+    assert call(**kw) == code
+
+
+def test_fp8_entry_checks_dtype_and_descales():
+    args = (P, P, P, P, P, 1, 1, 64, 64, 128, 0.088, 0, 0)
+    assert fa.fa_fwd_fp8(*args, fa.FA_BF16, None, 1.0, 1.0, 1.0) == fa.FA_ERR_DTYPE
+    assert fa.fa_fwd_fp8(*args, fa.FA_E4M3, None, 0.0, 1.0, 1.0) == fa.FA_ERR_SCALE
+    assert fa.fa_fwd_fp8(*args, fa.FA_E4M3, None, 1.0, float("nan"), 1.0) == fa.FA_ERR_SCALE
+
+
+def test_empty_problems_need_no_device():
+    assert call(B=0) == fa.FA_OK
+    assert call(H=0, q=0, k=0, v=0, o=0, lse=0) == fa.FA_OK
+    assert call(Nq=0) == fa.FA_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_valid_call_without_gpu_reports_device_error():
+    assert call() == fa.FA_ERR_DEVICE
+    assert call(Nk=0, k=0, v=0) == fa.FA_ERR_DEVICE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.load(str(tmp_path / "libfa.so"))

@@ -1,0 +1,329 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Bounds: max |O - O_ref| <= 2e-3 for float16 inputs and <= 1e-2 for bfloat16
+inputs, relative RMS <= 5e-2 for e4m3 inputs, and |LSE - LSE_ref| /
+max(1, |LSE_ref|) <= 1e-4, where O_ref and LSE_ref are the oracle's unrounded
+float64 results on the very same stored inputs. Rows that see no key must give
+O = 0 and LSE = -inf exactly.
+
+The five workloads run at full size in the launch configuration the benchmark
+times, compared on sampled rows the oracle computes one by one; smaller
+shapes that span several tiles with ragged tails are compared in full.
+"""
+import math
+
+import pytest
+import torch
+
+import exact_attention_02_amd as fa
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+O_BOUND = {"f16": 2e-3, "bf16": 1e-2}
+RMS_BOUND = 5e-2
+LSE_BOUND = 1e-4
+OUT_T = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def run_gpu(w: synth.Workload, inp: synth.Inputs, q=None, k=None, v=None):
+    q = inp.q.to(DEV) if q is None else q
+    k = inp.k.to(DEV) if k is None else k
+    v = inp.v.to(DEV) if v is None else v
+    descales = (inp.descale_q, inp.descale_k, inp.descale_v) if w.in_dtype == "e4m3" else None
+    o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window,
+                          out_dtype=OUT_T[w.out_dtype], descales=descales)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def reference(w, inp, rows=None):
+    return oracle.attention(inp.q, inp.k, inp.v, w.scale, w.causal, w.window,
+                            descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows)
+
+
+def compare(w, O, L, Oref, Lref, label=""):
+    """O, L: GPU results as float64 CPU tensors of the same shape as Oref, Lref."""
+    O = O.reshape(-1, w.D)
+    Oref = Oref.reshape(-1, w.D)
+    L = L.reshape(-1)
+    Lref = Lref.reshape(-1)
+    empty = torch.isneginf(Lref)
+    assert torch.all(O[empty] == 0), f"{label}: empty rows must give O = 0"
+    assert torch.all(torch.isneginf(L[empty])), f"{label}: empty rows must give LSE = -inf"
+    ne = ~empty
+    assert torch.all(torch.isfinite(O)), f"{label}: non-finite output"
+    stats = {}
+    if ne.any():
+        d = (O[ne] - Oref[ne])
+        if w.in_dtype == "e4m3":
+            rel = (d.norm() / Oref[ne].norm()).item()
+            stats["rel_rms"] = rel
+            assert rel <= RMS_BOUND, f"{label}: relative RMS {rel:.3e} > {RMS_BOUND}"
+        else:
+            err = d.abs().max().item()
+            stats["max_abs"] = err
+            assert err <= O_BOUND[w.in_dtype], f"{label}: max abs err {err:.3e} > {O_BOUND[w.in_dtype]}"
+        lerr = ((L[ne] - Lref[ne]).abs() / Lref[ne].abs().clamp(min=1.0)).max().item()
+        stats["lse_rel"] = lerr
+        assert lerr <= LSE_BOUND, f"{label}: LSE rel err {lerr:.3e} > {LSE_BOUND}"
+    print(f"{label}: {stats}", flush=True)
+    return stats
+
+
+def sample_rows(w, n_random=1500, seed=0):
+    """Row ids: the first 300 and last 64 rows of three heads, plus random rows."""
+    n_bh = w.B * w.H
+    rows = set()
+    for bh in sorted({0, n_bh // 2, n_bh - 1}):
+        base = bh * w.Nq
+        rows.update(base + i for i in range(min(300, w.Nq)))
+        rows.update(base + i for i in range(max(0, w.Nq - 64), w.Nq))
+    g = torch.Generator().manual_seed(seed)
+    rows.update(torch.randint(0, n_bh * w.Nq, (n_random,), generator=g).tolist())
+    return sorted(rows)
+
+
+# ------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_workload_full(name):
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("name", ["c3", "c4c", "c4w", "c5"])
+def test_workload_full_size_sampled_rows(name):
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    rows = sample_rows(w)
+    Oref, Lref = reference(w, inp, rows=rows)
+    idx = torch.tensor(rows)
+    O = o.reshape(-1, w.D)[idx.to(DEV)].double().cpu()
+    L = lse.reshape(-1)[idx.to(DEV)].double().cpu()
+    compare(w, O, L, Oref, Lref, f"{w.name} ({len(rows)} rows)")
+    assert torch.all(torch.isfinite(o)) and not torch.any(torch.isnan(lse))
+
+
+# ---------------------------------------------- smaller shapes, full compare
+
+SHAPES = [
+    # B, H, Nq, Nk
+    (1, 1, 1, 1), (1, 2, 17, 17), (2, 3, 300, 300), (1, 2, 200, 333), (1, 2, 333, 200),
+    (2, 1, 513, 513), (1, 1, 64, 1000), (1, 1, 1000, 64), (1, 4, 129, 65),
+]
+MODES = [(False, 0), (True, 0), (True, 1), (True, 100)]
+DTYPES = [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32"), ("e4m3", "bf16")]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", SHAPES)
+@pytest.mark.parametrize("causal,window", MODES)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("din,dout", DTYPES)
+def test_small_shapes(B, H, Nq, Nk, causal, window, D, din, dout):
+    seed = 1000 + B * 7 + H * 13 + Nq * 3 + Nk + D + (17 if causal else 0) + window
+    w = synth.small_workload(f"B{B}H{H}q{Nq}k{Nk}D{D}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, D,
+                             causal, window, din, dout, seed,
+                             outlier_frac=0.001 if din == "e4m3" else 0.0, outlier_mult=20.0)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+# ----------------------------------------------------------- edge cases
+
+def test_no_keys_gives_zero_and_minus_inf():
+    q = torch.randn(1, 2, 40, 64, device=DEV).to(torch.bfloat16)
+    k = torch.empty(1, 2, 0, 64, device=DEV, dtype=torch.bfloat16)
+    o = torch.full((1, 2, 40, 64), 7.0, device=DEV, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 40, device=DEV)
+    fa.attention(q, k, k, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_empty_batch_is_a_no_op():
+    q = torch.empty(0, 2, 40, 64, device=DEV, dtype=torch.float16)
+    o, lse = fa.attention(q, q, q)
+    assert o.shape == (0, 2, 40, 64)
+
+
+def test_rows_before_the_first_key_are_empty():
+    # Nq > Nk with bottom-right alignment: the first Nq - Nk rows see nothing.
+    w = synth.small_workload("empty_rows", 1, 2, 300, 100, 64, True, 0, "bf16", "bf16", 77)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    assert torch.isneginf(Lref[0, 0, :200]).all()
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("f16", "f16")])
+def test_large_scores_and_moving_max(din, dout):
+    # Scores that grow along the keys move the running max in every tile, and
+    # a large scale pushes scores far beyond exp's fp32 range before shifting.
+    B, H, N, D = 1, 2, 700, 64
+    w = synth.small_workload("ramp", B, H, N, N, D, True, 0, din, dout, 88)
+    inp = synth.make_inputs(w)
+    ramp = torch.linspace(0.0, 6.0, N, dtype=torch.float64).view(1, 1, N, 1)
+    kk = (inp.k.double() * 0.2 + ramp).to(inp.k.dtype)
+    qq = (inp.q.double() * 4.0).to(inp.q.dtype)
+    inp2 = synth.Inputs(qq, kk, inp.v)
+    for scale in (w.scale, 2.0):
+        w.scale = float(torch.tensor(scale, dtype=torch.float32))
+        o, lse = run_gpu(w, inp2)
+        Oref, Lref = reference(w, inp2)
+        compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, f"ramp scale={scale}")
+
+
+# -------------------------------------------------- closed forms on the GPU
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_zero_queries_average_the_visible_values(D):
+    N = 333
+    v = torch.randn(1, 2, N, D, dtype=torch.float64)
+    q = torch.zeros(1, 2, N, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(1, 2, N, D, device=DEV).to(torch.bfloat16)
+    vb = v.to(torch.bfloat16)
+    o, lse = fa.attention(q, k, vb.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    cnt = torch.arange(1, N + 1, dtype=torch.float64)
+    mean = vb.double().cumsum(dim=2) / cnt.view(1, 1, N, 1)
+    assert (o.double().cpu() - mean).abs().max().item() <= 1e-2
+    assert ((lse.double().cpu() - torch.log(cnt)).abs() / torch.log(cnt).clamp(min=1)).max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("D,a", [(64, 80.0), (128, 96.0)])
+@pytest.mark.parametrize("t", [0, 63, 64, 130, 255])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_one_hot_score_selects_value_row_exactly(D, a, t, dt):
+    N = 256
+    q = torch.zeros(1, 1, N, D, dtype=dt)
+    q[..., 0] = a
+    k = torch.zeros(1, 1, N, D, dtype=dt)
+    k[0, 0, t, 0] = a
+    v = torch.randn(1, 1, N, D).to(dt)
+    o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o.cpu(), v[0, 0, t].expand(1, 1, N, D))
+    ref = a * a * float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+    assert ((lse.double().cpu() - ref).abs() / ref).max().item() <= 1e-6
+
+
+def test_causal_first_row_is_first_value_exactly():
+    w = synth.small_workload("row0", 2, 3, 200, 200, 128, True, 0, "bf16", "bf16", 55)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    assert torch.equal(o[:, :, 0].cpu(), inp.v[:, :, 0])
+
+
+# -------------------------------------------- exactness and independence
+
+@pytest.mark.parametrize("din,D", [("bf16", 64), ("f16", 128), ("e4m3", 128)])
+def test_masked_keys_are_reproduced_exactly(din, D):
+    # Causal: perturbing keys/values j >= t (t not tile aligned) leaves rows i < t bitwise unchanged.
+    N, t = 400, 150
+    dout = "bf16" if din != "f16" else "f16"
+    w = synth.small_workload("mask_exact", 1, 2, N, N, D, True, 0, din, dout, 66)
+    inp = synth.make_inputs(w)
+    o1, l1 = run_gpu(w, inp)
+    k2, v2 = inp.k.clone(), inp.v.clone()
+    big = (torch.randn(1, 2, N - t, D) * 100).to(k2.dtype) if din != "e4m3" else \
+        (torch.randn(1, 2, N - t, D) * 100).clamp(-448, 448).to(k2.dtype)
+    k2[:, :, t:] = big
+    v2[:, :, t:] = big
+    o2, l2 = run_gpu(w, inp, k=k2.to(DEV), v=v2.to(DEV))
+    assert torch.equal(o1[:, :, :t].cpu().view(torch.uint8), o2[:, :, :t].cpu().view(torch.uint8))
+    assert torch.equal(l1[:, :, :t].cpu(), l2[:, :, :t].cpu())
+    assert not torch.equal(l1[:, :, t:].cpu(), l2[:, :, t:].cpu())
+
+
+def test_window_masked_keys_are_reproduced_exactly():
+    # Window w: rows i >= t + w do not see keys j < t.
+    N, t, win = 500, 70, 96
+    w = synth.small_workload("window_exact", 1, 2, N, N, 64, True, win, "bf16", "bf16", 67)
+    inp = synth.make_inputs(w)
+    o1, l1 = run_gpu(w, inp)
+    k2, v2 = inp.k.clone(), inp.v.clone()
+    big = (torch.randn(1, 2, t, 64) * 100).to(torch.bfloat16)
+    k2[:, :, :t] = big
+    v2[:, :, :t] = big
+    o2, l2 = run_gpu(w, inp, k=k2.to(DEV), v=v2.to(DEV))
+    r = t + win
+    assert torch.equal(o1[:, :, r:].cpu().view(torch.uint8), o2[:, :, r:].cpu().view(torch.uint8))
+    assert torch.equal(l1[:, :, r:].cpu(), l2[:, :, r:].cpu())
+
+
+def test_keys_beyond_nk_are_never_read():
+    # Nk' < allocated rows: rows past Nk' of K and V are poisoned with NaN and
+    # must not influence anything (they are never loaded).
+    B, H, N, D, Nk = 1, 2, 200, 64, 137
+    w = synth.small_workload("tail", B, H, N, Nk, D, False, 0, "bf16", "bf16", 68)
+    inp = synth.make_inputs(w)
+    kbig = torch.full((B, H, N, D), float("nan"), dtype=torch.bfloat16)
+    vbig = kbig.clone()
+    kbig[:, :, :Nk] = inp.k
+    vbig[:, :, :Nk] = inp.v
+    kd, vd = kbig.to(DEV), vbig.to(DEV)
+    q = inp.q.to(DEV)
+    o = torch.empty(B, H, N, D, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, H, N, device=DEV)
+    # pass the batch/head stride of N rows by calling per head (layout is [B,H,Nk,D] contiguous)
+    for h in range(H):
+        st = fa.fa_fwd(q[:, h].data_ptr(), kd[:, h].data_ptr(), vd[:, h].data_ptr(), o[:, h].data_ptr(),
+                       lse[:, h].data_ptr(), 1, 1, N, Nk, D, w.scale, 0, 0, fa.FA_BF16,
+                       torch.cuda.current_stream().cuda_stream)
+        assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, "tail")
+
+
+def test_run_to_run_determinism_and_head_independence():
+    w = synth.small_workload("det", 2, 3, 700, 700, 64, True, 0, "bf16", "bf16", 69)
+    inp = synth.make_inputs(w)
+    o1, l1 = run_gpu(w, inp)
+    o2, l2 = run_gpu(w, inp)
+    assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)) and torch.equal(l1, l2)
+    # one (b, h) slice alone equals the same slice inside the batch, bitwise
+    ws = synth.small_workload("det1", 1, 1, 700, 700, 64, True, 0, "bf16", "bf16", 69)
+    sl = synth.Inputs(inp.q[1:2, 2:3].contiguous(), inp.k[1:2, 2:3].contiguous(), inp.v[1:2, 2:3].contiguous())
+    o3, l3 = run_gpu(ws, sl)
+    assert torch.equal(o3[0, 0].view(torch.uint8), o1[1, 2].view(torch.uint8))
+    assert torch.equal(l3[0, 0], l1[1, 2])
+
+
+def test_power_of_two_rescaling_is_bitwise_invariant():
+    w = synth.small_workload("pow2", 1, 2, 300, 300, 128, True, 0, "bf16", "bf16", 70)
+    inp = synth.make_inputs(w)
+    o1, l1 = run_gpu(w, inp)
+    q2 = (inp.q.double() * 2).to(torch.bfloat16)
+    w.scale = w.scale / 2
+    o2, l2 = run_gpu(w, inp, q=q2.to(DEV))
+    assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)) and torch.equal(l1, l2)
+
+
+def test_no_device_allocation():
+    # The library allocates nothing: device free memory is unchanged by a
+    # full-size call (inputs and outputs allocated beforehand).
+    w = synth.WORKLOADS["c3"]
+    inp = synth.make_inputs(w)
+    q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device=DEV)
+    fa.attention(q, k, v, causal=True, out=o, lse=lse)   # code objects loaded
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    peak0 = torch.cuda.max_memory_allocated()
+    for _ in range(3):
+        fa.attention(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0 and torch.cuda.max_memory_allocated() == peak0

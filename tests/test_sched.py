@@ -1,0 +1,95 @@
+"""The logical-grid scheduler, exhaustively on small shapes (CPU).
+
+Checks against the mask predicate written out here: every visible
+(query, key) pair lies in its workgroup's key range; the workgroup ids map
+one-to-one onto (batch*head, query tile); the block classes the kernel uses
+are exact (skipped blocks hold no visible pair, unmasked blocks no hidden one).
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import exact_attention_02_amd as fa
+
+
+def vis(i, j, Nq, Nk, causal, window):
+    ip = i + Nk - Nq
+    return 0 <= j < Nk and (not causal or j <= ip) and (window == 0 or j > ip - window)
+
+
+def vis_matrix(Nq, Nk, causal, window):
+    ip = np.arange(Nq)[:, None] + (Nk - Nq)
+    j = np.arange(Nk)[None, :]
+    m = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        m &= j <= ip
+    if window:
+        m &= j > ip - window
+    return m
+
+
+SHAPES = [(1, 1, 1, 1), (2, 3, 5, 7), (1, 2, 130, 130), (2, 1, 300, 257), (1, 1, 257, 300), (1, 8, 256, 256),
+          (3, 8, 513, 513), (1, 1, 70, 1), (1, 1, 1, 200), (1, 16, 1000, 1000), (2, 4, 40, 0)]
+MODES = [(False, 0), (True, 0), (True, 1), (True, 63), (True, 200)]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", SHAPES)
+@pytest.mark.parametrize("causal,window", MODES)
+@pytest.mark.parametrize("D,dtype", [(64, fa.FA_BF16), (128, fa.FA_BF16), (128, fa.FA_E4M3), (64, fa.FA_F16)])
+def test_grid_covers_every_visible_pair_once(B, H, Nq, Nk, causal, window, D, dtype):
+    n_wg, br, qw, bc = fa.plan_grid(B, H, Nq, Nk, D, causal, window, dtype)
+    n_qt = (Nq + br - 1) // br
+    assert n_wg == B * H * n_qt and br % qw == 0 and bc == 64
+    seen = set()
+    vm = vis_matrix(Nq, Nk, causal, window)
+    for wg in range(n_wg):
+        bh, qt, lo, hi = fa.plan_tile(B, H, Nq, Nk, D, causal, window, dtype, wg)
+        assert 0 <= bh < B * H and 0 <= qt < n_qt
+        assert (bh, qt) not in seen
+        seen.add((bh, qt))
+        r0, r1 = qt * br, min(qt * br + br, Nq)
+        assert 0 <= lo <= hi <= Nk
+        cols = np.nonzero(vm[r0:r1].any(axis=0))[0]
+        if cols.size:
+            # every visible key of the tile's rows is in range, and the range is
+            # tight: its first and last keys are visible to some row
+            assert lo == cols.min() and hi == cols.max() + 1, (wg, lo, hi)
+        else:
+            assert lo == hi
+    assert len(seen) == n_wg
+
+
+@pytest.mark.parametrize("Nq,Nk", [(64, 64), (100, 37), (37, 100), (128, 200)])
+@pytest.mark.parametrize("causal,window", MODES)
+def test_block_class_is_exact(Nq, Nk, causal, window):
+    for w0, c0 in itertools.product(range(0, Nq, 13), range(0, Nk + 20, 17)):
+        for w1, c1 in [(w0 + 1, c0 + 1), (min(w0 + 32, Nq), c0 + 64), (min(w0 + 64, Nq), c0 + 9)]:
+            if w1 <= w0:
+                continue
+            cls = fa.plan_block_class(w0, w1, c0, c1, Nq, Nk, causal, window)
+            pairs = [vis(i, j, Nq, Nk, causal, window) for i in range(w0, w1) for j in range(c0, c1)]
+            if cls == 0:
+                assert not any(pairs)
+            elif cls == 1:
+                assert all(pairs)
+            else:
+                assert cls == 2 and any(pairs) and not all(pairs)
+
+
+def test_heads_stay_on_one_xcd_and_tiles_go_heavy_first():
+    # 48 heads (B4 H12), 32 query tiles: workgroups with the same id mod 8
+    # (the same XCD under round-robin dispatch) cover 6 whole heads, and
+    # within a head the causal query tiles come last-first.
+    B, H, N = 4, 12, 8192
+    n_wg, br, qw, bc = fa.plan_grid(B, H, N, N, 64, True, 0, fa.FA_BF16)
+    heads_of_xcd = {x: set() for x in range(8)}
+    order = {}
+    for wg in range(n_wg):
+        bh, qt, lo, hi = fa.plan_tile(B, H, N, N, 64, True, 0, fa.FA_BF16, wg)
+        heads_of_xcd[wg % 8].add(bh)
+        order.setdefault(bh, []).append(qt)
+    assert all(len(s) == 6 for s in heads_of_xcd.values())
+    assert set().union(*heads_of_xcd.values()) == set(range(48))
+    for bh, qts in order.items():
+        assert qts == sorted(qts, reverse=True)
