@@ -31,6 +31,7 @@
 //    converts with round-to-nearest-even and writes O and the row LSE.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "fa_launch.h"
 #include "fa_sched.h"
@@ -52,46 +53,48 @@ constexpr int BC = 64;
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float LOG2E = 1.44269504088896341f;
 
+// Per input type: the MFMA used for S^T = K Q^T (always a 16-bit MFMA: e4m3
+// inputs are widened exactly to bf16 for it, because the f8f6f4 MFMA sums its
+// 64 products with fewer bits than fp32 and the scores feed the LSE), the MFMA
+// used for O^T += V^T P^T, and the lazy-rescale threshold.
 template <int IN> struct In;
 template <> struct In<IN_BF16> {
-    static constexpr int EB = 2, KSTEP = 16, OPW = 4;
+    static constexpr int EB = 2;            // bytes per stored element
+    static constexpr int QK = IN_BF16;      // score MFMA operand type
+    static constexpr int PV_KSTEP = 16;     // keys per P.V MFMA
+    static constexpr int PV_OPW = 4;        // dwords per P.V operand
     static constexpr float TAU = 8.f, PRESCALE = 1.f;
 };
 template <> struct In<IN_F16> {
-    static constexpr int EB = 2, KSTEP = 16, OPW = 4;
+    static constexpr int EB = 2;
+    static constexpr int QK = IN_F16;
+    static constexpr int PV_KSTEP = 16;
+    static constexpr int PV_OPW = 4;
     static constexpr float TAU = 8.f, PRESCALE = 1.f;
 };
 // e4m3: P is stored as e4m3 of p * 2^6 with p <= 2^TAU = 4, so it stays below
 // 256 < 448 (the format's largest value) while small weights keep most of the
 // format's range above its smallest subnormal.
 template <> struct In<IN_E4M3> {
-    static constexpr int EB = 1, KSTEP = 64, OPW = 8;
+    static constexpr int EB = 1;
+    static constexpr int QK = IN_BF16;
+    static constexpr int PV_KSTEP = 64;
+    static constexpr int PV_OPW = 8;
     static constexpr float TAU = 2.f, PRESCALE = 64.f;
 };
 
-template <int N> struct OpT;
-template <> struct OpT<4> { typedef i32x4 type; };
-template <> struct OpT<8> { typedef i32x8 type; };
-
-template <int IN>
-__device__ __forceinline__ f32x16 mfma(const typename OpT<In<IN>::OPW>::type& a,
-                                       const typename OpT<In<IN>::OPW>::type& b, const f32x16& c);
-template <>
-__device__ __forceinline__ f32x16 mfma<IN_BF16>(const i32x4& a, const i32x4& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-template <>
-__device__ __forceinline__ f32x16 mfma<IN_F16>(const i32x4& a, const i32x4& b, const f32x16& c) {
+__device__ __forceinline__ f32x16 mfma16(int qk, const i32x4& a, const i32x4& b, const f32x16& c) {
+    if (qk == IN_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
-template <>
-__device__ __forceinline__ f32x16 mfma<IN_E4M3>(const i32x8& a, const i32x8& b, const f32x16& c) {
-    // format 0 for both operands = OCP E4M3; scales 0 = unscaled.
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+    // operand format 0 = OCP E4M3 for both; block scales 0 = unscaled.
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Two floats -> two 16-bit values (round to nearest even) in one dword.
-template <int IN> __device__ __forceinline__ int pack2(float a, float b);
+template <int T> __device__ __forceinline__ int pack2(float a, float b);
 template <> __device__ __forceinline__ int pack2<IN_BF16>(float a, float b) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -102,9 +105,9 @@ template <> __device__ __forceinline__ int pack2<IN_F16>(float a, float b) {
     f16x2 v = {(_Float16)a, (_Float16)b};
     return __builtin_bit_cast(int, v);
 }
-// Inverse of one half of pack2 (exact).
-template <int IN> __device__ __forceinline__ float unpack_lo(int w);
-template <int IN> __device__ __forceinline__ float unpack_hi(int w);
+// Exact inverse of one half of pack2.
+template <int T> __device__ __forceinline__ float unpack_lo(int w);
+template <int T> __device__ __forceinline__ float unpack_hi(int w);
 template <> __device__ __forceinline__ float unpack_lo<IN_BF16>(int w) { return __int_as_float(w << 16); }
 template <> __device__ __forceinline__ float unpack_hi<IN_BF16>(int w) { return __int_as_float(w & 0xffff0000); }
 template <> __device__ __forceinline__ float unpack_lo<IN_F16>(int w) {
@@ -114,31 +117,36 @@ template <> __device__ __forceinline__ float unpack_hi<IN_F16>(int w) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)((unsigned)w >> 16));
 }
 
+// Four e4m3 values (one dword) -> four bf16 values (two dwords), exactly.
+__device__ __forceinline__ i32x2 e4m3x4_to_bf16(int w) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return i32x2{__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+}
+
 // Output conversion of four consecutive values of a row.
 template <int OUT> struct Out;
 template <> struct Out<OUT_F32> {
     static constexpr int EB = 4;
     __device__ static void store4(uint8_t* dst, float a, float b, float c, float d) {
-        float4 v = make_float4(a, b, c, d);
-        *reinterpret_cast<float4*>(dst) = v;
+        *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
     }
 };
 template <> struct Out<OUT_BF16> {
     static constexpr int EB = 2;
     __device__ static void store4(uint8_t* dst, float a, float b, float c, float d) {
-        i32x2 v = {pack2<IN_BF16>(a, b), pack2<IN_BF16>(c, d)};
-        *reinterpret_cast<i32x2*>(dst) = v;
+        *reinterpret_cast<i32x2*>(dst) = i32x2{pack2<IN_BF16>(a, b), pack2<IN_BF16>(c, d)};
     }
 };
 template <> struct Out<OUT_F16> {
     static constexpr int EB = 2;
     __device__ static void store4(uint8_t* dst, float a, float b, float c, float d) {
-        i32x2 v = {pack2<IN_F16>(a, b), pack2<IN_F16>(c, d)};
-        *reinterpret_cast<i32x2*>(dst) = v;
+        *reinterpret_cast<i32x2*>(dst) = i32x2{pack2<IN_F16>(a, b), pack2<IN_F16>(c, d)};
     }
 };
 
-// Value of lane l^32 (the other half of the wave) combined with this lane's.
+// This lane's value combined with lane l^32's (the other half of the wave).
 __device__ __forceinline__ float max_halves(float x) {
     auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
@@ -169,21 +177,21 @@ __device__ __forceinline__ int v8_row(int x) {
 template <int IN, int OUT, int D, int QB>
 __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     typedef In<IN> I;
-    typedef typename OpT<I::OPW>::type Op;
-    constexpr int EB = I::EB;
-    constexpr int RB = D * EB;               // bytes per row
-    constexpr int CPR = RB / 16;             // 16-byte chunks per row
-    constexpr int TILE = BC * RB;            // bytes of one K or V tile
-    constexpr int LDT = BC * CPR / NTHREADS; // chunks each thread stages per tile
-    constexpr int NKS = D / I::KSTEP;        // MFMA steps of the score product
-    constexpr int OPB = I::OPW * 4;          // bytes of one MFMA operand per lane
-    constexpr int ND = D / 32;               // 32-wide blocks of the head dim
-    constexpr int QW = 32 * QB;              // query rows per wave
-    constexpr int BR = WAVES * QW;
+    constexpr int QK = I::QK;
     constexpr bool FP8 = (IN == IN_E4M3);
-    static_assert(LDT >= 1 && (BC * CPR) % NTHREADS == 0, "tile staging");
+    constexpr int GRB = D * I::EB;             // bytes per row in HBM (q, k, v)
+    constexpr int KRB = D * 2;                 // bytes per K row in LDS (16-bit)
+    constexpr int VRB = D * I::EB;             // bytes per V row in LDS
+    constexpr int KTILE = BC * KRB, VTILE = BC * VRB, STAGE = KTILE + VTILE;
+    constexpr int GCPR = GRB / 16;             // 16-byte chunks per HBM row
+    constexpr int GLD = BC * GCPR / NTHREADS;  // chunks per tensor each thread stages per tile
+    constexpr int NKS = D / 16;                // steps of the score MFMA over D
+    constexpr int ND = D / 32;                 // 32-wide blocks of the head dim
+    constexpr int QW = 32 * QB;                // query rows per wave
+    constexpr int BR = WAVES * QW;
+    static_assert(GLD >= 1 && (BC * GCPR) % NTHREADS == 0, "tile staging");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -204,34 +212,47 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     const int w0 = r0 + wave * QW;
     const int w1 = min(w0 + QW, Nq);
 
-    const uint8_t* qp = p.q + (size_t)bh * Nq * RB;
-    const uint8_t* kp = p.k + (size_t)bh * Nk * RB;
-    const uint8_t* vp = p.v + (size_t)bh * Nk * RB;
+    const uint8_t* qp = p.q + (size_t)bh * Nq * GRB;
+    const uint8_t* kp = p.k + (size_t)bh * Nk * GRB;
+    const uint8_t* vp = p.v + (size_t)bh * Nk * GRB;
 
-    // ---- Q fragments (B operand of S^T = K Q^T): lane holds query w0+32qb+l32,
-    // bytes [s*KSTEP*EB + hh*OPB, +OPB) of its row.
-    Op qf[QB][NKS];
+    // ---- per-row state. Row i = w0 + 32qb + l32 sees keys [klo, khi).
+    int klo[QB], khi[QB];
+    bool split_any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int i = w0 + 32 * qb + l32;
+        klo[qb] = 0;
+        khi[qb] = 0;
+        if (i < w1) kv_range(i, i + 1, Nq, Nk, causal, window, &klo[qb], &khi[qb]);
+        // Few visible keys make P's rounding the dominant error: such rows
+        // also multiply V by P's rounding residual (P = hi + lo).
+        if constexpr (!FP8) split_any |= (i < w1) && (khi[qb] - klo[qb] < 256);
+    }
+    const bool split = __builtin_amdgcn_ballot_w64(split_any) != 0;
+
+    // ---- Q fragments, B operand of S^T = K Q^T: lane holds query
+    // w0+32qb+l32, head-dim elements [16s + 8hh, +8), as 16-bit values.
+    i32x4 qf[QB][NKS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = w0 + 32 * qb + l32;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             if (row < Nq) {
-                const uint8_t* src = qp + (size_t)row * RB + s * I::KSTEP * EB + hh * OPB;
-                if constexpr (I::OPW == 4) {
-                    qf[qb][s] = *reinterpret_cast<const i32x4*>(src);
+                if constexpr (!FP8) {
+                    qf[qb][s] = *reinterpret_cast<const i32x4*>(qp + (size_t)row * GRB + (16 * s + 8 * hh) * 2);
                 } else {
-                    const i32x4 a = *reinterpret_cast<const i32x4*>(src);
-                    const i32x4 b = *reinterpret_cast<const i32x4*>(src + 16);
-                    qf[qb][s] = Op{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+                    const i32x2 w8 = *reinterpret_cast<const i32x2*>(qp + (size_t)row * GRB + 16 * s + 8 * hh);
+                    const i32x2 a = e4m3x4_to_bf16(w8[0]), b = e4m3x4_to_bf16(w8[1]);
+                    qf[qb][s] = i32x4{a[0], a[1], b[0], b[1]};
                 }
             } else {
-                qf[qb][s] = Op{};
+                qf[qb][s] = i32x4{};
             }
         }
     }
 
-    // ---- accumulators and softmax state
     f32x16 oacc[ND][QB];
 #pragma unroll
     for (int db = 0; db < ND; ++db)
@@ -239,41 +260,23 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x16{};
     float m_run[QB], l_run[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
-
-    // Few visible keys per row make P's rounding the dominant error, so rows
-    // that see fewer than 256 keys also multiply V by the rounding residual
-    // of P (P = hi + lo). The choice is per row (lane); other rows of the
-    // wave get lo = 0, which adds exactly nothing.
-    bool split_row[QB];
-    bool split_any = false;
-#pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        split_row[qb] = false;
-        if constexpr (!FP8) {
-            const int i = w0 + 32 * qb + l32;
-            if (i < w1) {
-                int a0, a1;
-                kv_range(i, i + 1, Nq, Nk, causal, window, &a0, &a1);
-                split_row[qb] = (a1 - a0) < 256;
-            }
-        }
-        split_any |= split_row[qb];
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.f;
     }
-    const bool split = __builtin_amdgcn_ballot_w64(split_any) != 0;
 
-    // ---- staging of K/V tiles: global -> registers -> LDS
-    i32x4 stk[LDT], stv[LDT];
+    // ---- K/V tile staging: HBM -> registers (issued a tile ahead) -> LDS
+    i32x4 stk[GLD], stv[GLD];
     auto load_tile = [&](int t) {
         const int kv0 = t * BC;
 #pragma unroll
-        for (int i = 0; i < LDT; ++i) {
+        for (int i = 0; i < GLD; ++i) {
             const int ci = tid + NTHREADS * i;
-            const int x = ci / CPR, c = ci % CPR;
-            const int kv = kv0 + x;
-            if (kv < Nk) {
-                stk[i] = *reinterpret_cast<const i32x4*>(kp + (size_t)kv * RB + c * 16);
-                stv[i] = *reinterpret_cast<const i32x4*>(vp + (size_t)kv * RB + c * 16);
+            const int x = ci / GCPR, c = ci % GCPR;
+            if (kv0 + x < Nk) {
+                const size_t off = (size_t)(kv0 + x) * GRB + c * 16;
+                stk[i] = *reinterpret_cast<const i32x4*>(kp + off);
+                stv[i] = *reinterpret_cast<const i32x4*>(vp + off);
             } else {
                 stk[i] = i32x4{};
                 stv[i] = i32x4{};
@@ -281,15 +284,23 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
         }
     };
     auto store_tile = [&](int buf) {
-        uint8_t* kb = smem + buf * 2 * TILE;
-        uint8_t* vb = kb + TILE;
+        uint8_t* kb = smem + buf * STAGE;
+        uint8_t* vb = kb + KTILE;
 #pragma unroll
-        for (int i = 0; i < LDT; ++i) {
+        for (int i = 0; i < GLD; ++i) {
             const int ci = tid + NTHREADS * i;
-            const int x = ci / CPR, c = ci % CPR;
-            *reinterpret_cast<i32x4*>(kb + lds_off<RB>(x, c)) = stk[i];
-            const int xv = FP8 ? v8_row(x) : x;
-            *reinterpret_cast<i32x4*>(vb + lds_off<RB>(xv, c)) = stv[i];
+            const int x = ci / GCPR, c = ci % GCPR;
+            if constexpr (!FP8) {
+                *reinterpret_cast<i32x4*>(kb + lds_off<KRB>(x, c)) = stk[i];
+                *reinterpret_cast<i32x4*>(vb + lds_off<VRB>(x, c)) = stv[i];
+            } else {
+                const i32x2 a = e4m3x4_to_bf16(stk[i][0]), b = e4m3x4_to_bf16(stk[i][1]);
+                const i32x2 e = e4m3x4_to_bf16(stk[i][2]), f = e4m3x4_to_bf16(stk[i][3]);
+                *reinterpret_cast<i32x4*>(kb + lds_off<KRB>(x, 2 * c)) = i32x4{a[0], a[1], b[0], b[1]};
+                *reinterpret_cast<i32x4*>(kb + lds_off<KRB>(x, 2 * c + 1)) = i32x4{e[0], e[1], f[0], f[1]};
+                const int xv = v8_row(x);
+                *reinterpret_cast<i32x4*>(vb + lds_off<VRB>(xv, c)) = stv[i];
+            }
         }
     };
 
@@ -300,6 +311,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     __syncthreads();
 
     const float c2 = p.c;
+    const int g = lane >> 4, cl = lane & 15;   // 16-lane group of the transposing reads
     for (int t = t_lo; t < t_hi; ++t) {
         const bool more = (t + 1 < t_hi);
         if (more) load_tile(t + 1);
@@ -307,10 +319,10 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
         const int c0 = t * BC;
         const int cls = tile_class(w0, w1, c0, c0 + BC, Nq, Nk, causal, window);
         if (cls != TILE_SKIP) {
-            const lds_u8* kbuf = (const lds_u8*)(smem + (t & 1) * 2 * TILE);
-            const lds_u8* vbuf = kbuf + TILE;
+            const lds_u8* kbuf = (const lds_u8*)(smem + (t & 1) * STAGE);
+            const lds_u8* vbuf = kbuf + KTILE;
 
-            // ---- S^T = K Q^T for the 64 keys of the tile (2 blocks of 32)
+            // ---- S^T = K Q^T over the tile's 64 keys (2 blocks of 32)
             f32x16 sacc[2][QB];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -320,41 +332,33 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
             for (int s = 0; s < NKS; ++s) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const int x = 32 * kb + l32;
-                    const int ch = (s * I::KSTEP * EB + hh * OPB) >> 4;
-                    Op a;
-                    if constexpr (I::OPW == 4) {
-                        a = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(kbuf + lds_off<RB>(x, ch));
-                    } else {
-                        const i32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(kbuf + lds_off<RB>(x, ch));
-                        const i32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(kbuf + lds_off<RB>(x, ch + 1));
-                        a = Op{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-                    }
+                    const i32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+                        kbuf + lds_off<KRB>(32 * kb + l32, 2 * s + hh));
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma<IN>(a, qf[qb][s], sacc[kb][qb]);
+                    for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma16(QK, a, qf[qb][s], sacc[kb][qb]);
                 }
             }
 
-            // ---- mask (edge tiles only): key of accumulator element r of
-            // block kb is c0 + 32kb + 8(r/4) + 4hh + r%4; query is w0+32qb+l32.
+            // ---- mask (edge tiles only). Element r of block kb holds key
+            // c0 + 4hh + off with off = 32kb + 8(r/4) + r%4.
             if (cls == TILE_EDGE) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    const int i = w0 + 32 * qb + l32;
+                    const int a = klo[qb] - c0 - 4 * hh, b = khi[qb] - c0 - 4 * hh;
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                            if (!visible(i, j, Nq, Nk, causal, window)) sacc[kb][qb][r] = -INFINITY;
+                            const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+                            if (off < a || off >= b) sacc[kb][qb][r] = -INFINITY;
                         }
                 }
             }
 
             // ---- online softmax (base 2). A row rescales only when its own
             // tile max passes its reference max by more than TAU; the other
-            // rows of the wave keep alpha = 1 (an exact no-op), so each row's
-            // arithmetic depends on its own scores alone.
+            // rows keep alpha = 1 (an exact no-op), so each row's arithmetic
+            // depends on its own scores alone.
             float alpha[QB];
             bool need = false;
 #pragma unroll
@@ -396,56 +400,52 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
 
             // ---- O^T += V^T P^T
             if constexpr (!FP8) {
-                // k-step s covers keys 16s..16s+15 of the tile; lane half hh
-                // supplies accumulator elements r = 8(s%2)+e of block s/2, i.e.
-                // keys 16s + 8(e/4) + 4hh + e%4.
-                Op pf[QB][4], pl[QB][4];
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const f32x16& e = sacc[s >> 1][qb];
-                        const int o = 8 * (s & 1);
-                        pf[qb][s] = Op{pack2<IN>(e[o + 0], e[o + 1]), pack2<IN>(e[o + 2], e[o + 3]),
-                                       pack2<IN>(e[o + 4], e[o + 5]), pack2<IN>(e[o + 6], e[o + 7])};
-                        if (split) {
-                            Op h = pf[qb][s];
-                            pl[qb][s] = !split_row[qb] ? Op{} : Op{pack2<IN>(e[o + 0] - unpack_lo<IN>(h[0]), e[o + 1] - unpack_hi<IN>(h[0])),
-                                           pack2<IN>(e[o + 2] - unpack_lo<IN>(h[1]), e[o + 3] - unpack_hi<IN>(h[1])),
-                                           pack2<IN>(e[o + 4] - unpack_lo<IN>(h[2]), e[o + 5] - unpack_hi<IN>(h[2])),
-                                           pack2<IN>(e[o + 6] - unpack_lo<IN>(h[3]), e[o + 7] - unpack_hi<IN>(h[3]))};
-                        }
-                    }
-                // V^T fragment: lane (group g = lane/16, c = lane%16) reads,
-                // with ds_read_b64_tr_b16, 4 rows x 16 columns per group and
-                // receives column 32db + 16(g%2) + c of those 4 rows.
-                const int g = lane >> 4, cl = lane & 15;
+                // k-step s covers the tile's keys 16s..16s+15: lane half hh
+                // supplies accumulator elements r = 8(s%2)+e of block s/2,
+                // i.e. keys 16s + 8(e/4) + 4hh + e%4, and the V^T operand is
+                // read in that order by two ds_read_b64_tr_b16 (4 rows x 16
+                // columns per 16-lane group; lane receives one column).
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
+                    i32x4 pf[QB], pl[QB];
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        const f32x16& e = sacc[s >> 1][qb];
+                        const int o = 8 * (s & 1);
+                        pf[qb] = i32x4{pack2<IN>(e[o + 0], e[o + 1]), pack2<IN>(e[o + 2], e[o + 3]),
+                                       pack2<IN>(e[o + 4], e[o + 5]), pack2<IN>(e[o + 6], e[o + 7])};
+                        if (split) {
+                            const bool sr = (khi[qb] - klo[qb]) < 256;
+                            const i32x4 h = pf[qb];
+                            pl[qb] = sr ? i32x4{pack2<IN>(e[o + 0] - unpack_lo<IN>(h[0]), e[o + 1] - unpack_hi<IN>(h[0])),
+                                                pack2<IN>(e[o + 2] - unpack_lo<IN>(h[1]), e[o + 3] - unpack_hi<IN>(h[1])),
+                                                pack2<IN>(e[o + 4] - unpack_lo<IN>(h[2]), e[o + 5] - unpack_hi<IN>(h[2])),
+                                                pack2<IN>(e[o + 6] - unpack_lo<IN>(h[3]), e[o + 7] - unpack_hi<IN>(h[3]))}
+                                        : i32x4{};
+                        }
+                    }
 #pragma unroll
                     for (int db = 0; db < ND; ++db) {
-                        const int d0 = 32 * db + 16 * (g & 1);
-                        const int ch = (2 * d0 + 8 * (cl & 3)) >> 4;
+                        const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
                         const int x0 = 16 * s + 4 * hh + (cl >> 2);
-                        const int x1 = x0 + 8;
                         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(vbuf + lds_off<RB>(x0, ch) + 8 * (cl & 1)));
+                            (__attribute__((address_space(3))) i16x4*)(vbuf + lds_off<VRB>(x0, ch) + 8 * (cl & 1)));
                         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(vbuf + lds_off<RB>(x1, ch) + 8 * (cl & 1)));
-                        const i32x2 w0v = __builtin_bit_cast(i32x2, v0);
-                        const i32x2 w1v = __builtin_bit_cast(i32x2, v1);
-                        const Op a = Op{w0v[0], w0v[1], w1v[0], w1v[1]};
+                            (__attribute__((address_space(3))) i16x4*)(vbuf + lds_off<VRB>(x0 + 8, ch) + 8 * (cl & 1)));
+                        const i32x2 u0 = __builtin_bit_cast(i32x2, v0), u1 = __builtin_bit_cast(i32x2, v1);
+                        const i32x4 a = i32x4{u0[0], u0[1], u1[0], u1[1]};
 #pragma unroll
                         for (int qb = 0; qb < QB; ++qb) {
-                            oacc[db][qb] = mfma<IN>(a, pf[qb][s], oacc[db][qb]);
-                            if (split) oacc[db][qb] = mfma<IN>(a, pl[qb][s], oacc[db][qb]);
+                            oacc[db][qb] = mfma16(IN, a, pf[qb], oacc[db][qb]);
+                            if (split) oacc[db][qb] = mfma16(IN, a, pl[qb], oacc[db][qb]);
                         }
                     }
                 }
             } else {
                 // One k-step of 64 keys: element t of lane half hh is
-                // accumulator element (block t/16, r = t%16).
-                Op pf[QB];
+                // accumulator element (block t/16, r = t%16); V^T comes from
+                // 4 ds_read_b64_tr_b8 of LDS rows 32hh + 8u + 0..7.
+                i32x8 pf[QB];
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -457,24 +457,20 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
                         pf[qb][w] = word;
                     }
                 }
-                // V^T fragment: 4 ds_read_b64_tr_b8, each 8 LDS rows x 16
-                // columns per 16-lane group; LDS rows 32hh + 8u + 0..7.
-                const int g = lane >> 4, cl = lane & 15;
 #pragma unroll
                 for (int db = 0; db < ND; ++db) {
-                    const int d0 = 32 * db + 16 * (g & 1);
-                    const int ch = d0 >> 4;
-                    Op a;
+                    const int ch = (32 * db + 16 * (g & 1)) >> 4;
+                    i32x8 a;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int x = 32 * hh + 8 * u + (cl >> 1);
                         const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                            (__attribute__((address_space(3))) i32x2*)(vbuf + lds_off<RB>(x, ch) + 8 * (cl & 1)));
+                            (__attribute__((address_space(3))) i32x2*)(vbuf + lds_off<VRB>(x, ch) + 8 * (cl & 1)));
                         a[2 * u] = r[0];
                         a[2 * u + 1] = r[1];
                     }
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma<IN>(a, pf[qb], oacc[db][qb]);
+                    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma_fp8(a, pf[qb], oacc[db][qb]);
                 }
             }
         }
@@ -524,6 +520,12 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq) {
         const long long wg2 = n_bh * ((Nq + 255) / 256);
         if (wg2 < 512) qb = 1;
     }
+    // Tuning override: FA_TILE_QB=1|2 forces the query blocks per wave (D = 64
+    // only; D = 128 keeps one block to stay within the register file).
+    if (const char* e = getenv("FA_TILE_QB")) {
+        const int f = atoi(e);
+        if ((f == 1 || f == 2) && (D == 64 || f == 1)) qb = f;
+    }
     pl.qb = qb;
     pl.br = WAVES * 32 * qb;
     pl.n_qt = (Nq + pl.br - 1) / pl.br;
@@ -539,7 +541,10 @@ static int launch_one(const Plan& pl, const Params& p, hipStream_t s) {
 
 template <int IN, int OUT, int D>
 static int launch_d(const Plan& pl, const Params& p, hipStream_t s) {
-    return pl.qb == 2 ? launch_one<IN, OUT, D, 2>(pl, p, s) : launch_one<IN, OUT, D, 1>(pl, p, s);
+    if constexpr (D == 64) {
+        if (pl.qb == 2) return launch_one<IN, OUT, D, 2>(pl, p, s);
+    }
+    return launch_one<IN, OUT, D, 1>(pl, p, s);
 }
 
 template <int IN, int OUT>

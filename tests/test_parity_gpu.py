@@ -10,7 +10,9 @@ The five workloads run at full size in the launch configuration the benchmark
 times, compared on sampled rows the oracle computes one by one; smaller
 shapes that span several tiles with ragged tails are compared in full.
 """
+import json
 import math
+import os
 
 import pytest
 import torch
@@ -70,6 +72,10 @@ def compare(w, O, L, Oref, Lref, label=""):
         stats["lse_rel"] = lerr
         assert lerr <= LSE_BOUND, f"{label}: LSE rel err {lerr:.3e} > {LSE_BOUND}"
     print(f"{label}: {stats}", flush=True)
+    log = os.environ.get("FA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": label, **stats}) + "\n")
     return stats
 
 
@@ -129,6 +135,24 @@ DTYPES = [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32"), ("e
 def test_small_shapes(B, H, Nq, Nk, causal, window, D, din, dout):
     seed = 1000 + B * 7 + H * 13 + Nq * 3 + Nk + D + (17 if causal else 0) + window
     w = synth.small_workload(f"B{B}H{H}q{Nq}k{Nk}D{D}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, D,
+                             causal, window, din, dout, seed,
+                             outlier_frac=0.001 if din == "e4m3" else 0.0, outlier_mult=20.0)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", [(2, 3, 300, 300), (1, 2, 200, 333), (1, 2, 333, 200), (1, 1, 1000, 64),
+                                       (1, 3, 700, 700)])
+@pytest.mark.parametrize("causal,window", MODES)
+@pytest.mark.parametrize("din,dout", DTYPES)
+def test_two_query_blocks_per_wave(monkeypatch, B, H, Nq, Nk, causal, window, din, dout):
+    # The tile shape with 64 query rows per wave (used for large D = 64
+    # problems) on shapes small enough to compare in full.
+    monkeypatch.setenv("FA_TILE_QB", "2")
+    seed = 2000 + B * 7 + H * 13 + Nq * 3 + Nk + (17 if causal else 0) + window
+    w = synth.small_workload(f"qb2_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, 64,
                              causal, window, din, dout, seed,
                              outlier_frac=0.001 if din == "e4m3" else 0.0, outlier_mult=20.0)
     inp = synth.make_inputs(w)
