@@ -10,6 +10,7 @@ SOURCES = ["fa_fwd.hip", "fa_api.hip"]
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32.
 HIPFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]

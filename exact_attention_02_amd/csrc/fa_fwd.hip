@@ -174,6 +174,35 @@ __device__ __forceinline__ int v8_row(int x) {
     return (h << 5) | (blk << 4) | (a << 2) | b;
 }
 
+__device__ __forceinline__ int v8_row_inv(int xv) {
+    const int h = xv >> 5, blk = (xv >> 4) & 1, a = (xv >> 2) & 3, b = xv & 3;
+    return (blk << 5) | (a << 3) | (h << 2) | b;
+}
+
+// Buffer resource over [base, base + bytes): loads beyond `bytes` return
+// zeros (and write zeros to LDS), so tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// The same descriptor as four dwords (base, stride 0, byte count, raw format).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
+    const unsigned long long a = (unsigned long long)base;
+    return i32x4{(int)(a & 0xffffffffu), (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address
+// lds_base + 16*l (lds_base wave-uniform). Issued from asm so that the
+// compiler does not hold every later transposing LDS read until all such
+// copies land; completion is awaited explicitly (vmcnt(0)) before the barrier
+// that publishes the tile. The block writes no register, and m0 is set here:
+// gfx950 does not use m0 for ordinary LDS access.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, unsigned lds_base, unsigned voff) {
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(lds_base), "s"(rsrc)
+                 : "memory", "m0");
+}
+
 template <int IN, int OUT, int D, int QB>
 __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     typedef In<IN> I;
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
@@ -218,39 +247,38 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
 
     // ---- per-row state. Row i = w0 + 32qb + l32 sees keys [klo, khi).
     int klo[QB], khi[QB];
-    bool split_any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int i = w0 + 32 * qb + l32;
         klo[qb] = 0;
         khi[qb] = 0;
         if (i < w1) kv_range(i, i + 1, Nq, Nk, causal, window, &klo[qb], &khi[qb]);
-        // Few visible keys make P's rounding the dominant error: such rows
-        // also multiply V by P's rounding residual (P = hi + lo).
-        if constexpr (!FP8) split_any |= (i < w1) && (khi[qb] - klo[qb] < 256);
     }
-    const bool split = __builtin_amdgcn_ballot_w64(split_any) != 0;
 
     // ---- Q fragments, B operand of S^T = K Q^T: lane holds query
     // w0+32qb+l32, head-dim elements [16s + 8hh, +8), as 16-bit values.
     i32x4 qf[QB][NKS];
+    {
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)(Nq * GRB));
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = w0 + 32 * qb + l32;
+        for (int qb = 0; qb < QB; ++qb) {
+            const int row = w0 + 32 * qb + l32;
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            if (row < Nq) {
+            for (int s = 0; s < NKS; ++s) {
                 if constexpr (!FP8) {
-                    qf[qb][s] = *reinterpret_cast<const i32x4*>(qp + (size_t)row * GRB + (16 * s + 8 * hh) * 2);
+                    qf[qb][s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        qrs, row * GRB + (16 * s + 8 * hh) * 2, 0, 0));
                 } else {
-                    const i32x2 w8 = *reinterpret_cast<const i32x2*>(qp + (size_t)row * GRB + 16 * s + 8 * hh);
+                    const i32x2 w8 = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                        qrs, row * GRB + 16 * s + 8 * hh, 0, 0));
                     const i32x2 a = e4m3x4_to_bf16(w8[0]), b = e4m3x4_to_bf16(w8[1]);
                     qf[qb][s] = i32x4{a[0], a[1], b[0], b[1]};
                 }
-            } else {
-                qf[qb][s] = i32x4{};
             }
         }
+        // Q has landed before the loop, so no wait inside the loop is left
+        // for the compiler to place (where it would also cover the K/V copies).
+        __builtin_amdgcn_s_waitcnt(0x0F70);
     }
 
     f32x16 oacc[ND][QB];
@@ -265,48 +293,70 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
         l_run[qb] = 0.f;
     }
 
-    // ---- K/V tile staging: HBM -> registers (issued a tile ahead) -> LDS
-    i32x4 stk[GLD], stv[GLD];
-    auto load_tile = [&](int t) {
+    // ---- K/V tile staging, issued a tile ahead. 16-bit K and V, and e4m3 V,
+    // go HBM -> LDS directly (buffer_load ... lds: lane l of a wave fills the
+    // l-th 16-byte slot of a 1 KiB run), each lane fetching the global chunk
+    // that belongs in its slot under the swizzled layout. e4m3 K passes
+    // through registers to be widened to bf16 on its way into LDS.
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)(Nk * GRB));
+    const i32x4 kwords = rsrc_words(kp, (unsigned)(Nk * GRB));
+    const i32x4 vwords = rsrc_words(vp, (unsigned)(Nk * GRB));
+    const unsigned smem_base = (unsigned)(unsigned long long)(lds_u8*)smem;
+    constexpr int KSLOTS = KTILE / 16, VSLOTS = VTILE / 16;
+    constexpr int KCPR = KRB / 16, VCPR = VRB / 16;
+    constexpr int KSW = KCPR < 8 ? KCPR : 8, VSW = VCPR < 8 ? VCPR : 8;
+    i32x4 stk[FP8 ? GLD : 1];
+    auto issue_tile = [&](int t, int buf) {
         const int kv0 = t * BC;
+        const unsigned kb = smem_base + buf * STAGE;
+        const unsigned vb = kb + KTILE;
+        if constexpr (!FP8) {
 #pragma unroll
-        for (int i = 0; i < GLD; ++i) {
-            const int ci = tid + NTHREADS * i;
-            const int x = ci / GCPR, c = ci % GCPR;
-            if (kv0 + x < Nk) {
-                const size_t off = (size_t)(kv0 + x) * GRB + c * 16;
-                stk[i] = *reinterpret_cast<const i32x4*>(kp + off);
-                stv[i] = *reinterpret_cast<const i32x4*>(vp + off);
-            } else {
-                stk[i] = i32x4{};
-                stv[i] = i32x4{};
+            for (int i = 0; i < KSLOTS / NTHREADS; ++i) {
+                const int run = 64 * wave + NTHREADS * i;     // first slot of this wave's run
+                const int slot = run + lane;
+                const int x = slot / KCPR, c = (slot % KCPR) ^ (x & (KSW - 1));
+                dma16(kwords, kb + run * 16, (kv0 + x) * GRB + c * 16);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < GLD; ++i) {
+                const int ci = tid + NTHREADS * i;
+                const int x = ci / GCPR, c = ci % GCPR;
+                stk[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (kv0 + x) * GRB + c * 16, 0, 0));
             }
         }
-    };
-    auto store_tile = [&](int buf) {
-        uint8_t* kb = smem + buf * STAGE;
-        uint8_t* vb = kb + KTILE;
 #pragma unroll
-        for (int i = 0; i < GLD; ++i) {
-            const int ci = tid + NTHREADS * i;
-            const int x = ci / GCPR, c = ci % GCPR;
-            if constexpr (!FP8) {
-                *reinterpret_cast<i32x4*>(kb + lds_off<KRB>(x, c)) = stk[i];
-                *reinterpret_cast<i32x4*>(vb + lds_off<VRB>(x, c)) = stv[i];
-            } else {
+        for (int i = 0; i < VSLOTS / NTHREADS; ++i) {
+            const int run = 64 * wave + NTHREADS * i;
+            const int slot = run + lane;
+            const int xv = slot / VCPR, c = (slot % VCPR) ^ (xv & (VSW - 1));
+            const int x = FP8 ? v8_row_inv(xv) : xv;
+            dma16(vwords, vb + run * 16, (kv0 + x) * GRB + c * 16);
+        }
+    };
+    // e4m3 K: widen the staged chunks to bf16 and write them to LDS.
+    auto finish_tile = [&](int buf) {
+        if constexpr (FP8) {
+            uint8_t* kb = smem + buf * STAGE;
+#pragma unroll
+            for (int i = 0; i < GLD; ++i) {
+                const int ci = tid + NTHREADS * i;
+                const int x = ci / GCPR, c = ci % GCPR;
                 const i32x2 a = e4m3x4_to_bf16(stk[i][0]), b = e4m3x4_to_bf16(stk[i][1]);
                 const i32x2 e = e4m3x4_to_bf16(stk[i][2]), f = e4m3x4_to_bf16(stk[i][3]);
                 *reinterpret_cast<i32x4*>(kb + lds_off<KRB>(x, 2 * c)) = i32x4{a[0], a[1], b[0], b[1]};
                 *reinterpret_cast<i32x4*>(kb + lds_off<KRB>(x, 2 * c + 1)) = i32x4{e[0], e[1], f[0], f[1]};
-                const int xv = v8_row(x);
-                *reinterpret_cast<i32x4*>(vb + lds_off<VRB>(xv, c)) = stv[i];
             }
         }
+        // the direct-to-LDS loads of this tile have landed (vmcnt(0)); the
+        // barrier that follows publishes them to the other waves
+        __builtin_amdgcn_s_waitcnt(0x0F70);
     };
 
     if (t_lo < t_hi) {
-        load_tile(t_lo);
-        store_tile(t_lo & 1);
+        issue_tile(t_lo, t_lo & 1);
+        finish_tile(t_lo & 1);
     }
     __syncthreads();
 
@@ -314,7 +364,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     const int g = lane >> 4, cl = lane & 15;   // 16-lane group of the transposing reads
     for (int t = t_lo; t < t_hi; ++t) {
         const bool more = (t + 1 < t_hi);
-        if (more) load_tile(t + 1);
+        if (more) issue_tile(t + 1, (t + 1) & 1);
 
         const int c0 = t * BC;
         const int cls = tile_class(w0, w1, c0, c0 + BC, Nq, Nk, causal, window);
@@ -359,7 +409,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
             // tile max passes its reference max by more than TAU; the other
             // rows keep alpha = 1 (an exact no-op), so each row's arithmetic
             // depends on its own scores alone.
-            float alpha[QB];
+            float alpha[QB], mt[QB];
             bool need = false;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -369,10 +419,10 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
                 mx = max_halves(mx);
-                const float mt = mx * c2;
-                const bool nd = mt > m_run[qb] + I::TAU;
-                alpha[qb] = nd ? __builtin_amdgcn_exp2f(m_run[qb] - mt) : 1.f;
-                m_run[qb] = nd ? mt : m_run[qb];
+                mt[qb] = mx * c2;
+                const bool nd = mt[qb] > m_run[qb] + I::TAU;
+                alpha[qb] = nd ? __builtin_amdgcn_exp2f(m_run[qb] - mt[qb]) : 1.f;
+                m_run[qb] = nd ? mt[qb] : m_run[qb];
                 need |= nd;
             }
             if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -383,6 +433,21 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
                     for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha[qb];
                 }
             }
+            // Rounding P to 16 bits costs up to 2^-9 (bf16) of each weight;
+            // averaged over many comparable weights that is negligible, but a
+            // row whose tile holds a weight above 1/32 of the row's running sum
+            // (its first tile, rows with few keys, peaked rows) also multiplies
+            // V by P's rounding residual, P = hi + lo. Other rows get lo = 0,
+            // an exact no-op.
+            bool sr[QB];
+            bool sp_any = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float ms = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+                sr[qb] = !FP8 && (__builtin_amdgcn_exp2f(mt[qb] - ms) * 32.f > l_run[qb]);
+                sp_any |= sr[qb];
+            }
+            const bool split = __builtin_amdgcn_ballot_w64(sp_any) != 0;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const float ms = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
@@ -415,9 +480,8 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
                         pf[qb] = i32x4{pack2<IN>(e[o + 0], e[o + 1]), pack2<IN>(e[o + 2], e[o + 3]),
                                        pack2<IN>(e[o + 4], e[o + 5]), pack2<IN>(e[o + 6], e[o + 7])};
                         if (split) {
-                            const bool sr = (khi[qb] - klo[qb]) < 256;
                             const i32x4 h = pf[qb];
-                            pl[qb] = sr ? i32x4{pack2<IN>(e[o + 0] - unpack_lo<IN>(h[0]), e[o + 1] - unpack_hi<IN>(h[0])),
+                            pl[qb] = sr[qb] ? i32x4{pack2<IN>(e[o + 0] - unpack_lo<IN>(h[0]), e[o + 1] - unpack_hi<IN>(h[0])),
                                                 pack2<IN>(e[o + 2] - unpack_lo<IN>(h[1]), e[o + 3] - unpack_hi<IN>(h[1])),
                                                 pack2<IN>(e[o + 4] - unpack_lo<IN>(h[2]), e[o + 5] - unpack_hi<IN>(h[2])),
                                                 pack2<IN>(e[o + 6] - unpack_lo<IN>(h[3]), e[o + 7] - unpack_hi<IN>(h[3]))}
@@ -475,7 +539,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
             }
         }
 
-        if (more) store_tile((t + 1) & 1);
+        if (more) finish_tile((t + 1) & 1);
         __syncthreads();
     }
 
