@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 512 MiB device-to-device copy (to scale the FETCH_SIZE/WRITE_SIZE "
+                         "counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -119,6 +122,16 @@ def main():
     import torch
     import exact_attention_02_amd as fa
     import synth
+
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
+        return
 
     w = synth.WORKLOADS[args.workload]
     inp = synth.make_inputs(w)

@@ -203,6 +203,23 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, unsigned lds_base, unsi
                  : "memory", "m0");
 }
 
+// Rounding P to 16 bits costs up to 2^-9 (bf16) of each weight. Averaged over
+// many comparable weights that is negligible (the output's own rounding
+// dominates), but a row whose tile holds a weight above a quarter of the row's
+// sum so far, this tile included -- its first tile, rows with few keys, peaked
+// rows -- also multiplies V by P's rounding residual, P = hi + lo, so no
+// dominant weight's rounding reaches the output. The decision is taken before
+// the tile's exponentials: the tile adds at least pmax to the sum, so
+// 3 * pmax > (sum before the tile) covers every case of 4 * pmax > (sum with
+// the tile). Other rows get lo = 0, an exact no-op. pmax is the tile's
+// largest exponentiated score, lhalf this lane half's share of the rescaled
+// sum before the tile.
+__device__ __forceinline__ bool split_row(float pmax, float lhalf) {
+    auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(lhalf), __float_as_uint(lhalf), false, false);
+    const float l = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+    return pmax * 3.f > l;
+}
+
 template <int IN, int OUT, int D, int QB>
 __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     typedef In<IN> I;
@@ -433,18 +450,12 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
                     for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha[qb];
                 }
             }
-            // Rounding P to 16 bits costs up to 2^-9 (bf16) of each weight;
-            // averaged over many comparable weights that is negligible, but a
-            // row whose tile holds a weight above 1/32 of the row's running sum
-            // (its first tile, rows with few keys, peaked rows) also multiplies
-            // V by P's rounding residual, P = hi + lo. Other rows get lo = 0,
-            // an exact no-op.
             bool sr[QB];
             bool sp_any = false;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const float ms = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-                sr[qb] = !FP8 && (__builtin_amdgcn_exp2f(mt[qb] - ms) * 32.f > l_run[qb]);
+                sr[qb] = !FP8 && split_row(__builtin_amdgcn_exp2f(mt[qb] - ms), l_run[qb]);
                 sp_any |= sr[qb];
             }
             const bool split = __builtin_amdgcn_ballot_w64(sp_any) != 0;

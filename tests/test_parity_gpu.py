@@ -68,8 +68,13 @@ def compare(w, O, L, Oref, Lref, label=""):
             err = d.abs().max().item()
             stats["max_abs"] = err
             assert err <= O_BOUND[w.in_dtype], f"{label}: max abs err {err:.3e} > {O_BOUND[w.in_dtype]}"
-        lerr = ((L[ne] - Lref[ne]).abs() / Lref[ne].abs().clamp(min=1.0)).max().item()
+        lrel = (L[ne] - Lref[ne]).abs() / Lref[ne].abs().clamp(min=1.0)
+        lerr = lrel.max().item()
         stats["lse_rel"] = lerr
+        if lerr > LSE_BOUND:
+            idx = ne.nonzero().flatten()[lrel > LSE_BOUND][:8].tolist()
+            print(f"{label}: LSE outside the bound at flattened rows {idx}: gpu {L[idx].tolist()} "
+                  f"ref {Lref[idx].tolist()}", flush=True)
         assert lerr <= LSE_BOUND, f"{label}: LSE rel err {lerr:.3e} > {LSE_BOUND}"
     print(f"{label}: {stats}", flush=True)
     log = os.environ.get("FA_PARITY_LOG")
