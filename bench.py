@@ -56,7 +56,7 @@ def algorithmic_bytes(w):
 
 def kernel_hash():
     h = hashlib.sha256()
-    for name in ("fa_fwd.hip", "fa_sched.h", "fa_launch.h"):
+    for name in ("fa_fwd.hip", "fa_fwd16.hip", "fa_device.h", "fa_sched.h", "fa_launch.h"):
         with open(os.path.join(ROOT, "exact_attention_02_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

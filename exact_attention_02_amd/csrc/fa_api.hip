@@ -47,6 +47,9 @@ int check_shape(int B, int H, int Nq, int Nk, int D, int causal, int window, int
     if (bh > (1LL << 31)) return FA_ERR_SHAPE;
     const long long nmax = Nq > Nk ? Nq : Nk;
     if (nmax > 0 && bh > (1LL << 62) / ((long long)nmax * D * 4)) return FA_ERR_SHAPE;
+    // one head's rows of any tensor must stay below 2^31 bytes (32-bit
+    // buffer descriptors and offsets in the kernels)
+    if (nmax * D * 4 >= (1LL << 31)) return FA_ERR_SHAPE;
     const fa::Plan pl = fa::make_plan(di->in, di->out, D, B, H, Nq);
     if (pl.n_wg > 0x7fffffffLL) return FA_ERR_SHAPE;
     return FA_OK;
@@ -97,14 +100,15 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.Nq = Nq;
     p.Nk = Nk;
     p.causal = causal ? 1 : 0;
-    p.window = window;
+    // a window of Nk or more keys removes nothing beyond the causal mask
+    p.window = (window >= Nk) ? 0 : window;
     p.n_bh = B * H;
     p.n_qt = pl.n_qt;
     p.c = scale * dq * dk * 1.44269504088896341f;
     p.out_mul = dv;
     if (std::getenv("FA_DEBUG"))
-        std::fprintf(stderr, "fa_fwd: in=%d out=%d D=%d qb=%d br=%d bc=%d n_qt=%d n_wg=%lld\n", pl.in, pl.out,
-                     pl.D, pl.qb, pl.br, pl.bc, pl.n_qt, pl.n_wg);
+        std::fprintf(stderr, "fa_fwd: in=%d out=%d D=%d kernel=%d nw=%d qb=%d br=%d bc=%d n_qt=%d n_wg=%lld\n",
+                     pl.in, pl.out, pl.D, pl.kernel, pl.nw, pl.qb, pl.br, pl.bc, pl.n_qt, pl.n_wg);
     (void)hipGetLastError();  // clear a stale error left by the caller
     const int err = fa::launch(pl, p, stream);
     return err == 0 ? FA_OK : FA_ERR_LAUNCH;

@@ -1,0 +1,460 @@
+// Fused exact-attention forward for 16-bit inputs (fp16, bf16) on gfx950,
+// software-pipelined over blocks of 32 queries x 32 keys.
+//
+// The computation is the block-by-block loop of the aiinarabic.com
+// flash-attention page (load a block of K and V on chip, score it, softmax it,
+// multiply by V, merge), with the running max and sum of the FLASHLIGHT
+// summary on gist.science (Methodology item 3). It is reorganised so that the
+// matrix cores and the vector ALU work at the same time inside one wave.
+//
+// A wave owns QB blocks of 32 query rows. Its work is a sequence of steps
+// u = QB*j + qb, one per (32-key sub-tile j, query block qb). Step u runs, in
+// one straight-line block:
+//   * the softmax VALU work of block u (exponentials, row sums, rounding to
+//     the 16-bit MFMA type), whose scores were formed in step u-1,
+//   * the score MFMAs of block u+1 (S^T = K Q^T),
+//   * the P.V MFMAs of block u-1 (O^T += V^T P^T).
+// The three are independent, so the MFMA pipe and the VALU overlap; per step
+// the MFMA work and the VALU work are of similar length.
+//
+// No row max on the common path. Every row keeps a reference m; a lane forms
+// p = 2^(c*s - m) for its 16 scores of the row and sums them. If a lane half's
+// sum exceeds SUM_LIMIT (a score has grown well past m) or the lane half has no
+// weight yet, the step is redone exactly: the row max is taken across both
+// lane halves, m moves up to it (the
+// accumulator and the sums are rescaled by 2^(m_old - m_new)) and p is formed
+// again. Rows whose m does not move form the same bits again, so a row's
+// result depends on its own scores alone; O / l and the log-sum-exp do not
+// depend on which m was used. Blocks on a mask edge take the same path after
+// their masked scores are set to -inf.
+//
+// P's rounding residual (P = hi + lo, both 16-bit) also multiplies V in a step
+// where a lane half's new weight exceeds a quarter of that half's total so
+// far -- the first sub-tiles of a row and peaked rows -- so no dominant
+// weight's rounding reaches the output.
+//
+// K and V tiles of 64 keys go HBM -> LDS with direct-to-LDS buffer loads into
+// a ring of three slots: the score look-ahead crosses into tile t+1 before
+// tile t is finished, and tile t+2 is copied meanwhile. One barrier per tile.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+#include "fa_sched.h"
+
+namespace fa {
+
+constexpr int NSLOT = 3;
+// Largest sum of a lane half's 16 weights of one block kept without moving
+// the reference max: every weight is then at most 2^10.
+constexpr float SUM_LIMIT = 1024.f;
+
+template <int IN, int OUT, int D, int NW, int QB>
+__global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
+    constexpr int NT = 64 * NW;
+    constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
+    constexpr int CPR = RB / 16;           // 16-byte chunks per row
+    constexpr int SW = CPR < 8 ? CPR : 8;  // swizzle period (lds_off)
+    constexpr int TILE = BC * RB;          // bytes of one K or V tile
+    constexpr int SLOT = 2 * TILE;         // K tile, then V tile
+    constexpr int NKS = D / 16;            // score MFMA steps over D
+    constexpr int ND = D / 32;             // 32-row blocks of O^T
+    constexpr int QW = 32 * QB;            // query rows per wave
+    constexpr int BR = NW * QW;            // query rows per workgroup
+    constexpr int NDMA = TILE / 16 / NT;   // 16-byte copies per thread per tensor per tile
+    constexpr int SPT = 2 * QB;            // steps per 64-key tile
+    static_assert(NDMA >= 1 && TILE % (16 * NT) == 0, "tile staging");
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NSLOT * SLOT];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int g = lane >> 4, cl = lane & 15;   // 16-lane group of the transposing reads
+
+    const int Nq = p.Nq, Nk = p.Nk, causal = p.causal, window = p.window;
+    int bh, qt;
+    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, &bh, &qt);
+    const int r0 = qt * BR;
+    const int r1 = min(r0 + BR, Nq);
+    int kv_lo, kv_hi;
+    kv_range(r0, r1, Nq, Nk, causal, window, &kv_lo, &kv_hi);
+    const int t_lo = kv_lo / BC;
+    const int t_hi = (kv_hi > kv_lo) ? (kv_hi + BC - 1) / BC : t_lo;
+    const int w0 = r0 + wave * QW;
+    const int w1 = min(w0 + QW, Nq);
+
+    const uint8_t* qp = p.q + (size_t)bh * Nq * RB;
+    const uint8_t* kp = p.k + (size_t)bh * Nk * RB;
+    const uint8_t* vp = p.v + (size_t)bh * Nk * RB;
+
+    // Q fragments, B operand of S^T = K Q^T: lane holds query w0+32qb+l32,
+    // head-dim elements [16s + 8hh, +8).
+    i32x4 qf[QB][NKS];
+    {
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)(Nq * RB));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int row = w0 + 32 * qb + l32;
+#pragma unroll
+            for (int s = 0; s < NKS; ++s)
+                qf[qb][s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    qrs, row * RB + (16 * s + 8 * hh) * 2, 0, 0));
+        }
+    }
+
+    f32x16 oacc[ND][QB];
+    float m[QB], lh[QB];   // reference max (base-2 units) and this lane half's weight sum
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db][qb] = f32x16{};
+        m[qb] = -INFINITY;
+        lh[qb] = 0.f;
+    }
+    const float c2 = p.c;
+
+    // ---- K/V copies: lane l of a wave fills the l-th 16-byte slot of a 1 KiB
+    // run of the tile, fetching the global chunk that belongs there under the
+    // swizzled layout; rows at or past Nk read as zeros.
+    const i32x4 kwords = rsrc_words(kp, (unsigned)(Nk * RB));
+    const i32x4 vwords = rsrc_words(vp, (unsigned)(Nk * RB));
+    const unsigned smem_base = (unsigned)(unsigned long long)(lds_u8*)smem;
+    auto issue_tile = [&](int t) {
+        const int kv0 = t * BC;
+        const unsigned kb = smem_base + (unsigned)((t % NSLOT) * SLOT);
+        int ln = lane;
+        asm volatile("" : "+v"(ln));   // offsets are recomputed per tile, not held in registers
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int run = 64 * wave + NT * i;
+            const int slot = run + ln;
+            const int x = slot / CPR, c = (slot % CPR) ^ (x & (SW - 1));
+            const unsigned goff = (unsigned)((kv0 + x) * RB + c * 16);
+            dma16(kwords, kb + run * 16, goff);
+            dma16(vwords, kb + TILE + run * 16, goff);
+        }
+    };
+    auto tile_lds = [&](int t) { return (const lds_u8*)(smem + (t % NSLOT) * SLOT); };
+    // Class of block (j, qb), rows of query block qb x keys of sub-tile j,
+    // from two sub-tile ranges per query block: [jf0, jf1) has every pair
+    // visible, [ju0, ju1) at least one (the same answers as tile_class).
+    int jf0[QB], jf1[QB], ju0[QB], ju1[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int a0 = w0 + 32 * qb;
+        block_ranges32(a0, min(a0 + 32, w1), Nq, Nk, causal, window, &jf0[qb], &jf1[qb], &ju0[qb], &ju1[qb]);
+    }
+    auto block_class = [&](int j, int qb) {
+        if (j >= jf0[qb] && j < jf1[qb]) return (int)TILE_FULL;
+        if (j >= ju0[qb] && j < ju1[qb]) return (int)TILE_EDGE;
+        return (int)TILE_SKIP;
+    };
+
+    // S^T of block (j, qb): element r of lane (l32, hh) is key
+    // 32j + 8(r/4) + 4hh + r%4 against query w0 + 32qb + l32.
+    // Per-lane parts of the LDS addresses; the rest (slot, sub-tile half, MFMA
+    // step) is uniform. The swizzle term depends on the row mod 8 only, which
+    // the uniform row offsets (multiples of 16) leave unchanged.
+    int kofs[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) kofs[s] = lds_off<RB>(l32, 2 * s + hh);
+    int vofs[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+        const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
+        vofs[db] = lds_off<RB>(4 * hh + (cl >> 2), ch) + 8 * (cl & 1);
+    }
+    auto k_read = [&](int j, i32x4(&a)[NKS]) __attribute__((always_inline)) {
+        const lds_u8* kb = tile_lds(j >> 1) + 32 * (j & 1) * RB;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+            a[s] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(kb + kofs[s]);
+    };
+    auto s_mfma = [&](const i32x4(&a)[NKS], int qb, f32x16& S) __attribute__((always_inline)) {
+        S = f32x16{};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) S = mfma16(IN, a[s], qf[qb][s], S);
+    };
+    auto scores = [&](int j, int qb, f32x16& S) __attribute__((always_inline)) {
+        i32x4 a[NKS];
+        k_read(j, a);
+        s_mfma(a, qb, S);
+    };
+
+    // V^T operands of sub-tile j for its two 16-key MFMA steps, in the key
+    // order P has: step sp, lane half hh, k-slot e holds key
+    // 32j + 16sp + 8(e/4) + 4hh + e%4 (two transposing reads of 4 rows).
+    auto v_operands = [&](int j, i32x4(&va)[2][ND]) __attribute__((always_inline)) {
+        const lds_u8* vb = tile_lds(j >> 1) + TILE + 32 * (j & 1) * RB;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            const lds_u8* a = vb + vofs[db];
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const i32x2 u0 = read_tr16(a + 16 * sp * RB);
+                const i32x2 u1 = read_tr16(a + (16 * sp + 8) * RB);
+                va[sp][db] = i32x4{u0[0], u0[1], u1[0], u1[1]};
+            }
+        }
+    };
+
+    // Masked scores become -inf: row i = w0 + 32qb + l32 sees keys [klo, khi)
+    // (none when i is past the wave's rows).
+    auto mask = [&](int j, int qb, f32x16& S) __attribute__((always_inline)) {
+        const int c0 = 32 * j;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));   // recomputed here, not held across the loop
+        const int i = w0 + 32 * qb + (ln & 31);
+        const int ip = i + (Nk - Nq);
+        int klo = (window > 0) ? ip - window + 1 : 0;
+        int khi = causal ? ip + 1 : Nk;
+        klo = klo > 0 ? klo : 0;
+        khi = khi < Nk ? khi : Nk;
+        if (i >= w1) khi = klo;   // past the last query row: nothing visible
+        const int a = klo - c0 - 4 * (ln >> 5), b = khi - c0 - 4 * (ln >> 5);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            S[r] = (off < a || off >= b) ? -INFINITY : S[r];
+        }
+    };
+
+    // p = 2^(c*s - ms) for the 16 scores, their sum (a fixed pairwise order)
+    // and p rounded to the MFMA type.
+    auto p_phase = [&](const f32x16& S, float ms, float& ts, i32x4(&hi)[2]) __attribute__((always_inline)) {
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+        float s8[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) s8[r] = pr[2 * r] + pr[2 * r + 1];
+        ts = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            const int o = 8 * sp;
+            hi[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
+                           pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
+        }
+    };
+
+    auto pv = [&](int qb, const i32x4(&va)[2][ND], const i32x4(&P)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+            for (int db = 0; db < ND; ++db) oacc[db][qb] = mfma16(IN, va[sp][db], P[sp], oacc[db][qb]);
+    };
+
+    // ---- per-step state; the buffers alternate between even and odd steps
+    f32x16 sbuf[2];        // scores of the current step and of the next
+    i32x4 pbuf[2][2];      // rounded weights of the current step and of the previous
+    i32x4 va[2][ND];       // V operands of the sub-tile of step u-1
+    // With two query blocks per wave, K operands are read a step ahead: at
+    // the start of sub-tile j's first step kpf holds K of sub-tile j.
+    constexpr bool PF = QB == 2;
+    i32x4 kpf[NKS];
+
+    // After the first p_phase of block (j, qb): masking of edge blocks, the
+    // exact redo for flagged rows, the residual pass and the row sums (a
+    // skipped block changes nothing). S still holds the block's scores.
+    auto tail = [&](int j, int qb, int cls, f32x16& S, float& ms, float& ts, i32x4(&hi)[2])
+        __attribute__((always_inline)) {
+        const bool active = cls != TILE_SKIP;
+        bool trig = active && ((lh[qb] == 0.f) || !(ts <= SUM_LIMIT));
+        if (cls == TILE_EDGE) {
+            // the weights so far saw every key of the sub-tile: mask, form
+            // them again, and decide on the visible keys alone
+            mask(j, qb, S);
+            p_phase(S, ms, ts, hi);
+            trig = (lh[qb] == 0.f) || !(ts <= SUM_LIMIT);
+        }
+        if (__builtin_amdgcn_ballot_w64(trig) != 0) {
+            const unsigned tr = trig ? 1u : 0u;
+            auto pr = __builtin_amdgcn_permlane32_swap(tr, tr, false, false);
+            const bool row = (pr[0] | pr[1]) != 0;
+            float mx = S[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+            mx = max_halves(mx);
+            const float mnew = row ? fmaxf(m[qb], mx * c2) : m[qb];
+            const bool mv = mnew != m[qb];
+            const float alpha = mv ? __builtin_amdgcn_exp2f(m[qb] - mnew) : 1.f;
+            m[qb] = mnew;
+            if (__builtin_amdgcn_ballot_w64(mv) != 0) {
+                lh[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha;
+            }
+            ms = (mnew == -INFINITY) ? 0.f : mnew;
+            p_phase(S, ms, ts, hi);
+        }
+        const bool sr = active && ts * 3.f > lh[qb];
+        lh[qb] += ts;   // zero for a skipped block
+        if (__builtin_amdgcn_ballot_w64(sr) != 0) {
+            i32x4 lo[2];
+            float pr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const int o = 8 * sp;
+                const i32x4 h = hi[sp];
+                const i32x4 d = i32x4{pack2<IN>(pr[o + 0] - unpack_lo<IN>(h[0]), pr[o + 1] - unpack_hi<IN>(h[0])),
+                                      pack2<IN>(pr[o + 2] - unpack_lo<IN>(h[1]), pr[o + 3] - unpack_hi<IN>(h[1])),
+                                      pack2<IN>(pr[o + 4] - unpack_lo<IN>(h[2]), pr[o + 5] - unpack_hi<IN>(h[2])),
+                                      pack2<IN>(pr[o + 6] - unpack_lo<IN>(h[3]), pr[o + 7] - unpack_hi<IN>(h[3]))};
+                lo[sp] = i32x4{sr ? d[0] : 0, sr ? d[1] : 0, sr ? d[2] : 0, sr ? d[3] : 0};
+            }
+            i32x4 vt[2][ND];
+            v_operands(j, vt);
+            pv(qb, vt, lo);
+        }
+    };
+
+    // ---- one step (see the file comment); KP = u % 2 picks the buffers.
+    // Branch-free apart from the rare exact path: the look-ahead scores and
+    // the softmax are formed on every step, and a skipped step's weights are
+    // zeroed, so the next step's P.V adds exactly nothing for it.
+    auto step = [&](auto kp, int u) __attribute__((always_inline)) {
+        constexpr int KP = decltype(kp)::value;
+        const int j = u / QB;
+        constexpr int qb = KP % QB;                 // steps alternate query blocks when QB = 2
+        constexpr int qn = (KP + 1) % QB;           // query block of step u+1
+        constexpr int qpv = (KP + QB - 1) % QB;     // query block of step u-1
+        constexpr bool load_v = qpv == 0;           // step u-1 is the first of its sub-tile
+        const int jn = (qn == 0) ? j + 1 : j;       // sub-tile of step u+1
+        // sub-tile of step u-1; before the first sub-tile, any loaded one will
+        // do (its weights are zero)
+        const int jp = max((qb == 0) ? j - 1 : j, 2 * t_lo);
+        f32x16& S = sbuf[KP];
+        f32x16& Sn = sbuf[KP ^ 1];
+        i32x4(&Pc)[2] = pbuf[KP];
+        i32x4(&Pp)[2] = pbuf[KP ^ 1];
+        const int cls = block_class(j, qb);
+        // a skipped block's weights are 2^-inf = 0: the next step's P.V of
+        // them adds exactly nothing and the sums are unchanged
+        float ms = (cls == TILE_SKIP) ? INFINITY : ((m[qb] == -INFINITY) ? 0.f : m[qb]);
+        float ts;
+        if (load_v) v_operands(jp, va);
+        if constexpr (PF) {
+            // qb 0: scores of (j, 1) from K(j), then K(j+1) is requested;
+            // qb 1: scores of (j+1, 0) from K(j+1), read a step ago
+            s_mfma(kpf, qn, Sn);
+            if (KP == 0) k_read(j + 1, kpf);
+        } else {
+            scores(jn, qn, Sn);
+        }
+        p_phase(S, ms, ts, Pc);
+        pv(qpv, va, Pp);
+        tail(j, qb, cls, S, ms, ts, Pc);
+    };
+
+    // ---- prologue: Q and tile t_lo land, tile t_lo+1 is requested, the
+    // first block's scores are formed; no weights are pending yet
+    if (t_lo < t_hi) issue_tile(t_lo);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (t_lo + 1 < t_hi) issue_tile(t_lo + 1);
+    if (t_lo < t_hi) {
+        if constexpr (PF) {
+            k_read(2 * t_lo, kpf);
+            s_mfma(kpf, 0, sbuf[0]);
+        } else {
+            scores(2 * t_lo, 0, sbuf[0]);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            pbuf[b][sp] = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int db = 0; db < ND; ++db) va[sp][db] = i32x4{0, 0, 0, 0};
+        }
+
+    // ---- main loop: iteration i runs steps 2i and 2i+1 (sub-tile i's two
+    // query blocks when QB = 2, tile i's two sub-tiles when QB = 1). A
+    // barrier publishes tile t+1 before its first read -- the K read-ahead
+    // of sub-tile 2t+1's first step when QB = 2, the score look-ahead of tile
+    // t's last step when QB = 1 -- and follows every use of tile t-1, whose
+    // slot then receives tile t+2.
+    const int i_lo = SPT * t_lo / 2, i_hi = SPT * t_hi / 2;
+    auto tile_barrier = [&](int t) __attribute__((always_inline)) {
+        if (t + 1 < t_hi) __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's copies of tile t+1 landed
+        __syncthreads();
+        if (t + 2 < t_hi) issue_tile(t + 2);
+    };
+    for (int i = i_lo; i < i_hi; ++i) {
+        if constexpr (PF) {
+            if (i & 1) tile_barrier(i >> 1);
+            step(std::integral_constant<int, 0>{}, 2 * i);
+            step(std::integral_constant<int, 1>{}, 2 * i + 1);
+        } else {
+            step(std::integral_constant<int, 0>{}, 2 * i);
+            tile_barrier(i);
+            step(std::integral_constant<int, 1>{}, 2 * i + 1);
+        }
+    }
+    // ---- the last step's P.V (zero weights if that step was skipped)
+    if (t_lo < t_hi) {
+        v_operands(2 * t_hi - 1, va);
+        pv(QB - 1, va, pbuf[1]);
+    }
+
+    // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
+    uint8_t* op = p.o + (size_t)bh * Nq * D * Out<OUT>::EB;
+    float* lp = p.lse + (size_t)bh * Nq;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float lt = sum_halves(lh[qb]);
+        const int i = w0 + 32 * qb + l32;
+        if (i < w1) {
+            const float inv = (lt > 0.f) ? p.out_mul / lt : 0.f;
+            uint8_t* orow = op + (size_t)i * D * Out<OUT>::EB;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x16& a = oacc[db][qb];
+                    const int d = 32 * db + 8 * r4 + 4 * hh;
+                    Out<OUT>::store4(orow + d * Out<OUT>::EB, a[4 * r4] * inv, a[4 * r4 + 1] * inv,
+                                     a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv);
+                }
+            if (hh == 0) lp[i] = (lt > 0.f) ? (m[qb] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+template <int IN, int OUT, int D, int NW, int QB>
+static int launch16_one(const Plan& pl, const Params& p, hipStream_t s) {
+    hipLaunchKernelGGL((fa_fwd16_kernel<IN, OUT, D, NW, QB>), dim3((unsigned)pl.n_wg), dim3(64 * NW), 0, s, p);
+    return (int)hipGetLastError();
+}
+
+template <int IN, int OUT>
+static int launch16_io(const Plan& pl, const Params& p, hipStream_t s) {
+    if (pl.D == 64) {
+        if (pl.qb == 2) return launch16_one<IN, OUT, 64, 4, 2>(pl, p, s);
+        return launch16_one<IN, OUT, 64, 4, 1>(pl, p, s);
+    }
+    return launch16_one<IN, OUT, 128, 8, 1>(pl, p, s);
+}
+
+int launch16(const Plan& pl, const Params& p, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (pl.in == IN_F16 && pl.out == OUT_F16) return launch16_io<IN_F16, OUT_F16>(pl, p, s);
+    if (pl.in == IN_F16 && pl.out == OUT_F32) return launch16_io<IN_F16, OUT_F32>(pl, p, s);
+    if (pl.in == IN_BF16 && pl.out == OUT_BF16) return launch16_io<IN_BF16, OUT_BF16>(pl, p, s);
+    if (pl.in == IN_BF16 && pl.out == OUT_F32) return launch16_io<IN_BF16, OUT_F32>(pl, p, s);
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -8,6 +8,11 @@ namespace fa {
 enum InKind { IN_F16 = 0, IN_BF16 = 1, IN_E4M3 = 2 };
 enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
 
+// KERNEL_TILE64: 64-key tiles, one softmax per tile (all input types).
+// KERNEL_PIPE16: 16-bit inputs, scores of the next 32 keys formed during the
+// softmax of the current 32 (fa_fwd16.hip).
+enum KernelKind { KERNEL_TILE64 = 0, KERNEL_PIPE16 = 1 };
+
 // Everything a workgroup needs; passed by value as the kernel argument.
 struct Params {
     const uint8_t* q;
@@ -26,8 +31,10 @@ struct Params {
 // Tile shape a launch uses.
 struct Plan {
     int in, out, D;
+    int kernel;     // KERNEL_TILE64 or KERNEL_PIPE16
+    int nw;         // waves per workgroup
     int qb;         // 32-row query blocks per wave
-    int br;         // query rows per workgroup (4 waves)
+    int br;         // query rows per workgroup (nw * 32 * qb)
     int bc;         // key rows per tile
     int n_qt;
     long long n_wg;
@@ -39,5 +46,6 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq);
 // Enqueues the kernel chosen by `plan` on `stream`; returns the hipError_t
 // value of hipGetLastError() after the launch (0 on success).
 int launch(const Plan& plan, const Params& p, void* stream);
+int launch16(const Plan& plan, const Params& p, void* stream);
 
 }  // namespace fa

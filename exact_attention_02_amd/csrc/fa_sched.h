@@ -84,6 +84,50 @@ FA_HD int tile_class(int w0, int w1, int c0, int c1, int Nq, int Nk, int causal,
     return TILE_EDGE;
 }
 
+// tile_class in 32-bit arithmetic, for the kernels: exact whenever Nq, Nk
+// and window are below 2^30 (the entry points keep every tensor below 2^31
+// bytes for the buffer descriptors, and pass window < Nk).
+FA_HD int tile_class32(int w0, int w1, int c0, int c1, int Nq, int Nk, int causal, int window) {
+    if (w1 <= w0 || c1 <= c0) return TILE_SKIP;
+    const int d = Nk - Nq;
+    int ulo = 0, uhi = Nk;
+    if (causal && w1 + d < uhi) uhi = w1 + d;
+    if (window > 0 && w0 + d - window + 1 > ulo) ulo = w0 + d - window + 1;
+    if (c1 <= ulo || c0 >= uhi) return TILE_SKIP;
+    int ilo = 0, ihi = Nk;
+    if (causal && w0 + d + 1 < ihi) ihi = w0 + d + 1;
+    if (window > 0 && w1 + d - window > ilo) ilo = w1 + d - window;
+    if (c0 >= ilo && c1 <= ihi) return TILE_FULL;
+    return TILE_EDGE;
+}
+
+// The same classes for the blocks rows [a0, a1) x keys [32j, 32j + 32), as
+// two ranges of j: every pair visible for j in [*jf0, *jf1), at least one for
+// j in [*ju0, *ju1) (outside it the block is skipped). 32-bit arithmetic, under
+// the same limits as tile_class32.
+FA_HD void block_ranges32(int a0, int a1, int Nq, int Nk, int causal, int window, int* jf0, int* jf1, int* ju0,
+                          int* ju1) {
+    const int d = Nk - Nq;
+    int ulo = 0, uhi = Nk, ilo = 0, ihi = Nk;   // union and intersection of the rows' key ranges
+    if (causal) {
+        if (a1 + d < uhi) uhi = a1 + d;
+        if (a0 + d + 1 < ihi) ihi = a0 + d + 1;
+    }
+    if (window > 0) {
+        if (a0 + d - window + 1 > ulo) ulo = a0 + d - window + 1;
+        if (a1 + d - window > ilo) ilo = a1 + d - window;
+    }
+    if (a1 <= a0 || uhi <= ulo) {
+        *jf0 = *jf1 = *ju0 = *ju1 = 0;
+        return;
+    }
+    *ju0 = ulo / 32;                      // first j with 32j + 32 > ulo
+    *ju1 = (uhi + 31) / 32;               // past the last j with 32j < uhi
+    *jf0 = (ilo + 31) / 32;               // first j with 32j >= ilo
+    *jf1 = (ihi > 0) ? ihi / 32 : 0;      // past the last j with 32j + 32 <= ihi
+    if (*jf1 < *jf0) *jf1 = *jf0;
+}
+
 // Hardware workgroup id -> (batch*head, query tile).
 //
 // Workgroups are handed to the 8 XCDs of the chip round-robin by id, and each

@@ -56,7 +56,8 @@ enum {
 enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL */
-    FA_ERR_SHAPE = 2,     /* a negative size, or sizes whose products overflow */
+    FA_ERR_SHAPE = 2,     /* a negative size, sizes whose products overflow, or
+                             max(Nq, Nk) * D * 4 >= 2^31 (one head's rows) */
     FA_ERR_HEADDIM = 3,   /* D is not 64 or 128 */
     FA_ERR_DTYPE = 4,     /* unknown dtype, or fa_fwd_fp8 with a non-e4m3 dtype */
     FA_ERR_MASK = 5,      /* window < 0, or window > 0 without causal */

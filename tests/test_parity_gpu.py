@@ -166,6 +166,24 @@ def test_two_query_blocks_per_wave(monkeypatch, B, H, Nq, Nk, causal, window, di
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
+@pytest.mark.parametrize("B,H,Nq,Nk", [(2, 3, 300, 300), (1, 2, 200, 333), (1, 2, 333, 200), (1, 3, 700, 700)])
+@pytest.mark.parametrize("causal,window", MODES)
+@pytest.mark.parametrize("D,qb", [(64, "1"), (64, "2"), (128, "1")])
+@pytest.mark.parametrize("din,dout", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")])
+def test_tile64_kernel_on_16bit_inputs(monkeypatch, B, H, Nq, Nk, causal, window, D, qb, din, dout):
+    # 16-bit inputs run the pipelined kernel by default; the 64-key-tile
+    # kernel (the e4m3 kernel) stays selectable for them and must agree too.
+    monkeypatch.setenv("FA_KERNEL", "0")
+    monkeypatch.setenv("FA_TILE_QB", qb)
+    seed = 3000 + B * 7 + H * 13 + Nq * 3 + Nk + D + (17 if causal else 0) + window
+    w = synth.small_workload(f"t64_B{B}H{H}q{Nq}k{Nk}D{D}c{int(causal)}w{window}_{din}_{dout}_qb{qb}", B, H, Nq, Nk, D,
+                             causal, window, din, dout, seed)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
 # ----------------------------------------------------------- edge cases
 
 def test_no_keys_gives_zero_and_minus_inf():

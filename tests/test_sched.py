@@ -93,3 +93,53 @@ def test_heads_stay_on_one_xcd_and_tiles_go_heavy_first():
     assert set().union(*heads_of_xcd.values()) == set(range(48))
     for bh, qts in order.items():
         assert qts == sorted(qts, reverse=True)
+
+
+def test_32bit_block_class_equals_64bit(tmp_path):
+    """The kernels classify blocks in 32-bit arithmetic, one block at a time or
+    as ranges of 32-key sub-tiles; both must agree with the 64-bit classifier
+    everywhere the entry points allow (sizes below 2^30, window < Nk),
+    including the extremes of that range."""
+    import subprocess
+    src = tmp_path / "cls.cpp"
+    hdr = fa.LIB_PATH.replace("libfa.so", "csrc/fa_sched.h")
+    src.write_text(f'''
+#include <cstdio>
+#include <cstdlib>
+#include <initializer_list>
+#include "{hdr}"
+int main() {{
+    long long n = 0, bad = 0;
+    const int sizes[] = {{1, 2, 31, 32, 33, 64, 100, 257, 1000}};
+    for (int Nq : sizes) for (int Nk : sizes) for (int causal = 0; causal < 2; ++causal)
+    for (int window = 0; window < Nk; window += (window < 3 ? 1 : 37)) {{
+        if (window > 0 && !causal) continue;
+        for (int w0 = 0; w0 < Nq; w0 += 7) for (int w1 = w0 + 1; w1 <= Nq; w1 += 13)
+        for (int c0 = 0; c0 < Nk + 40; c0 += 32) {{
+            const int a = fa::tile_class(w0, w1, c0, c0 + 32, Nq, Nk, causal, window);
+            const int b = fa::tile_class32(w0, w1, c0, c0 + 32, Nq, Nk, causal, window);
+            int jf0, jf1, ju0, ju1;
+            fa::block_ranges32(w0, w1, Nq, Nk, causal, window, &jf0, &jf1, &ju0, &ju1);
+            const int j = c0 / 32;
+            const int r = (j >= jf0 && j < jf1) ? 1 : ((j >= ju0 && j < ju1) ? 2 : 0);
+            ++n; if (a != b || a != r) {{ if (bad < 5) std::printf("mismatch %d %d %d %d %d %d %d: %d vs %d vs %d\\n", w0, w1, c0, Nq, Nk, causal, window, a, b, r); ++bad; }}
+        }}
+    }}
+    // extremes: sizes near 2^30, a window just below Nk
+    const int big = (1 << 30) - 64;
+    const int ext[][4] = {{{{big, big, 1, big - 1}}, {{big, 64, 1, 63}}, {{64, big, 1, 0}}, {{big, big, 0, 0}}, {{big, big, 1, 0}}}};
+    for (const auto& e : ext) for (int w0 : {{0, 64, e[0] - 64}}) for (int c0 : {{0, 32, e[1] - 32, e[1] - 64}}) {{
+        if (w0 < 0 || c0 < 0) continue;
+        const int w1 = w0 + 64 < e[0] ? w0 + 64 : e[0];
+        const int a = fa::tile_class(w0, w1, c0, c0 + 32, e[0], e[1], e[2], e[3]);
+        const int b = fa::tile_class32(w0, w1, c0, c0 + 32, e[0], e[1], e[2], e[3]);
+        ++n; if (a != b) {{ std::printf("extreme mismatch %d %d %d\\n", w0, c0, e[0]); ++bad; }}
+    }}
+    std::printf("%lld cases, %lld mismatches\\n", n, bad);
+    return bad != 0;
+}}
+''')
+    exe = tmp_path / "cls"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-o", str(exe), str(src)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout
