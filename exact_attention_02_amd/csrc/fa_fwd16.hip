@@ -152,9 +152,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
         block_ranges32(a0, min(a0 + 32, w1), Nq, Nk, causal, window, &jf0[qb], &jf1[qb], &ju0[qb], &ju1[qb]);
     }
     auto block_class = [&](int j, int qb) {
-        if (j >= jf0[qb] && j < jf1[qb]) return (int)TILE_FULL;
-        if (j >= ju0[qb] && j < ju1[qb]) return (int)TILE_EDGE;
-        return (int)TILE_SKIP;
+        const bool full = (unsigned)(j - jf0[qb]) < (unsigned)(jf1[qb] - jf0[qb]);
+        const bool any = (unsigned)(j - ju0[qb]) < (unsigned)(ju1[qb] - ju0[qb]);
+        return full ? (int)TILE_FULL : (any ? (int)TILE_EDGE : (int)TILE_SKIP);
     };
 
     // S^T of block (j, qb): element r of lane (l32, hh) is key
@@ -171,8 +171,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
         const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
         vofs[db] = lds_off<RB>(4 * hh + (cl >> 2), ch) + 8 * (cl & 1);
     }
-    auto k_read = [&](int j, i32x4(&a)[NKS]) __attribute__((always_inline)) {
-        const lds_u8* kb = tile_lds(j >> 1) + 32 * (j & 1) * RB;
+    auto k_read = [&](const lds_u8* tb, int j, i32x4(&a)[NKS]) __attribute__((always_inline)) {
+        const lds_u8* kb = tb + 32 * (j & 1) * RB;
 #pragma unroll
         for (int s = 0; s < NKS; ++s)
             a[s] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(kb + kofs[s]);
@@ -182,17 +182,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < NKS; ++s) S = mfma16(IN, a[s], qf[qb][s], S);
     };
-    auto scores = [&](int j, int qb, f32x16& S) __attribute__((always_inline)) {
+    auto scores = [&](const lds_u8* tb, int j, int qb, f32x16& S) __attribute__((always_inline)) {
         i32x4 a[NKS];
-        k_read(j, a);
+        k_read(tb, j, a);
         s_mfma(a, qb, S);
     };
 
     // V^T operands of sub-tile j for its two 16-key MFMA steps, in the key
     // order P has: step sp, lane half hh, k-slot e holds key
     // 32j + 16sp + 8(e/4) + 4hh + e%4 (two transposing reads of 4 rows).
-    auto v_operands = [&](int j, i32x4(&va)[2][ND]) __attribute__((always_inline)) {
-        const lds_u8* vb = tile_lds(j >> 1) + TILE + 32 * (j & 1) * RB;
+    auto v_operands = [&](const lds_u8* tb, int j, i32x4(&va)[2][ND]) __attribute__((always_inline)) {
+        const lds_u8* vb = tb + TILE + 32 * (j & 1) * RB;
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
             const lds_u8* a = vb + vofs[db];
@@ -251,6 +251,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
             for (int db = 0; db < ND; ++db) oacc[db][qb] = mfma16(IN, va[sp][db], P[sp], oacc[db][qb]);
     };
 
+    // ---- LDS bases of the slots of tiles t-1, t and t+1 while the loop is at
+    // tile t (rotated when t advances)
+    const lds_u8* lds_prev = tile_lds(t_lo + 2);
+    const lds_u8* lds_cur = tile_lds(t_lo);
+    const lds_u8* lds_next = tile_lds(t_lo + 1);
+
     // ---- per-step state; the buffers alternate between even and odd steps
     f32x16 sbuf[2];        // scores of the current step and of the next
     i32x4 pbuf[2][2];      // rounded weights of the current step and of the previous
@@ -266,13 +272,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
     auto tail = [&](int j, int qb, int cls, f32x16& S, float& ms, float& ts, i32x4(&hi)[2])
         __attribute__((always_inline)) {
         const bool active = cls != TILE_SKIP;
-        bool trig = active && ((lh[qb] == 0.f) || !(ts <= SUM_LIMIT));
+        bool trig = active & ((lh[qb] == 0.f) | !(ts <= SUM_LIMIT));
         if (cls == TILE_EDGE) {
             // the weights so far saw every key of the sub-tile: mask, form
             // them again, and decide on the visible keys alone
             mask(j, qb, S);
             p_phase(S, ms, ts, hi);
-            trig = (lh[qb] == 0.f) || !(ts <= SUM_LIMIT);
+            trig = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
         }
         if (__builtin_amdgcn_ballot_w64(trig) != 0) {
             const unsigned tr = trig ? 1u : 0u;
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
             ms = (mnew == -INFINITY) ? 0.f : mnew;
             p_phase(S, ms, ts, hi);
         }
-        const bool sr = active && ts * 3.f > lh[qb];
+        const bool sr = active & (ts * 3.f > lh[qb]);
         lh[qb] += ts;   // zero for a skipped block
         if (__builtin_amdgcn_ballot_w64(sr) != 0) {
             i32x4 lo[2];
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
                 lo[sp] = i32x4{sr ? d[0] : 0, sr ? d[1] : 0, sr ? d[2] : 0, sr ? d[3] : 0};
             }
             i32x4 vt[2][ND];
-            v_operands(j, vt);
+            v_operands(lds_cur, j, vt);   // sub-tile j lies in the loop's current tile
             pv(qb, vt, lo);
         }
     };
@@ -341,17 +347,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
         // them adds exactly nothing and the sums are unchanged
         float ms = (cls == TILE_SKIP) ? INFINITY : ((m[qb] == -INFINITY) ? 0.f : m[qb]);
         float ts;
-        if (load_v) v_operands(jp, va);
+        const int t = j >> 1;   // the loop's current tile
+        if (load_v) v_operands(((jp >> 1) == t) ? lds_cur : lds_prev, jp, va);
         if constexpr (PF) {
             // qb 0: scores of (j, 1) from K(j), then K(j+1) is requested;
             // qb 1: scores of (j+1, 0) from K(j+1), read a step ago
             s_mfma(kpf, qn, Sn);
-            if (KP == 0) k_read(j + 1, kpf);
+            if (KP == 0) k_read(((j + 1) >> 1 == t) ? lds_cur : lds_next, j + 1, kpf);
         } else {
-            scores(jn, qn, Sn);
+            scores(((jn >> 1) == t) ? lds_cur : lds_next, jn, qn, Sn);
         }
         p_phase(S, ms, ts, Pc);
         pv(qpv, va, Pp);
+#ifdef FA_LDS_FIRST
+        // the LDS reads go first and a run of softmax VALU work covers their
+        // latency before the first MFMA that needs them
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_LDS_FIRST, 0);
+#endif
         tail(j, qb, cls, S, ms, ts, Pc);
     };
 
@@ -363,10 +376,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
     if (t_lo + 1 < t_hi) issue_tile(t_lo + 1);
     if (t_lo < t_hi) {
         if constexpr (PF) {
-            k_read(2 * t_lo, kpf);
+            k_read(lds_cur, 2 * t_lo, kpf);
             s_mfma(kpf, 0, sbuf[0]);
         } else {
-            scores(2 * t_lo, 0, sbuf[0]);
+            scores(lds_cur, 2 * t_lo, 0, sbuf[0]);
         }
     }
 #pragma unroll
@@ -390,20 +403,28 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
         __syncthreads();
         if (t + 2 < t_hi) issue_tile(t + 2);
     };
+    auto rotate = [&]() __attribute__((always_inline)) {
+        const lds_u8* x = lds_prev;
+        lds_prev = lds_cur;
+        lds_cur = lds_next;
+        lds_next = x;
+    };
     for (int i = i_lo; i < i_hi; ++i) {
         if constexpr (PF) {
             if (i & 1) tile_barrier(i >> 1);
             step(std::integral_constant<int, 0>{}, 2 * i);
             step(std::integral_constant<int, 1>{}, 2 * i + 1);
+            if (i & 1) rotate();
         } else {
             step(std::integral_constant<int, 0>{}, 2 * i);
             tile_barrier(i);
             step(std::integral_constant<int, 1>{}, 2 * i + 1);
+            rotate();
         }
     }
     // ---- the last step's P.V (zero weights if that step was skipped)
     if (t_lo < t_hi) {
-        v_operands(2 * t_hi - 1, va);
+        v_operands(tile_lds(t_hi - 1), 2 * t_hi - 1, va);
         pv(QB - 1, va, pbuf[1]);
     }
 
