@@ -53,12 +53,32 @@ constexpr int NSLOT = 3;
 // the reference max: every weight is then at most 2^10.
 constexpr float SUM_LIMIT = 1024.f;
 
+// LDS layout of a K or V tile: row x of RB bytes holds its 16-byte chunk c at
+// position c ^ swz(x). LDS serves 256 bytes (64 banks of 4 bytes) per cycle:
+// a 16-lane group of 16-byte score-operand reads covers 16 consecutive rows
+// at one chunk, and a 32-lane half of the transposing V reads covers 4
+// consecutive rows at 4 aligned chunks. swz spreads both over distinct
+// banks: at 128-byte rows, two rows share a 256-byte bank cycle and
+// swz = ((x >> 1) & 1) << 2 | (x >> 2) & 3 separates rows x, x + 2 into
+// different groups of four chunks; at 256-byte rows, swz = (x & 3) << 2 |
+// (x >> 2) & 3 does the same for four consecutive rows. It depends on x mod
+// 16 only.
+template <int RB>
+__device__ __forceinline__ int swz16(int x) {
+    if constexpr (RB == 128) return (((x >> 1) & 1) << 2) | ((x >> 2) & 3);
+    else return ((x & 3) << 2) | ((x >> 2) & 3);
+}
+template <int RB>
+__device__ __forceinline__ int lds_pos(int x, int c) {
+    return x * RB + ((c ^ swz16<RB>(x)) << 4);
+}
+
 template <int IN, int OUT, int D, int NW, int QB>
 __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
     constexpr int NT = 64 * NW;
     constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
-    constexpr int SW = CPR < 8 ? CPR : 8;  // swizzle period (lds_off)
+    static_assert(RB == 128 || RB == 256, "row size");
     constexpr int TILE = BC * RB;          // bytes of one K or V tile
     constexpr int SLOT = 2 * TILE;         // K tile, then V tile
     constexpr int NKS = D / 16;            // score MFMA steps over D
@@ -135,7 +155,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
         for (int i = 0; i < NDMA; ++i) {
             const int run = 64 * wave + NT * i;
             const int slot = run + ln;
-            const int x = slot / CPR, c = (slot % CPR) ^ (x & (SW - 1));
+            const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
             const unsigned goff = (unsigned)((kv0 + x) * RB + c * 16);
             dma16(kwords, kb + run * 16, goff);
             dma16(vwords, kb + TILE + run * 16, goff);
@@ -164,12 +184,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
     // the uniform row offsets (multiples of 16) leave unchanged.
     int kofs[NKS];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) kofs[s] = lds_off<RB>(l32, 2 * s + hh);
-    int vofs[ND];
+    for (int s = 0; s < NKS; ++s) kofs[s] = lds_pos<RB>(l32, 2 * s + hh);
+    int vofs[ND][2];   // rows 4hh + cl/4 and 8 rows further
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
         const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
-        vofs[db] = lds_off<RB>(4 * hh + (cl >> 2), ch) + 8 * (cl & 1);
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) vofs[db][h8] = lds_pos<RB>(4 * hh + (cl >> 2) + 8 * h8, ch) + 8 * (cl & 1);
     }
     auto k_read = [&](const lds_u8* tb, int j, i32x4(&a)[NKS]) __attribute__((always_inline)) {
         const lds_u8* kb = tb + 32 * (j & 1) * RB;
@@ -195,11 +216,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
         const lds_u8* vb = tb + TILE + 32 * (j & 1) * RB;
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-            const lds_u8* a = vb + vofs[db];
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) {
-                const i32x2 u0 = read_tr16(a + 16 * sp * RB);
-                const i32x2 u1 = read_tr16(a + (16 * sp + 8) * RB);
+                const i32x2 u0 = read_tr16(vb + 16 * sp * RB + vofs[db][0]);
+                const i32x2 u1 = read_tr16(vb + 16 * sp * RB + vofs[db][1]);
                 va[sp][db] = i32x4{u0[0], u0[1], u1[0], u1[1]};
             }
         }
