@@ -49,6 +49,15 @@
 namespace fa {
 
 constexpr int NSLOT = 3;
+
+// Operand read-ahead with one query block per wave (see the kernel):
+// 0 none, 1 V, 2 K and V.
+#ifndef FA_RA_D64
+#define FA_RA_D64 2
+#endif
+#ifndef FA_RA_D128
+#define FA_RA_D128 1
+#endif
 // Largest sum of a lane half's 16 weights of one block kept without moving
 // the reference max: every weight is then at most 2^10.
 constexpr float SUM_LIMIT = 1024.f;
@@ -73,8 +82,16 @@ __device__ __forceinline__ int lds_pos(int x, int c) {
     return x * RB + ((c ^ swz16<RB>(x)) << 4);
 }
 
+// Waves per SIMD the register budget is sized for: three with one query
+// block per wave at D = 64 (three workgroups' LDS rings fit a CU), else two.
+#ifndef FA_WPS_D64
+#define FA_WPS_D64 3
+#endif
+template <int D, int QB>
+constexpr int waves_per_simd() { return (D == 64 && QB == 1) ? FA_WPS_D64 : 2; }
+
 template <int IN, int OUT, int D, int NW, int QB>
-__global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
+__global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_kernel(Params p) {
     constexpr int NT = 64 * NW;
     constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
@@ -285,6 +302,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
     // the start of sub-tile j's first step kpf holds K of sub-tile j.
     constexpr bool PF = QB == 2;
     i32x4 kpf[NKS];
+    // With one query block per wave, operands are read a step ahead of their
+    // MFMAs: RA >= 1 reads V of sub-tile j in step j (vb[j % 2]) for the
+    // P.V of step j+1; RA == 2 also keeps kpf = K of sub-tile j+1 at the
+    // start of step j, read in step j-1.
+    constexpr int RA = (QB == 1) ? ((D == 64) ? FA_RA_D64 : FA_RA_D128) : 0;
+    i32x4 vb[2][2][ND];
 
     // After the first p_phase of block (j, qb): masking of edge blocks, the
     // exact redo for flagged rows, the residual pass and the row sums (a
@@ -337,9 +360,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
                                       pack2<IN>(pr[o + 6] - unpack_lo<IN>(h[3]), pr[o + 7] - unpack_hi<IN>(h[3]))};
                 lo[sp] = i32x4{sr ? d[0] : 0, sr ? d[1] : 0, sr ? d[2] : 0, sr ? d[3] : 0};
             }
-            i32x4 vt[2][ND];
-            v_operands(lds_cur, j, vt);   // sub-tile j lies in the loop's current tile
-            pv(qb, vt, lo);
+            if constexpr (RA >= 1) {
+                if (j & 1) pv(qb, vb[1], lo); else pv(qb, vb[0], lo);   // V of sub-tile j, read this step
+            } else {
+                i32x4 vt[2][ND];
+                v_operands(lds_cur, j, vt);   // sub-tile j lies in the loop's current tile
+                pv(qb, vt, lo);
+            }
         }
     };
 
@@ -368,36 +395,56 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
         float ms = (cls == TILE_SKIP) ? INFINITY : ((m[qb] == -INFINITY) ? 0.f : m[qb]);
         float ts;
         const int t = j >> 1;   // the loop's current tile
-        if (load_v) v_operands(((jp >> 1) == t) ? lds_cur : lds_prev, jp, va);
+        if constexpr (RA >= 1) {
+            v_operands(lds_cur, j, vb[KP]);   // for the next step's P.V
+        } else if (load_v) {
+            v_operands(((jp >> 1) == t) ? lds_cur : lds_prev, jp, va);
+        }
         if constexpr (PF) {
             // qb 0: scores of (j, 1) from K(j), then K(j+1) is requested;
             // qb 1: scores of (j+1, 0) from K(j+1), read a step ago
             s_mfma(kpf, qn, Sn);
             if (KP == 0) k_read(((j + 1) >> 1 == t) ? lds_cur : lds_next, j + 1, kpf);
+        } else if constexpr (RA == 2) {
+            s_mfma(kpf, 0, Sn);              // K of sub-tile j+1, read a step ago
+            k_read(lds_next, j + 2, kpf);    // K of sub-tile j+2 lies in tile t+1
         } else {
             scores(((jn >> 1) == t) ? lds_cur : lds_next, jn, qn, Sn);
         }
         p_phase(S, ms, ts, Pc);
-        pv(qpv, va, Pp);
-#ifdef FA_LDS_FIRST
-        // the LDS reads go first and a run of softmax VALU work covers their
-        // latency before the first MFMA that needs them
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FA_LDS_FIRST, 0);
-#endif
+        if constexpr (RA >= 1) pv(qpv, vb[KP ^ 1], Pp);
+        else pv(qpv, va, Pp);
+        if constexpr (RA == 2) {
+            // operands are in registers already: each MFMA is followed by
+            // two exponentials (a wave overlaps transcendental work with its
+            // own MFMA; MFMA and VALU work of different waves on one SIMD do
+            // not overlap) and a share of the other VALU work
+#pragma unroll
+            for (int g = 0; g < NKS + 2 * ND; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);   // transcendental
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+            }
+        }
         tail(j, qb, cls, S, ms, ts, Pc);
     };
 
-    // ---- prologue: Q and tile t_lo land, tile t_lo+1 is requested, the
-    // first block's scores are formed; no weights are pending yet
+    // ---- prologue: Q and tile t_lo land, tile t_lo+1 is requested (with
+    // RA == 2 it lands too and tile t_lo+2 is requested), the first block's
+    // scores are formed; no weights are pending yet
     if (t_lo < t_hi) issue_tile(t_lo);
+    if (RA == 2 && t_lo + 1 < t_hi) issue_tile(t_lo + 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
-    if (t_lo + 1 < t_hi) issue_tile(t_lo + 1);
+    if (RA != 2 && t_lo + 1 < t_hi) issue_tile(t_lo + 1);
+    if (RA == 2 && t_lo + 2 < t_hi) issue_tile(t_lo + 2);
     if (t_lo < t_hi) {
         if constexpr (PF) {
             k_read(lds_cur, 2 * t_lo, kpf);
             s_mfma(kpf, 0, sbuf[0]);
+        } else if constexpr (RA == 2) {
+            scores(lds_cur, 2 * t_lo, 0, sbuf[0]);
+            k_read(lds_cur, 2 * t_lo + 1, kpf);
         } else {
             scores(lds_cur, 2 * t_lo, 0, sbuf[0]);
         }
@@ -408,7 +455,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
         for (int sp = 0; sp < 2; ++sp) {
             pbuf[b][sp] = i32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int db = 0; db < ND; ++db) va[sp][db] = i32x4{0, 0, 0, 0};
+            for (int db = 0; db < ND; ++db) {
+                va[sp][db] = i32x4{0, 0, 0, 0};
+                vb[b][sp][db] = i32x4{0, 0, 0, 0};
+            }
         }
 
     // ---- main loop: iteration i runs steps 2i and 2i+1 (sub-tile i's two
@@ -435,6 +485,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
             step(std::integral_constant<int, 0>{}, 2 * i);
             step(std::integral_constant<int, 1>{}, 2 * i + 1);
             if (i & 1) rotate();
+        } else if constexpr (RA == 2) {
+            // the K read-ahead of tile i's first step already reads tile
+            // i+1, and tile i-1 was last read in the step before: one barrier
+            // before the tile does both (tile t_lo+1 landed in the prologue)
+            if (i > i_lo) tile_barrier(i);
+            step(std::integral_constant<int, 0>{}, 2 * i);
+            step(std::integral_constant<int, 1>{}, 2 * i + 1);
+            rotate();
         } else {
             step(std::integral_constant<int, 0>{}, 2 * i);
             tile_barrier(i);
@@ -444,8 +502,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fa_fwd16_kernel(Params p) {
     }
     // ---- the last step's P.V (zero weights if that step was skipped)
     if (t_lo < t_hi) {
-        v_operands(tile_lds(t_hi - 1), 2 * t_hi - 1, va);
-        pv(QB - 1, va, pbuf[1]);
+        if constexpr (RA >= 1) {
+            pv(0, vb[1], pbuf[1]);   // V of the last sub-tile, read in its step
+        } else {
+            v_operands(tile_lds(t_hi - 1), 2 * t_hi - 1, va);
+            pv(QB - 1, va, pbuf[1]);
+        }
     }
 
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
