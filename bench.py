@@ -183,7 +183,7 @@ def main():
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic_for(w.name),
-                     "kernel": "fa_fwd_kernel", "flop_per_launch": fl,
+                     "kernel": "fa_fwd_kernel" if w.in_dtype == "e4m3" else "fa_fwd16_kernel", "flop_per_launch": fl,
                      "algorithmic_hbm_bytes": algorithmic_bytes(w),
                      "timing": "HIP events on the launch stream, mean over the timed steps"},
         "wall_s_timed_region": round(wall, 4),
