@@ -172,6 +172,13 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, unsigned lds_base, unsi
                  : "v"(voff), "s"(lds_base), "s"(rsrc)
                  : "memory", "m0");
 }
+// The same with a wave-uniform byte offset soff added to every lane's voff.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, unsigned lds_base, unsigned voff, unsigned soff) {
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+                 :
+                 : "v"(voff), "s"(lds_base), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
 
 // ds_read_b64_tr_b16 at an LDS byte address: in each 16-lane group, lanes
 // 4r..4r+3 name row r of a 4 x 16 block of 16-bit values (8 bytes each) and

@@ -163,19 +163,23 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
     const i32x4 kwords = rsrc_words(kp, (unsigned)(Nk * RB));
     const i32x4 vwords = rsrc_words(vp, (unsigned)(Nk * RB));
     const unsigned smem_base = (unsigned)(unsigned long long)(lds_u8*)smem;
+    // Copy i of a lane fills tile row x + i*NT/CPR: the swizzle depends on the
+    // row mod 16 and NT/CPR is a multiple of 16, so one per-lane offset serves
+    // every copy and every tile; the rest is a wave-uniform offset.
+    static_assert((NT / CPR) % 16 == 0, "copy rows");
+    const unsigned dma_voff = [&] {
+        const int slot = 64 * wave + lane;
+        const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
+        return (unsigned)(x * RB + c * 16);
+    }();
     auto issue_tile = [&](int t) {
-        const int kv0 = t * BC;
         const unsigned kb = smem_base + (unsigned)((t % NSLOT) * SLOT);
-        int ln = lane;
-        asm volatile("" : "+v"(ln));   // offsets are recomputed per tile, not held in registers
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
             const int run = 64 * wave + NT * i;
-            const int slot = run + ln;
-            const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
-            const unsigned goff = (unsigned)((kv0 + x) * RB + c * 16);
-            dma16(kwords, kb + run * 16, goff);
-            dma16(vwords, kb + TILE + run * 16, goff);
+            const unsigned soff = (unsigned)((t * BC + i * (NT / CPR)) * RB);
+            dma16(kwords, kb + run * 16, dma_voff, soff);
+            dma16(vwords, kb + TILE + run * 16, dma_voff, soff);
         }
     };
     auto tile_lds = [&](int t) { return (const lds_u8*)(smem + (t % NSLOT) * SLOT); };
@@ -188,11 +192,8 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
         const int a0 = w0 + 32 * qb;
         block_ranges32(a0, min(a0 + 32, w1), Nq, Nk, causal, window, &jf0[qb], &jf1[qb], &ju0[qb], &ju1[qb]);
     }
-    auto block_class = [&](int j, int qb) {
-        const bool full = (unsigned)(j - jf0[qb]) < (unsigned)(jf1[qb] - jf0[qb]);
-        const bool any = (unsigned)(j - ju0[qb]) < (unsigned)(ju1[qb] - ju0[qb]);
-        return full ? (int)TILE_FULL : (any ? (int)TILE_EDGE : (int)TILE_SKIP);
-    };
+    auto block_skip = [&](int j, int qb) { return (unsigned)(j - ju0[qb]) >= (unsigned)(ju1[qb] - ju0[qb]); };
+    auto block_full = [&](int j, int qb) { return (unsigned)(j - jf0[qb]) < (unsigned)(jf1[qb] - jf0[qb]); };
 
     // S^T of block (j, qb): element r of lane (l32, hh) is key
     // 32j + 8(r/4) + 4hh + r%4 against query w0 + 32qb + l32.
@@ -311,63 +312,71 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
 
     // After the first p_phase of block (j, qb): masking of edge blocks, the
     // exact redo for flagged rows, the residual pass and the row sums (a
-    // skipped block changes nothing). S still holds the block's scores.
-    auto tail = [&](int j, int qb, int cls, f32x16& S, float& ms, float& ts, i32x4(&hi)[2])
+    // skipped block changes nothing: its weights and ts are zero). The common
+    // path keeps no scores: the rare path forms the block's scores again from
+    // K in LDS (sub-tile j lies in the loop's current tile), the same bits.
+    auto tail = [&](int j, int qb, bool skip, float& ms, float& ts, i32x4(&hi)[2])
         __attribute__((always_inline)) {
-        const bool active = cls != TILE_SKIP;
-        bool trig = active & ((lh[qb] == 0.f) | !(ts <= SUM_LIMIT));
-        if (cls == TILE_EDGE) {
-            // the weights so far saw every key of the sub-tile: mask, form
-            // them again, and decide on the visible keys alone
-            mask(j, qb, S);
-            p_phase(S, ms, ts, hi);
-            trig = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
-        }
-        if (__builtin_amdgcn_ballot_w64(trig) != 0) {
-            const unsigned tr = trig ? 1u : 0u;
-            auto pr = __builtin_amdgcn_permlane32_swap(tr, tr, false, false);
-            const bool row = (pr[0] | pr[1]) != 0;
-            float mx = S[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-            mx = max_halves(mx);
-            const float mnew = row ? fmaxf(m[qb], mx * c2) : m[qb];
-            const bool mv = mnew != m[qb];
-            const float alpha = mv ? __builtin_amdgcn_exp2f(m[qb] - mnew) : 1.f;
-            m[qb] = mnew;
-            if (__builtin_amdgcn_ballot_w64(mv) != 0) {
-                lh[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha;
+        const bool edge = !skip & !block_full(j, qb);
+        const bool first = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
+        const bool flag = !skip & (first | (ts * 3.f > lh[qb]));
+        if (edge || __builtin_amdgcn_ballot_w64(flag) != 0) {
+            f32x16 S;
+            scores(lds_cur, j, qb, S);
+            bool trig = !skip & first;
+            if (edge) {
+                // the weights so far saw every key of the sub-tile: mask, form
+                // them again, and decide on the visible keys alone
+                mask(j, qb, S);
+                p_phase(S, ms, ts, hi);
+                trig = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
             }
-            ms = (mnew == -INFINITY) ? 0.f : mnew;
-            p_phase(S, ms, ts, hi);
+            if (__builtin_amdgcn_ballot_w64(trig) != 0) {
+                const unsigned tr = trig ? 1u : 0u;
+                auto pr = __builtin_amdgcn_permlane32_swap(tr, tr, false, false);
+                const bool row = (pr[0] | pr[1]) != 0;
+                float mx = S[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+                mx = max_halves(mx);
+                const float mnew = row ? fmaxf(m[qb], mx * c2) : m[qb];
+                const bool mv = mnew != m[qb];
+                const float alpha = mv ? __builtin_amdgcn_exp2f(m[qb] - mnew) : 1.f;
+                m[qb] = mnew;
+                if (__builtin_amdgcn_ballot_w64(mv) != 0) {
+                    lh[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha;
+                }
+                ms = (mnew == -INFINITY) ? 0.f : mnew;
+                p_phase(S, ms, ts, hi);
+            }
+            const bool sr = !skip & (ts * 3.f > lh[qb]);
+            if (__builtin_amdgcn_ballot_w64(sr) != 0) {
+                i32x4 lo[2];
+                float pr[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    const int o = 8 * sp;
+                    const i32x4 h = hi[sp];
+                    const i32x4 d = i32x4{pack2<IN>(pr[o + 0] - unpack_lo<IN>(h[0]), pr[o + 1] - unpack_hi<IN>(h[0])),
+                                          pack2<IN>(pr[o + 2] - unpack_lo<IN>(h[1]), pr[o + 3] - unpack_hi<IN>(h[1])),
+                                          pack2<IN>(pr[o + 4] - unpack_lo<IN>(h[2]), pr[o + 5] - unpack_hi<IN>(h[2])),
+                                          pack2<IN>(pr[o + 6] - unpack_lo<IN>(h[3]), pr[o + 7] - unpack_hi<IN>(h[3]))};
+                    lo[sp] = i32x4{sr ? d[0] : 0, sr ? d[1] : 0, sr ? d[2] : 0, sr ? d[3] : 0};
+                }
+                if constexpr (RA >= 1) {
+                    if (j & 1) pv(qb, vb[1], lo); else pv(qb, vb[0], lo);   // V of sub-tile j, read this step
+                } else {
+                    i32x4 vt[2][ND];
+                    v_operands(lds_cur, j, vt);
+                    pv(qb, vt, lo);
+                }
+            }
         }
-        const bool sr = active & (ts * 3.f > lh[qb]);
         lh[qb] += ts;   // zero for a skipped block
-        if (__builtin_amdgcn_ballot_w64(sr) != 0) {
-            i32x4 lo[2];
-            float pr[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
-#pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
-                const int o = 8 * sp;
-                const i32x4 h = hi[sp];
-                const i32x4 d = i32x4{pack2<IN>(pr[o + 0] - unpack_lo<IN>(h[0]), pr[o + 1] - unpack_hi<IN>(h[0])),
-                                      pack2<IN>(pr[o + 2] - unpack_lo<IN>(h[1]), pr[o + 3] - unpack_hi<IN>(h[1])),
-                                      pack2<IN>(pr[o + 4] - unpack_lo<IN>(h[2]), pr[o + 5] - unpack_hi<IN>(h[2])),
-                                      pack2<IN>(pr[o + 6] - unpack_lo<IN>(h[3]), pr[o + 7] - unpack_hi<IN>(h[3]))};
-                lo[sp] = i32x4{sr ? d[0] : 0, sr ? d[1] : 0, sr ? d[2] : 0, sr ? d[3] : 0};
-            }
-            if constexpr (RA >= 1) {
-                if (j & 1) pv(qb, vb[1], lo); else pv(qb, vb[0], lo);   // V of sub-tile j, read this step
-            } else {
-                i32x4 vt[2][ND];
-                v_operands(lds_cur, j, vt);   // sub-tile j lies in the loop's current tile
-                pv(qb, vt, lo);
-            }
-        }
     };
 
     // ---- one step (see the file comment); KP = u % 2 picks the buffers.
@@ -389,10 +398,12 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
         f32x16& Sn = sbuf[KP ^ 1];
         i32x4(&Pc)[2] = pbuf[KP];
         i32x4(&Pp)[2] = pbuf[KP ^ 1];
-        const int cls = block_class(j, qb);
+        const bool skip = block_skip(j, qb);
         // a skipped block's weights are 2^-inf = 0: the next step's P.V of
-        // them adds exactly nothing and the sums are unchanged
-        float ms = (cls == TILE_SKIP) ? INFINITY : ((m[qb] == -INFINITY) ? 0.f : m[qb]);
+        // them adds exactly nothing and the sums are unchanged. Before a row's
+        // first reference (m = -inf) the weights come out +inf or NaN; such
+        // a row has no weight yet and always takes the exact redo.
+        float ms = skip ? INFINITY : m[qb];
         float ts;
         const int t = j >> 1;   // the loop's current tile
         if constexpr (RA >= 1) {
@@ -426,7 +437,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
             }
         }
-        tail(j, qb, cls, S, ms, ts, Pc);
+        tail(j, qb, skip, ms, ts, Pc);
     };
 
     // ---- prologue: Q and tile t_lo land, tile t_lo+1 is requested (with
