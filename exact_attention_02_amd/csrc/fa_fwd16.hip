@@ -61,6 +61,13 @@ constexpr int NSLOT = 3;
 // Largest sum of a lane half's 16 weights of one block kept without moving
 // the reference max: every weight is then at most 2^10.
 constexpr float SUM_LIMIT = 1024.f;
+// Tiles at the start of a wave's key range whose steps keep the fp32 weights
+// and take the residual pass on every lane (the running sums are small there,
+// so most rows need it).
+#ifndef FA_EARLY_TILES
+#define FA_EARLY_TILES 4
+#endif
+constexpr int EARLY_TILES = FA_EARLY_TILES;
 
 // LDS layout of a K or V tile: row x of RB bytes holds its 16-byte chunk c at
 // position c ^ swz(x). LDS serves 256 bytes (64 banks of 4 bytes) per cycle:
@@ -266,8 +273,8 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
 
     // p = 2^(c*s - ms) for the 16 scores, their sum (a fixed pairwise order)
     // and p rounded to the MFMA type.
-    auto p_phase = [&](const f32x16& S, float ms, float& ts, i32x4(&hi)[2]) __attribute__((always_inline)) {
-        float pr[16];
+    auto p_phase_pr = [&](const f32x16& S, float ms, float& ts, i32x4(&hi)[2], float(&pr)[16])
+        __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
         float s8[8];
@@ -279,6 +286,24 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
             const int o = 8 * sp;
             hi[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
                            pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
+        }
+    };
+    auto p_phase = [&](const f32x16& S, float ms, float& ts, i32x4(&hi)[2]) __attribute__((always_inline)) {
+        float pr[16];
+        p_phase_pr(S, ms, ts, hi, pr);
+    };
+    // The rounding residual of the weights, lo = p - hi rounded to the MFMA
+    // type (zero where on is false).
+    auto residual = [&](const float(&pr)[16], const i32x4(&hi)[2], bool on, i32x4(&lo)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            const int o = 8 * sp;
+            const i32x4 h = hi[sp];
+            const i32x4 d = i32x4{pack2<IN>(pr[o + 0] - unpack_lo<IN>(h[0]), pr[o + 1] - unpack_hi<IN>(h[0])),
+                                  pack2<IN>(pr[o + 2] - unpack_lo<IN>(h[1]), pr[o + 3] - unpack_hi<IN>(h[1])),
+                                  pack2<IN>(pr[o + 4] - unpack_lo<IN>(h[2]), pr[o + 5] - unpack_hi<IN>(h[2])),
+                                  pack2<IN>(pr[o + 6] - unpack_lo<IN>(h[3]), pr[o + 7] - unpack_hi<IN>(h[3]))};
+            lo[sp] = i32x4{on ? d[0] : 0, on ? d[1] : 0, on ? d[2] : 0, on ? d[3] : 0};
         }
     };
 
@@ -294,6 +319,34 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
     const lds_u8* lds_prev = tile_lds(t_lo + 2);
     const lds_u8* lds_cur = tile_lds(t_lo);
     const lds_u8* lds_next = tile_lds(t_lo + 1);
+    // With K and V read ahead (RA == 2) the steps read K only from the slot
+    // of tile t+1 and V only from the slot of tile t: their per-lane
+    // addresses are kept whole and advanced once per tile, so that a read is
+    // one register plus an immediate offset.
+    const lds_u8* kan[NKS];
+    const lds_u8* van[ND][2];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) kan[s] = lds_next + kofs[s];
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) van[db][h8] = lds_cur + TILE + vofs[db][h8];
+    auto k_read_next = [&](int j, i32x4(&a)[NKS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+            a[s] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(kan[s] + 32 * (j & 1) * RB);
+    };
+    auto v_operands_cur = [&](int j, i32x4(&va)[2][ND]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const i32x2 u0 = read_tr16(van[db][0] + (32 * (j & 1) + 16 * sp) * RB);
+                const i32x2 u1 = read_tr16(van[db][1] + (32 * (j & 1) + 16 * sp) * RB);
+                va[sp][db] = i32x4{u0[0], u0[1], u1[0], u1[1]};
+            }
+        }
+    };
 
     // ---- per-step state; the buffers alternate between even and odd steps
     f32x16 sbuf[2];        // scores of the current step and of the next
@@ -315,11 +368,15 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
     // skipped block changes nothing: its weights and ts are zero). The common
     // path keeps no scores: the rare path forms the block's scores again from
     // K in LDS (sub-tile j lies in the loop's current tile), the same bits.
-    auto tail = [&](int j, int qb, bool skip, float& ms, float& ts, i32x4(&hi)[2])
+    // In the first sub-tiles of a row (EARLY) the residual pass is taken by
+    // every lane from the weights pr kept by the step; later it is taken by
+    // the rows whose new weight exceeds a quarter of their sum so far.
+    auto tail = [&](auto early, int j, int qb, bool skip, float& ms, float& ts, i32x4(&hi)[2], float(&pr)[16])
         __attribute__((always_inline)) {
+        constexpr bool EARLY = decltype(early)::value;
         const bool edge = !skip & !block_full(j, qb);
         const bool first = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
-        const bool flag = !skip & (first | (ts * 3.f > lh[qb]));
+        const bool flag = !skip & (EARLY ? first : (first | (ts * 3.f > lh[qb])));
         if (edge || __builtin_amdgcn_ballot_w64(flag) != 0) {
             f32x16 S;
             scores(lds_cur, j, qb, S);
@@ -328,13 +385,13 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
                 // the weights so far saw every key of the sub-tile: mask, form
                 // them again, and decide on the visible keys alone
                 mask(j, qb, S);
-                p_phase(S, ms, ts, hi);
+                p_phase_pr(S, ms, ts, hi, pr);
                 trig = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
             }
             if (__builtin_amdgcn_ballot_w64(trig) != 0) {
                 const unsigned tr = trig ? 1u : 0u;
-                auto pr = __builtin_amdgcn_permlane32_swap(tr, tr, false, false);
-                const bool row = (pr[0] | pr[1]) != 0;
+                auto pw = __builtin_amdgcn_permlane32_swap(tr, tr, false, false);
+                const bool row = (pw[0] | pw[1]) != 0;
                 float mx = S[0];
 #pragma unroll
                 for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
@@ -349,31 +406,31 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
                     for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha;
                 }
                 ms = (mnew == -INFINITY) ? 0.f : mnew;
-                p_phase(S, ms, ts, hi);
+                p_phase_pr(S, ms, ts, hi, pr);
             }
-            const bool sr = !skip & (ts * 3.f > lh[qb]);
-            if (__builtin_amdgcn_ballot_w64(sr) != 0) {
+            if constexpr (!EARLY) {
+                const bool sr = !skip & (ts * 3.f > lh[qb]);
+                if (__builtin_amdgcn_ballot_w64(sr) != 0) {
+                    float pe[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+                    i32x4 lo[2];
+                    residual(pe, hi, sr, lo);
+                    if constexpr (RA >= 1) {
+                        if (j & 1) pv(qb, vb[1], lo); else pv(qb, vb[0], lo);   // V of sub-tile j, read this step
+                    } else {
+                        i32x4 vt[2][ND];
+                        v_operands(lds_cur, j, vt);
+                        pv(qb, vt, lo);
+                    }
+                }
+            }
+        }
+        if constexpr (EARLY) {
+            if (!skip) {
                 i32x4 lo[2];
-                float pr[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
-#pragma unroll
-                for (int sp = 0; sp < 2; ++sp) {
-                    const int o = 8 * sp;
-                    const i32x4 h = hi[sp];
-                    const i32x4 d = i32x4{pack2<IN>(pr[o + 0] - unpack_lo<IN>(h[0]), pr[o + 1] - unpack_hi<IN>(h[0])),
-                                          pack2<IN>(pr[o + 2] - unpack_lo<IN>(h[1]), pr[o + 3] - unpack_hi<IN>(h[1])),
-                                          pack2<IN>(pr[o + 4] - unpack_lo<IN>(h[2]), pr[o + 5] - unpack_hi<IN>(h[2])),
-                                          pack2<IN>(pr[o + 6] - unpack_lo<IN>(h[3]), pr[o + 7] - unpack_hi<IN>(h[3]))};
-                    lo[sp] = i32x4{sr ? d[0] : 0, sr ? d[1] : 0, sr ? d[2] : 0, sr ? d[3] : 0};
-                }
-                if constexpr (RA >= 1) {
-                    if (j & 1) pv(qb, vb[1], lo); else pv(qb, vb[0], lo);   // V of sub-tile j, read this step
-                } else {
-                    i32x4 vt[2][ND];
-                    v_operands(lds_cur, j, vt);
-                    pv(qb, vt, lo);
-                }
+                residual(pr, hi, true, lo);
+                if (j & 1) pv(qb, vb[1], lo); else pv(qb, vb[0], lo);   // V of sub-tile j, read this step
             }
         }
         lh[qb] += ts;   // zero for a skipped block
@@ -383,8 +440,9 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
     // Branch-free apart from the rare exact path: the look-ahead scores and
     // the softmax are formed on every step, and a skipped step's weights are
     // zeroed, so the next step's P.V adds exactly nothing for it.
-    auto step = [&](auto kp, int u) __attribute__((always_inline)) {
+    auto step = [&](auto kp, int u, auto early) __attribute__((always_inline)) {
         constexpr int KP = decltype(kp)::value;
+        constexpr bool EARLY = decltype(early)::value;   // only with RA == 2
         const int j = u / QB;
         constexpr int qb = KP % QB;                 // steps alternate query blocks when QB = 2
         constexpr int qn = (KP + 1) % QB;           // query block of step u+1
@@ -406,7 +464,9 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
         float ms = skip ? INFINITY : m[qb];
         float ts;
         const int t = j >> 1;   // the loop's current tile
-        if constexpr (RA >= 1) {
+        if constexpr (RA == 2) {
+            v_operands_cur(j, vb[KP]);        // for the next step's P.V (and an early residual)
+        } else if constexpr (RA == 1) {
             v_operands(lds_cur, j, vb[KP]);   // for the next step's P.V
         } else if (load_v) {
             v_operands(((jp >> 1) == t) ? lds_cur : lds_prev, jp, va);
@@ -416,13 +476,17 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
             // qb 1: scores of (j+1, 0) from K(j+1), read a step ago
             s_mfma(kpf, qn, Sn);
             if (KP == 0) k_read(((j + 1) >> 1 == t) ? lds_cur : lds_next, j + 1, kpf);
+        } else if constexpr (RA == 2 && EARLY) {
+            // no read-ahead: the registers hold the weights for the residual
+            scores((KP == 0) ? lds_cur : lds_next, j + 1, 0, Sn);
         } else if constexpr (RA == 2) {
             s_mfma(kpf, 0, Sn);              // K of sub-tile j+1, read a step ago
-            k_read(lds_next, j + 2, kpf);    // K of sub-tile j+2 lies in tile t+1
+            k_read_next(j + 2, kpf);         // K of sub-tile j+2 lies in tile t+1
         } else {
             scores(((jn >> 1) == t) ? lds_cur : lds_next, jn, qn, Sn);
         }
-        p_phase(S, ms, ts, Pc);
+        float pr[16];
+        p_phase_pr(S, ms, ts, Pc, pr);
         if constexpr (RA >= 1) pv(qpv, vb[KP ^ 1], Pp);
         else pv(qpv, va, Pp);
         if constexpr (RA == 2) {
@@ -437,7 +501,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
             }
         }
-        tail(j, qb, skip, ms, ts, Pc);
+        tail(early, j, qb, skip, ms, ts, Pc, pr);
     };
 
     // ---- prologue: Q and tile t_lo land, tile t_lo+1 is requested (with
@@ -454,8 +518,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
             k_read(lds_cur, 2 * t_lo, kpf);
             s_mfma(kpf, 0, sbuf[0]);
         } else if constexpr (RA == 2) {
-            scores(lds_cur, 2 * t_lo, 0, sbuf[0]);
-            k_read(lds_cur, 2 * t_lo + 1, kpf);
+            scores(lds_cur, 2 * t_lo, 0, sbuf[0]);   // the early steps read K just in time
         } else {
             scores(lds_cur, 2 * t_lo, 0, sbuf[0]);
         }
@@ -485,30 +548,56 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
         if (t + 2 < t_hi) issue_tile(t + 2);
     };
     auto rotate = [&]() __attribute__((always_inline)) {
+        if constexpr (RA == 2) {
+            const int dk = (int)(lds_prev - lds_next), dv = (int)(lds_next - lds_cur);
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) kan[s] += dk;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int h8 = 0; h8 < 2; ++h8) van[db][h8] += dv;
+        }
         const lds_u8* x = lds_prev;
         lds_prev = lds_cur;
         lds_cur = lds_next;
         lds_next = x;
     };
-    for (int i = i_lo; i < i_hi; ++i) {
-        if constexpr (PF) {
-            if (i & 1) tile_barrier(i >> 1);
-            step(std::integral_constant<int, 0>{}, 2 * i);
-            step(std::integral_constant<int, 1>{}, 2 * i + 1);
-            if (i & 1) rotate();
-        } else if constexpr (RA == 2) {
-            // the K read-ahead of tile i's first step already reads tile
-            // i+1, and tile i-1 was last read in the step before: one barrier
-            // before the tile does both (tile t_lo+1 landed in the prologue)
-            if (i > i_lo) tile_barrier(i);
-            step(std::integral_constant<int, 0>{}, 2 * i);
-            step(std::integral_constant<int, 1>{}, 2 * i + 1);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using NotEarly = std::false_type;
+    if constexpr (RA == 2) {
+        // the K read-ahead of tile t's first step already reads tile t+1, and
+        // tile t-1 was last read in the step before: one barrier before the
+        // tile does both (tile t_lo+1 landed in the prologue). The first
+        // EARLY_TILES tiles take the early steps.
+        const int t_e = min(t_hi, t_lo + EARLY_TILES);
+        int t = t_lo;
+        for (; t < t_e; ++t) {
+            if (t > t_lo) tile_barrier(t);
+            step(I0{}, 2 * t, std::true_type{});
+            step(I1{}, 2 * t + 1, std::true_type{});
             rotate();
-        } else {
-            step(std::integral_constant<int, 0>{}, 2 * i);
-            tile_barrier(i);
-            step(std::integral_constant<int, 1>{}, 2 * i + 1);
+        }
+        if (t < t_hi) k_read(lds_cur, 2 * t + 1, kpf);   // the read-ahead of the first later step
+        for (; t < t_hi; ++t) {
+            if (t > t_lo) tile_barrier(t);
+            step(I0{}, 2 * t, NotEarly{});
+            step(I1{}, 2 * t + 1, NotEarly{});
             rotate();
+        }
+    } else {
+        for (int i = i_lo; i < i_hi; ++i) {
+            if constexpr (PF) {
+                if (i & 1) tile_barrier(i >> 1);
+                step(I0{}, 2 * i, NotEarly{});
+                step(I1{}, 2 * i + 1, NotEarly{});
+                if (i & 1) rotate();
+            } else {
+                step(I0{}, 2 * i, NotEarly{});
+                tile_barrier(i);
+                step(I1{}, 2 * i + 1, NotEarly{});
+                rotate();
+            }
         }
     }
     // ---- the last step's P.V (zero weights if that step was skipped)
