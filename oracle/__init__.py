@@ -42,6 +42,9 @@ def load(path: str = _LIB):
     L = ctypes.c_long
     fn.argtypes = [P, P, P, P, P, L, L, L, L, L, ctypes.c_double, ctypes.c_int, L, P, L, ctypes.c_int]
     fn.restype = ctypes.c_int
+    fw = lib.oracle_attn_fwd_window
+    fw.argtypes = [P, P, P, P, P, L, L, L, L, L, ctypes.c_double, L, L, P, L, ctypes.c_int]
+    fw.restype = ctypes.c_int
     return lib
 
 
@@ -71,15 +74,29 @@ def decode(x: torch.Tensor, descale: float = 1.0) -> torch.Tensor:
 
 
 def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
-              rows=None, threads=None, lib=None):
+              rows=None, threads=None, lib=None, window_left=None, window_right=None):
     """float64 O and LSE of softmax(scale * Q K^T) V.
 
     q [B,H,Nq,D], k and v [B,H,Nk,D] (CPU or device tensors of any float dtype).
     scale is used as float64(fp32(scale)) -- the fp32 value the kernel gets.
     rows: None for every row (O [B,H,Nq,D], LSE [B,H,Nq]); otherwise an
     iterable of flattened row ids (b*H + h)*Nq + i (O [n,D], LSE [n]).
+    The mask is (causal, window), or, when window_left or window_right is
+    given, the keys [i' - window_left, i' + window_right] of row i (None or a
+    negative extent: that side open); causal and window are then ignored.
     """
     lib = lib or _get()
+    if window_left is not None or window_right is not None:
+        wl = -1 if window_left is None else int(window_left)
+        wr = -1 if window_right is None else int(window_right)
+
+        def call(Qp, Kp, Vp, Op, Lp, B_, H_, rows_p, nrows):
+            return lib.oracle_attn_fwd_window(Qp, Kp, Vp, Op, Lp, B_, H_, Nq, Nk, D, scale64, wl, wr,
+                                              rows_p, nrows, threads)
+    else:
+        def call(Qp, Kp, Vp, Op, Lp, B_, H_, rows_p, nrows):
+            return lib.oracle_attn_fwd(Qp, Kp, Vp, Op, Lp, B_, H_, Nq, Nk, D, scale64, int(bool(causal)),
+                                       int(window), rows_p, nrows, threads)
     threads = threads or default_threads()
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
@@ -90,8 +107,7 @@ def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
         V = decode(v, descales[2])
         O = torch.empty((B, H, Nq, D), dtype=torch.float64)
         LSE = torch.empty((B, H, Nq), dtype=torch.float64)
-        rc = lib.oracle_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), LSE.data_ptr(),
-                                 B, H, Nq, Nk, D, scale64, int(bool(causal)), int(window), None, 0, threads)
+        rc = call(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), LSE.data_ptr(), B, H, None, 0)
         if rc != 0:
             raise RuntimeError(f"oracle_attn_fwd returned {rc}")
         return O, LSE
@@ -109,9 +125,8 @@ def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
         local = (rows[sel] % Nq).contiguous()
         Oh = torch.empty((sel.numel(), D), dtype=torch.float64)
         Lh = torch.empty((sel.numel(),), dtype=torch.float64)
-        rc = lib.oracle_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), Oh.data_ptr(), Lh.data_ptr(),
-                                 1, 1, Nq, Nk, D, scale64, int(bool(causal)), int(window),
-                                 local.data_ptr(), local.numel(), threads)
+        rc = call(Q.data_ptr(), K.data_ptr(), V.data_ptr(), Oh.data_ptr(), Lh.data_ptr(), 1, 1,
+                  local.data_ptr(), local.numel())
         if rc != 0:
             raise RuntimeError(f"oracle_attn_fwd returned {rc}")
         O[sel] = Oh
@@ -130,6 +145,25 @@ def visible_keys(i: int, Nq: int, Nk: int, causal: bool, window: int):
     hi = max(hi, 0)
     lo = min(lo, hi)
     return lo, hi
+
+
+def visible_keys_window(i: int, Nq: int, Nk: int, window_left: int, window_right: int):
+    """[lo, hi) of the keys row i sees under the extents mask (negative: open side)."""
+    ip = i + (Nk - Nq)
+    lo = max(0, ip - window_left) if window_left >= 0 else 0
+    hi = min(Nk, ip + window_right + 1) if window_right >= 0 else Nk
+    hi = max(hi, 0)
+    lo = min(lo, hi)
+    return lo, hi
+
+
+def pair_count_window(Nq: int, Nk: int, window_left: int, window_right: int) -> int:
+    """Number of (query, key) pairs the extents mask keeps, per (b, h)."""
+    total = 0
+    for i in range(Nq):
+        lo, hi = visible_keys_window(i, Nq, Nk, window_left, window_right)
+        total += hi - lo
+    return total
 
 
 def pair_count(Nq: int, Nk: int, causal: bool, window: int) -> int:

@@ -25,6 +25,13 @@
  * module; the window keeps the w keys i-w < j <= i (a causal sliding window;
  * the same module's "Sparse patterns" section names sliding windows).
  *
+ * oracle_attn_fwd_window takes the mask as two extents instead:
+ *   J  = { j < Nk : (wl < 0 || j >= i' - wl) && (wr < 0 || j <= i' + wr) }
+ * This is the sliding window of that "Sparse patterns" section, where each
+ * token sees the w tokens on either side of it (its example mask keeps columns
+ * max(0, i-w) .. min(n, i+w+1)-1 of row i), with the two sides allowed to
+ * differ and a negative extent leaving a side open.
+ *
  * Inputs are float64 arrays the caller decoded exactly from the storage
  * dtype. Layout: Q [B,H,Nq,D], K and V [B,H,Nk,D], contiguous.
  */
@@ -41,6 +48,8 @@ typedef struct {
     long B, H, Nq, Nk, D, window;
     double scale;
     int causal;
+    int extents;        /* 1: the mask is (wl, wr) below, not (causal, window) */
+    long wl, wr;
     const long *rows;   /* flattened (b*H + h)*Nq + i, or NULL for every row */
     long nrows;
     long next;          /* work counter, shared */
@@ -60,8 +69,13 @@ static int one_row(const job_t *jb, long flat, double *s, double *o_row, double 
 
     /* Visible keys J_i: j in [lo, hi). */
     long lo = 0, hi = Nk;
-    if (jb->causal) hi = ip + 1 < Nk ? ip + 1 : Nk;
-    if (jb->window > 0) lo = ip - jb->window + 1 > 0 ? ip - jb->window + 1 : 0;
+    if (jb->extents) {
+        if (jb->wl >= 0) lo = ip - jb->wl > 0 ? ip - jb->wl : 0;
+        if (jb->wr >= 0) hi = ip + jb->wr + 1 < Nk ? ip + jb->wr + 1 : Nk;
+    } else {
+        if (jb->causal) hi = ip + 1 < Nk ? ip + 1 : Nk;
+        if (jb->window > 0) lo = ip - jb->window + 1 > 0 ? ip - jb->window + 1 : 0;
+    }
     if (hi < 0) hi = 0;
     if (lo > hi) lo = hi;
 
@@ -136,6 +150,8 @@ static void *worker(void *arg)
  * Returns 0 on success, 1 if some softmax row failed the sum-to-one check,
  * -1 on bad arguments.
  */
+static int run_job(job_t *jbp, int nthreads);
+
 int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o, double *lse,
                     long B, long H, long Nq, long Nk, long D, double scale, int causal,
                     long window, const long *rows, long nrows, int nthreads)
@@ -147,6 +163,27 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o
     jb.B = B; jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.D = D;
     jb.window = window; jb.scale = scale; jb.causal = causal;
     jb.rows = rows; jb.nrows = nrows;
+    return run_job(&jb, nthreads);
+}
+
+/* The same with the mask as the extents (wl, wr); a negative extent is open. */
+int oracle_attn_fwd_window(const double *q, const double *k, const double *v, double *o, double *lse,
+                           long B, long H, long Nq, long Nk, long D, double scale, long wl, long wr,
+                           const long *rows, long nrows, int nthreads)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D <= 0 || nthreads <= 0) return -1;
+    job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.q = q; jb.k = k; jb.v = v; jb.o = o; jb.lse = lse;
+    jb.B = B; jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.D = D;
+    jb.scale = scale; jb.extents = 1; jb.wl = wl; jb.wr = wr;
+    jb.rows = rows; jb.nrows = nrows;
+    return run_job(&jb, nthreads);
+}
+
+static int run_job(job_t *jbp, int nthreads)
+{
+    job_t jb = *jbp;
     pthread_mutex_init(&jb.lock, NULL);
     if (nthreads > 256) nthreads = 256;
     pthread_t tid[256];

@@ -43,6 +43,30 @@ def mask_matrix(Nq, Nk, causal, window):
     return keep
 
 
+def mask_matrix_window(Nq, Nk, wl, wr):
+    """Boolean [Nq, Nk] keep-mask of the extents mask, independently of the oracle:
+    row i keeps j with i' - wl <= j <= i' + wr (i' = i + Nk - Nq; a negative extent is open)."""
+    i = torch.arange(Nq).view(-1, 1) + (Nk - Nq)
+    j = torch.arange(Nk).view(1, -1)
+    keep = torch.ones(Nq, Nk, dtype=torch.bool)
+    if wl >= 0:
+        keep &= j >= i - wl
+    if wr >= 0:
+        keep &= j <= i + wr
+    return keep
+
+
+def page_sliding_window_mask(n, window):
+    """The sliding-window mask exactly as the inskillml module's sparse-patterns
+    example builds it: row i keeps columns max(0, i - window) .. min(n, i + window + 1) - 1."""
+    mask = torch.zeros(n, n, dtype=torch.bool)
+    for i in range(n):
+        lo = max(0, i - window)
+        hi = min(n, i + window + 1)
+        mask[i, lo:hi] = True
+    return mask
+
+
 # ---------------------------------------------------------------- brute force
 
 def mp_attention(Q, K, V, scale, keep):
@@ -89,6 +113,28 @@ def test_bruteforce_50_digits(Nq, Nk, D, causal, window):
             assert abs(O[0, 0, i, d].item() - float(Om[i][d])) <= 1e-13
 
 
+@pytest.mark.parametrize("Nq,Nk,D,wl,wr", [
+    (4, 4, 3, 1, 1), (5, 5, 4, 0, 2), (5, 5, 3, 2, 0), (4, 4, 4, 0, 0), (3, 6, 3, 3, -1),
+    (6, 3, 3, -1, 1), (5, 5, 3, 1, 1),
+])
+def test_bruteforce_50_digits_window_extents(Nq, Nk, D, wl, wr):
+    Q = rnd((1, 1, Nq, D), 12, 0) * 1.7
+    K = rnd((1, 1, Nk, D), 12, 1) * 1.3
+    V = rnd((1, 1, Nk, D), 12, 2)
+    scale = 0.61
+    O, L = oracle.attention(Q, K, V, scale, window_left=wl, window_right=wr)
+    keep = mask_matrix_window(Nq, Nk, wl, wr)
+    Om, Lm = mp_attention(Q[0, 0], K[0, 0], V[0, 0], float(torch.tensor(scale, dtype=torch.float32)), keep)
+    for i in range(Nq):
+        if Lm[i] == -mpmath.inf:
+            assert L[0, 0, i].item() == -math.inf
+            assert torch.all(O[0, 0, i] == 0)
+            continue
+        assert abs(L[0, 0, i].item() - float(Lm[i])) <= 1e-13 * max(1.0, abs(float(Lm[i])))
+        for d in range(D):
+            assert abs(O[0, 0, i, d].item() - float(Om[i][d])) <= 1e-13
+
+
 # ------------------------------------------------------- independent library
 
 @pytest.mark.parametrize("Nq,Nk,D,causal,window", [
@@ -113,6 +159,37 @@ def test_against_torch_sdpa_float64(Nq, Nk, D, causal, window):
     assert torch.allclose(L[:, :, rows_ok], Lref[:, :, rows_ok], rtol=1e-13, atol=1e-13)
     assert torch.all(O[:, :, ~rows_ok] == 0)
     assert torch.all(L[:, :, ~rows_ok] == -math.inf)
+
+
+@pytest.mark.parametrize("Nq,Nk,D,wl,wr", [
+    (129, 129, 64, 16, 16), (200, 200, 64, 8, 40), (100, 64, 128, -1, 5), (64, 100, 64, 10, -1),
+    (257, 257, 64, 100, 100), (90, 90, 64, 0, 0),
+])
+def test_window_extents_against_torch_sdpa_float64(Nq, Nk, D, wl, wr):
+    B, H = 1, 2
+    Q, K, V = rnd((B, H, Nq, D), 22, 0), rnd((B, H, Nk, D), 22, 1), rnd((B, H, Nk, D), 22, 2)
+    s32 = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+    O, L = oracle.attention(Q, K, V, 1.0 / math.sqrt(D), window_left=wl, window_right=wr)
+    keep = mask_matrix_window(Nq, Nk, wl, wr)
+    Oref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=keep, scale=s32)
+    Lref = torch.logsumexp((torch.matmul(Q, K.transpose(-1, -2)) * s32).masked_fill(~keep, -math.inf), dim=-1)
+    rows_ok = keep.any(dim=1)
+    assert torch.allclose(O[:, :, rows_ok], Oref[:, :, rows_ok], rtol=0, atol=1e-12)
+    assert torch.allclose(L[:, :, rows_ok], Lref[:, :, rows_ok], rtol=1e-13, atol=1e-13)
+    assert torch.all(L[:, :, ~rows_ok] == -math.inf)
+
+
+def test_sliding_window_matches_the_pages_mask_example():
+    """The pages' own sliding-window example (n = 1024, window = 128), mask built as the page builds it."""
+    n, window, D = 1024, 128, 64
+    keep = page_sliding_window_mask(n, window)
+    assert torch.equal(keep, mask_matrix_window(n, n, window, window))
+    Q, K, V = rnd((1, 1, n, D), 23, 0), rnd((1, 1, n, D), 23, 1), rnd((1, 1, n, D), 23, 2)
+    s32 = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+    O, L = oracle.attention(Q, K, V, 1.0 / math.sqrt(D), window_left=window, window_right=window)
+    Oref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=keep, scale=s32)
+    assert torch.allclose(O, Oref, rtol=0, atol=1e-12)
+    assert oracle.pair_count_window(n, n, window, window) == int(keep.sum())
 
 
 # ------------------------------------------------------------- closed forms
@@ -154,6 +231,23 @@ def test_one_hot_score_selects_value_row(D, a, t):
     O, L = oracle.attention(Q, K, V, scale, False, 0)
     assert torch.equal(O[0, 0], V[0, 0, t].expand(N, D))
     assert torch.allclose(L[0, 0], torch.full((N,), a * a * scale, dtype=torch.float64), rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("Nq,Nk,wl,wr", [(40, 40, 5, 5), (40, 40, 0, 7), (30, 50, -1, 3), (50, 30, 4, -1)])
+def test_zero_query_window_extents_gives_mean_of_visible_values(Nq, Nk, wl, wr):
+    D = 64
+    Q = torch.zeros(1, 1, Nq, D, dtype=torch.float64)
+    K, V = rnd((1, 1, Nk, D), 32, 1), rnd((1, 1, Nk, D), 32, 2)
+    O, L = oracle.attention(Q, K, V, 0.125, window_left=wl, window_right=wr)
+    ip = torch.arange(Nq) + (Nk - Nq)
+    for i in range(Nq):
+        lo = max(0, int(ip[i]) - wl) if wl >= 0 else 0
+        hi = min(Nk, int(ip[i]) + wr + 1) if wr >= 0 else Nk
+        if hi <= lo:
+            assert L[0, 0, i].item() == -math.inf
+            continue
+        assert abs(L[0, 0, i].item() - math.log(hi - lo)) <= 1e-13
+        assert torch.allclose(O[0, 0, i], V[0, 0, lo:hi].mean(0), atol=1e-13)
 
 
 def test_window_one_sees_only_itself():
@@ -302,6 +396,12 @@ MUTANTS = {
                            "for (long d = 0; d < D - 1; ++d) dot += qi[d] * kj[d];"),
     "sum_drops_first_key": ("l += s[j];", "if (j > 0) l += s[j];"),
     "output_drops_last_key": ("for (long j = lo; j < hi; ++j) {\n        const double p", "for (long j = lo; j < hi - 1; ++j) {\n        const double p"),
+    "extent_left_off_by_one": ("if (jb->wl >= 0) lo = ip - jb->wl > 0 ? ip - jb->wl : 0;",
+                               "if (jb->wl >= 0) lo = ip - jb->wl + 1 > 0 ? ip - jb->wl + 1 : 0;"),
+    "extent_right_off_by_one": ("if (jb->wr >= 0) hi = ip + jb->wr + 1 < Nk ? ip + jb->wr + 1 : Nk;",
+                                "if (jb->wr >= 0) hi = ip + jb->wr < Nk ? ip + jb->wr : Nk;"),
+    "extents_swapped": ("if (jb->wl >= 0) lo = ip - jb->wl > 0 ? ip - jb->wl : 0;",
+                        "if (jb->wr >= 0) lo = ip - jb->wr > 0 ? ip - jb->wr : 0;"),
 }
 
 
@@ -334,6 +434,18 @@ def pin_suite(lib) -> bool:
         O, L = oracle.attention(Q2, K2, V2, 0.125, True, 1, lib=lib, threads=1)
         if not torch.equal(O, V2):
             return False
+        # the extents mask at 50 digits, both sides bounded and unequal
+        for wl, wr in [(1, 2), (2, 0)]:
+            O, L = oracle.attention(Q, K, V, 0.7, lib=lib, threads=1, window_left=wl, window_right=wr)
+            Om, Lm = mp_attention(Q[0, 0], K[0, 0], V[0, 0], float(torch.tensor(0.7, dtype=torch.float32)),
+                                  mask_matrix_window(4, 6, wl, wr))
+            for i in range(4):
+                if Lm[i] == -mpmath.inf:
+                    if L[0, 0, i].item() != -math.inf:
+                        return False
+                    continue
+                if abs(L[0, 0, i].item() - float(Lm[i])) > 1e-12:
+                    return False
         return True
     except RuntimeError:
         return False
