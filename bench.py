@@ -43,8 +43,24 @@ def visible_pairs(Nq, Nk, causal, window):
     return int(np.clip(hi - lo, 0, None).sum())
 
 
+def visible_pairs_window(Nq, Nk, wl, wr):
+    """Visible pairs per (batch, head) when row i keeps keys [i' - wl, i' + wr] (-1: open side)."""
+    import numpy as np
+    i = np.arange(Nq, dtype=np.int64) + (Nk - Nq)
+    lo = np.maximum(i - wl, 0) if wl >= 0 else np.zeros(Nq, dtype=np.int64)
+    hi = np.minimum(i + wr + 1, Nk) if wr >= 0 else np.full(Nq, Nk, dtype=np.int64)
+    return int(np.clip(hi - lo, 0, None).sum())
+
+
+def pairs(w):
+    if w.window_left is not None or w.window_right is not None:
+        return visible_pairs_window(w.Nq, w.Nk, -1 if w.window_left is None else w.window_left,
+                                    -1 if w.window_right is None else w.window_right)
+    return visible_pairs(w.Nq, w.Nk, w.causal, w.window)
+
+
 def flops(w):
-    return 4.0 * w.D * w.B * w.H * visible_pairs(w.Nq, w.Nk, w.causal, w.window)
+    return 4.0 * w.D * w.B * w.H * pairs(w)
 
 
 def algorithmic_bytes(w):
@@ -82,10 +98,19 @@ def cpu_baseline(w, inp, target_s=15.0):
     g = torch.Generator().manual_seed(1234)
     n_rows_total = w.B * w.H * w.Nq
 
+    ext = w.window_left is not None or w.window_right is not None
+    wl = -1 if w.window_left is None else w.window_left
+    wr = -1 if w.window_right is None else w.window_right
+    mask = dict(window_left=wl, window_right=wr) if ext else {}
+
     def row_pairs(rows):
         i = rows % w.Nq + (w.Nk - w.Nq)
-        hi = torch.clamp(i + 1, max=w.Nk) if w.causal else torch.full_like(i, w.Nk)
-        lo = torch.clamp(i - w.window + 1, min=0) if w.window > 0 else torch.zeros_like(i)
+        if ext:
+            lo = torch.clamp(i - wl, min=0) if wl >= 0 else torch.zeros_like(i)
+            hi = torch.clamp(i + wr + 1, max=w.Nk) if wr >= 0 else torch.full_like(i, w.Nk)
+        else:
+            hi = torch.clamp(i + 1, max=w.Nk) if w.causal else torch.full_like(i, w.Nk)
+            lo = torch.clamp(i - w.window + 1, min=0) if w.window > 0 else torch.zeros_like(i)
         return int(torch.clamp(hi - lo, min=0).sum())
 
     n = 256
@@ -93,7 +118,8 @@ def cpu_baseline(w, inp, target_s=15.0):
         rows = torch.randint(0, n_rows_total, (n,), generator=g)
         t0 = time.perf_counter()
         oracle.attention(inp.q, inp.k, inp.v, w.scale, w.causal, w.window,
-                         descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows, threads=threads)
+                         descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows, threads=threads,
+                         **mask)
         dt = time.perf_counter() - t0
         if dt >= 0.5 * target_s or n >= n_rows_total:
             fl = 4.0 * w.D * row_pairs(rows)
@@ -108,7 +134,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5")
+    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (to scale the FETCH_SIZE/WRITE_SIZE "
@@ -145,6 +171,7 @@ def main():
 
     def step():
         fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window, out=o, lse=lse,
+                     window_left=w.window_left, window_right=w.window_right,
                      descales=descales, stream=stream.cuda_stream)
 
     for _ in range(args.warmup):
@@ -178,7 +205,8 @@ def main():
         "dtype": w.in_dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
-                   "causal": w.causal, "window": w.window, "in": w.in_dtype, "out": w.out_dtype,
+                   "causal": w.causal, "window": w.window, "window_left": w.window_left,
+                   "window_right": w.window_right, "in": w.in_dtype, "out": w.out_dtype,
                    "parallelism": "single GPU"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",

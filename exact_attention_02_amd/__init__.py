@@ -24,7 +24,8 @@ FA_F16, FA_BF16, FA_F16_F32OUT, FA_E4M3, FA_BF16_F32OUT = 1, 2, 3, 4, 5
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE = 0, 1, 2, 3, 4
 FA_ERR_MASK, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_DEVICE, FA_ERR_LAUNCH = 5, 6, 7, 8, 9
 
-EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class")
+EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_status_str", "fa_plan_grid", "fa_plan_tile",
+           "fa_plan_block_class", "fa_plan_window_range", "fa_plan_block_class_window")
 
 _lib = None
 
@@ -49,6 +50,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd.restype = I
     lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, F, F, F]
     lib.fa_fwd_fp8.restype = I
+    lib.fa_fwd_window.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, F, F, F]
+    lib.fa_fwd_window.restype = I
     lib.fa_status_str.argtypes = [I]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_plan_grid.argtypes = [I, I, I, I, I, I, I, I, pLL, pI, pI, pI]
@@ -57,6 +60,10 @@ def load(path: str = LIB_PATH):
     lib.fa_plan_tile.restype = I
     lib.fa_plan_block_class.argtypes = [I, I, I, I, I, I, I, I]
     lib.fa_plan_block_class.restype = I
+    lib.fa_plan_window_range.argtypes = [I, I, I, I, I, I, pI, pI]
+    lib.fa_plan_window_range.restype = I
+    lib.fa_plan_block_class_window.argtypes = [I, I, I, I, I, I, I, I]
+    lib.fa_plan_block_class_window.restype = I
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -71,6 +78,12 @@ def fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, dtype, s
                descale_q, descale_k, descale_v) -> int:
     return load().fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(causal), int(window), dtype, stream,
                              descale_q, descale_k, descale_v)
+
+
+def fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_right, dtype, stream,
+                  descale_q=1.0, descale_k=1.0, descale_v=1.0) -> int:
+    return load().fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(window_left), int(window_right), dtype,
+                                stream, descale_q, descale_k, descale_v)
 
 
 def fa_status_str(status: int) -> str:
@@ -102,6 +115,19 @@ def plan_block_class(w0, w1, c0, c1, Nq, Nk, causal, window) -> int:
     return load().fa_plan_block_class(w0, w1, c0, c1, Nq, Nk, int(causal), int(window))
 
 
+def plan_window_range(r0, r1, Nq, Nk, window_left, window_right):
+    """Keys [lo, hi) visible to at least one row of [r0, r1) under fa_fwd_window's mask."""
+    lo, hi = ctypes.c_int(), ctypes.c_int()
+    st = load().fa_plan_window_range(r0, r1, Nq, Nk, window_left, window_right, ctypes.byref(lo), ctypes.byref(hi))
+    if st != FA_OK:
+        raise FaError(st, "fa_plan_window_range")
+    return lo.value, hi.value
+
+
+def plan_block_class_window(w0, w1, c0, c1, Nq, Nk, window_left, window_right) -> int:
+    return load().fa_plan_block_class_window(w0, w1, c0, c1, Nq, Nk, window_left, window_right)
+
+
 def dtype_code(in_dtype, out_dtype) -> int:
     import torch
     table = {
@@ -117,12 +143,16 @@ def dtype_code(in_dtype, out_dtype) -> int:
 
 
 def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, out_dtype=None,
-              descales=None, stream=None):
+              descales=None, stream=None, window_left=None, window_right=None):
     """O [B,H,Nq,D] and LSE [B,H,Nq] (float32) of softmax(scale Q K^T) V via libfa.
 
     q [B,H,Nq,D], k and v [B,H,Nk,D]: contiguous device tensors of one dtype
     (float16, bfloat16 or float8_e4m3fn). out_dtype defaults to the input dtype
     (bfloat16 for e4m3). descales = (dq, dk, dv) for e4m3 inputs.
+    The mask is (causal, window) as in fa_fwd, or, when window_left or
+    window_right is given, the key interval [i' - window_left, i' + window_right]
+    of fa_fwd_window (None or -1: that side unbounded; causal and window are then
+    ignored).
     """
     import torch
     B, H, Nq, D = q.shape
@@ -145,8 +175,16 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            B, H, Nq, Nk, D, float(scale), int(bool(causal)), int(window), code, stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    if window_left is not None or window_right is not None:
+        wl = -1 if window_left is None else int(window_left)
+        wr = -1 if window_right is None else int(window_right)
+        ds = [float(x) for x in descales] if (code == FA_E4M3 and descales is not None) else [1.0, 1.0, 1.0]
+        st = fa_fwd_window(*ptrs, B, H, Nq, Nk, D, float(scale), wl, wr, code, stream, *ds)
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_window")
+        return out, lse
+    args = (*ptrs, B, H, Nq, Nk, D, float(scale), int(bool(causal)), int(window), code, stream)
     if code == FA_E4M3 and descales is not None:
         st = fa_fwd_fp8(*args, *[float(x) for x in descales])
         where = "fa_fwd_fp8"

@@ -36,12 +36,10 @@ bool dtype_info(int dtype, DtypeInfo* di) {
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.f; }
 
 // Argument checks shared by the entry points and the plan introspection.
-int check_shape(int B, int H, int Nq, int Nk, int D, int causal, int window, int dtype, DtypeInfo* di) {
-    (void)causal;
+int check_shape(int B, int H, int Nq, int Nk, int D, int dtype, DtypeInfo* di) {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
     if (D != 64 && D != 128) return FA_ERR_HEADDIM;
     if (!dtype_info(dtype, di)) return FA_ERR_DTYPE;
-    if (window < 0 || (window > 0 && !causal)) return FA_ERR_MASK;
     // element counts must fit 63 bits; the grid must fit 2^31 - 1 workgroups
     const long long bh = (long long)B * H;
     if (bh > (1LL << 31)) return FA_ERR_SHAPE;
@@ -74,10 +72,22 @@ int check_device() {
     return ok ? FA_OK : FA_ERR_DEVICE;
 }
 
+// fa_fwd's mask arguments: window >= 0, and a window needs causal.
+bool causal_window_ok(int causal, int window) { return window >= 0 && (window == 0 || causal); }
+
+// The interval extents of fa_fwd_window (-1: unbounded), clamped to Nq + Nk.
+bool window_extents(int window_left, int window_right, int Nq, int Nk, int* wl, int* wr) {
+    if (window_left < -1 || window_right < -1) return false;
+    const int big = Nq + Nk;
+    *wl = (window_left < 0 || window_left > big) ? big : window_left;
+    *wr = (window_right < 0 || window_right > big) ? big : window_right;
+    return true;
+}
+
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
-        float scale, int causal, int window, int dtype, void* stream, float dq, float dk, float dv) {
+        float scale, int wl, int wr, int dtype, void* stream, float dq, float dk, float dv) {
     DtypeInfo di;
-    const int st = check_shape(B, H, Nq, Nk, D, causal, window, dtype, &di);
+    const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
     if (st != FA_OK) return st;
     if (!finite_positive(scale) || !finite_positive(dq) || !finite_positive(dk) || !finite_positive(dv))
         return FA_ERR_SCALE;
@@ -99,9 +109,8 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.lse = lse;
     p.Nq = Nq;
     p.Nk = Nk;
-    p.causal = causal ? 1 : 0;
-    // a window of Nk or more keys removes nothing beyond the causal mask
-    p.window = (window >= Nk) ? 0 : window;
+    p.wl = wl;
+    p.wr = wr;
     p.n_bh = B * H;
     p.n_qt = pl.n_qt;
     p.c = scale * dq * dk * 1.44269504088896341f;
@@ -120,15 +129,40 @@ extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
            float scale, int causal, int window, int dtype, void* stream) {
-    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, dtype, stream, 1.f, 1.f, 1.f);
+    if (!causal_window_ok(causal, window)) {
+        DtypeInfo di;
+        const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
+        return st != FA_OK ? st : FA_ERR_MASK;
+    }
+    int wl, wr;
+    fa::mask_extents(causal, window, Nq, Nk, &wl, &wr);
+    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, 1.f, 1.f, 1.f);
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
                int D, float scale, int causal, int window, int dtype, void* stream, float descale_q,
                float descale_k, float descale_v) {
     if (dtype != FA_E4M3) return FA_ERR_DTYPE;
-    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, dtype, stream, descale_q, descale_k,
-               descale_v);
+    if (!causal_window_ok(causal, window)) {
+        DtypeInfo di;
+        const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
+        return st != FA_OK ? st : FA_ERR_MASK;
+    }
+    int wl, wr;
+    fa::mask_extents(causal, window, Nq, Nk, &wl, &wr);
+    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, descale_q, descale_k, descale_v);
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int D, float scale, int window_left, int window_right, int dtype, void* stream, float descale_q,
+                  float descale_k, float descale_v) {
+    DtypeInfo di;
+    const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
+    if (st != FA_OK) return st;
+    int wl, wr;
+    if (!window_extents(window_left, window_right, Nq, Nk, &wl, &wr)) return FA_ERR_MASK;
+    if (dtype != FA_E4M3 && (descale_q != 1.f || descale_k != 1.f || descale_v != 1.f)) return FA_ERR_SCALE;
+    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, descale_q, descale_k, descale_v);
 }
 
 const char* fa_status_str(int status) {
@@ -138,7 +172,7 @@ const char* fa_status_str(int status) {
         case FA_ERR_SHAPE: return "invalid or too large sizes";
         case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
         case FA_ERR_DTYPE: return "unsupported dtype";
-        case FA_ERR_MASK: return "window must be >= 0 and needs causal";
+        case FA_ERR_MASK: return "window must be >= 0 and needs causal; window extents must be >= -1";
         case FA_ERR_SCALE: return "scale and descales must be finite and positive";
         case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
         case FA_ERR_DEVICE: return "no gfx950 HIP device is current";
@@ -150,8 +184,9 @@ const char* fa_status_str(int status) {
 int fa_plan_grid(int B, int H, int Nq, int Nk, int D, int causal, int window, int dtype, long long* n_wg, int* br,
                  int* qw, int* bc) {
     DtypeInfo di;
-    const int st = check_shape(B, H, Nq, Nk, D, causal, window, dtype, &di);
+    const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
     if (st != FA_OK) return st;
+    if (!causal_window_ok(causal, window)) return FA_ERR_MASK;
     if (!n_wg || !br || !qw || !bc) return FA_ERR_NULL;
     const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq);
     *n_wg = pl.n_wg;
@@ -164,20 +199,41 @@ int fa_plan_grid(int B, int H, int Nq, int Nk, int D, int causal, int window, in
 int fa_plan_tile(int B, int H, int Nq, int Nk, int D, int causal, int window, int dtype, long long wg, int* bh,
                  int* qtile, int* kv_lo, int* kv_hi) {
     DtypeInfo di;
-    const int st = check_shape(B, H, Nq, Nk, D, causal, window, dtype, &di);
+    const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
     if (st != FA_OK) return st;
+    if (!causal_window_ok(causal, window)) return FA_ERR_MASK;
     if (!bh || !qtile || !kv_lo || !kv_hi) return FA_ERR_NULL;
     const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq);
     if (wg < 0 || wg >= pl.n_wg) return FA_ERR_SHAPE;
     fa::decode_wg(wg, B * H, pl.n_qt, bh, qtile);
     const int r0 = *qtile * pl.br;
     const int r1 = (r0 + pl.br < Nq) ? r0 + pl.br : Nq;
-    fa::kv_range(r0, r1, Nq, Nk, causal ? 1 : 0, window, kv_lo, kv_hi);
+    int wl, wr;
+    fa::mask_extents(causal, window, Nq, Nk, &wl, &wr);
+    fa::kv_range(r0, r1, Nq, Nk, wl, wr, kv_lo, kv_hi);
     return FA_OK;
 }
 
 int fa_plan_block_class(int w0, int w1, int c0, int c1, int Nq, int Nk, int causal, int window) {
-    return fa::tile_class(w0, w1, c0, c1, Nq, Nk, causal ? 1 : 0, window);
+    int wl, wr;
+    fa::mask_extents(causal, window, Nq, Nk, &wl, &wr);
+    return fa::tile_class(w0, w1, c0, c1, Nq, Nk, wl, wr);
+}
+
+int fa_plan_window_range(int r0, int r1, int Nq, int Nk, int window_left, int window_right, int* kv_lo,
+                         int* kv_hi) {
+    int wl, wr;
+    if (!window_extents(window_left, window_right, Nq, Nk, &wl, &wr)) return FA_ERR_MASK;
+    if (r0 < 0 || r1 <= r0 || r1 > Nq || Nk < 0) return FA_ERR_SHAPE;
+    if (!kv_lo || !kv_hi) return FA_ERR_NULL;
+    fa::kv_range(r0, r1, Nq, Nk, wl, wr, kv_lo, kv_hi);
+    return FA_OK;
+}
+
+int fa_plan_block_class_window(int w0, int w1, int c0, int c1, int Nq, int Nk, int window_left, int window_right) {
+    int wl, wr;
+    if (!window_extents(window_left, window_right, Nq, Nk, &wl, &wr)) return -1;
+    return fa::tile_class(w0, w1, c0, c1, Nq, Nk, wl, wr);
 }
 
 }  // extern "C"

@@ -84,13 +84,13 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
-    const int Nq = p.Nq, Nk = p.Nk, causal = p.causal, window = p.window;
+    const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
     int bh, qt;
     decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, &bh, &qt);
     const int r0 = qt * BR;
     const int r1 = min(r0 + BR, Nq);
     int kv_lo, kv_hi;
-    kv_range(r0, r1, Nq, Nk, causal, window, &kv_lo, &kv_hi);
+    kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
     const int t_lo = kv_lo / BC;
     const int t_hi = (kv_hi > kv_lo) ? (kv_hi + BC - 1) / BC : t_lo;
 
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
         const int i = w0 + 32 * qb + l32;
         klo[qb] = 0;
         khi[qb] = 0;
-        if (i < w1) kv_range(i, i + 1, Nq, Nk, causal, window, &klo[qb], &khi[qb]);
+        if (i < w1) kv_range(i, i + 1, Nq, Nk, wl, wr, &klo[qb], &khi[qb]);
     }
 
     // ---- Q fragments, B operand of S^T = K Q^T: lane holds query
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
         if (more) issue_tile(t + 1, (t + 1) & 1);
 
         const int c0 = t * BC;
-        const int cls = tile_class(w0, w1, c0, c0 + BC, Nq, Nk, causal, window);
+        const int cls = tile_class(w0, w1, c0, c0 + BC, Nq, Nk, wl, wr);
         if (cls != TILE_SKIP) {
             const lds_u8* kbuf = (const lds_u8*)(smem + (t & 1) * STAGE);
             const lds_u8* vbuf = kbuf + KTILE;

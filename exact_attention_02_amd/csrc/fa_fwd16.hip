@@ -122,13 +122,13 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
     const int hh = lane >> 5;
     const int g = lane >> 4, cl = lane & 15;   // 16-lane group of the transposing reads
 
-    const int Nq = p.Nq, Nk = p.Nk, causal = p.causal, window = p.window;
+    const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
     int bh, qt;
     decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, &bh, &qt);
     const int r0 = qt * BR;
     const int r1 = min(r0 + BR, Nq);
     int kv_lo, kv_hi;
-    kv_range(r0, r1, Nq, Nk, causal, window, &kv_lo, &kv_hi);
+    kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
     const int t_lo = kv_lo / BC;
     const int t_hi = (kv_hi > kv_lo) ? (kv_hi + BC - 1) / BC : t_lo;
     const int w0 = r0 + wave * QW;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int a0 = w0 + 32 * qb;
-        block_ranges32(a0, min(a0 + 32, w1), Nq, Nk, causal, window, &jf0[qb], &jf1[qb], &ju0[qb], &ju1[qb]);
+        block_ranges32(a0, min(a0 + 32, w1), Nq, Nk, wl, wr, &jf0[qb], &jf1[qb], &ju0[qb], &ju1[qb]);
     }
     auto block_skip = [&](int j, int qb) { return (unsigned)(j - ju0[qb]) >= (unsigned)(ju1[qb] - ju0[qb]); };
     auto block_full = [&](int j, int qb) { return (unsigned)(j - jf0[qb]) < (unsigned)(jf1[qb] - jf0[qb]); };
@@ -258,8 +258,8 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
         asm volatile("" : "+v"(ln));   // recomputed here, not held across the loop
         const int i = w0 + 32 * qb + (ln & 31);
         const int ip = i + (Nk - Nq);
-        int klo = (window > 0) ? ip - window + 1 : 0;
-        int khi = causal ? ip + 1 : Nk;
+        int klo = ip - wl;
+        int khi = ip + wr + 1;
         klo = klo > 0 ? klo : 0;
         khi = khi < Nk ? khi : Nk;
         if (i >= w1) khi = klo;   // past the last query row: nothing visible

@@ -21,7 +21,7 @@ struct Params {
     uint8_t* o;
     float* lse;
     int Nq, Nk;
-    int causal, window;
+    int wl, wr;     // row i sees keys [i' - wl, i' + wr], i' = i + Nk - Nq (clamped to Nq + Nk)
     int n_bh;       // B * H
     int n_qt;       // query tiles per head
     float c;        // scale * descale_q * descale_k * log2(e): scores in base-2 units

@@ -21,29 +21,27 @@
 
 namespace fa {
 
-// Visibility of key j to query row i, with delta = Nk - Nq (bottom-right
-// causal alignment): j < Nk, and j <= i + delta if causal, and
-// j > i + delta - window if window > 0.
-FA_HD bool visible(long long i, long long j, int Nq, int Nk, int causal, int window) {
+// The mask as one key interval per query row. With delta = Nk - Nq
+// (bottom-right alignment) and i' = i + delta, row i sees the keys
+//   max(0, i' - wl) <= j <= min(Nk - 1, i' + wr).
+// Causal is wr = 0; the causal window of w keys is (wl, wr) = (w - 1, 0); the
+// symmetric window |i - j| <= w is (w, w); no mask is wl = wr >= Nq + Nk.
+// The entry points clamp wl and wr to Nq + Nk, so every sum below stays far
+// inside 32 bits.
+FA_HD bool visible(long long i, long long j, int Nq, int Nk, int wl, int wr) {
     const long long ip = i + (long long)Nk - Nq;
     if (j < 0 || j >= Nk) return false;
-    if (causal && j > ip) return false;
-    if (window > 0 && j <= ip - window) return false;
-    return true;
+    return j >= ip - wl && j <= ip + wr;
 }
 
 // Keys [lo, hi) visible to at least one row of [r0, r1) (r1 exclusive, r1 > r0).
-FA_HD void kv_range(int r0, int r1, int Nq, int Nk, int causal, int window, int* lo, int* hi) {
+// Both interval ends grow with the row, so the union runs from row r0's start
+// to row r1-1's end.
+FA_HD void kv_range(int r0, int r1, int Nq, int Nk, int wl, int wr, int* lo, int* hi) {
     const long long d = (long long)Nk - Nq;
-    long long l = 0, h = Nk;
-    if (causal) {
-        const long long c = (long long)(r1 - 1) + d + 1;
-        h = c < Nk ? c : Nk;
-    }
-    if (window > 0) {
-        const long long c = (long long)r0 + d - window + 1;
-        l = c > 0 ? c : 0;
-    }
+    long long l = (long long)r0 + d - wl, h = (long long)(r1 - 1) + d + wr + 1;
+    if (l < 0) l = 0;
+    if (h > Nk) h = Nk;
     if (h < 0) h = 0;
     if (l > h) l = h;
     *lo = (int)l;
@@ -56,47 +54,35 @@ FA_HD void kv_range(int r0, int r1, int Nq, int Nk, int causal, int window, int*
 //   2: mixed (the element-wise predicate is applied).
 enum { TILE_SKIP = 0, TILE_FULL = 1, TILE_EDGE = 2 };
 
-FA_HD int tile_class(int w0, int w1, int c0, int c1, int Nq, int Nk, int causal, int window) {
+FA_HD int tile_class(int w0, int w1, int c0, int c1, int Nq, int Nk, int wl, int wr) {
     if (w1 <= w0 || c1 <= c0) return TILE_SKIP;
     const long long d = (long long)Nk - Nq;
-    // union over the rows of the visible key interval
-    long long ulo = 0, uhi = Nk;  // [ulo, uhi)
-    if (causal) {
-        const long long c = (long long)(w1 - 1) + d + 1;
-        if (c < uhi) uhi = c;
-    }
-    if (window > 0) {
-        const long long c = (long long)w0 + d - window + 1;
-        if (c > ulo) ulo = c;
-    }
-    if ((long long)c1 <= ulo || (long long)c0 >= uhi) return TILE_SKIP;
-    // intersection over the rows
-    long long ilo = 0, ihi = Nk;
-    if (causal) {
-        const long long c = (long long)w0 + d + 1;
-        if (c < ihi) ihi = c;
-    }
-    if (window > 0) {
-        const long long c = (long long)(w1 - 1) + d - window + 1;
-        if (c > ilo) ilo = c;
-    }
+    // union over the rows of the visible key interval, [ulo, uhi)
+    long long ulo = (long long)w0 + d - wl, uhi = (long long)(w1 - 1) + d + wr + 1;
+    if (ulo < 0) ulo = 0;
+    if (uhi > Nk) uhi = Nk;
+    if ((long long)c1 <= ulo || (long long)c0 >= uhi || uhi <= ulo) return TILE_SKIP;
+    // intersection over the rows, [ilo, ihi)
+    long long ilo = (long long)(w1 - 1) + d - wl, ihi = (long long)w0 + d + wr + 1;
+    if (ilo < 0) ilo = 0;
+    if (ihi > Nk) ihi = Nk;
     if ((long long)c0 >= ilo && (long long)c1 <= ihi) return TILE_FULL;
     return TILE_EDGE;
 }
 
-// tile_class in 32-bit arithmetic, for the kernels: exact whenever Nq, Nk
-// and window are below 2^30 (the entry points keep every tensor below 2^31
-// bytes for the buffer descriptors, and pass window < Nk).
-FA_HD int tile_class32(int w0, int w1, int c0, int c1, int Nq, int Nk, int causal, int window) {
+// tile_class in 32-bit arithmetic, for the kernels: exact whenever Nq and Nk
+// are below 2^28 and wl, wr <= Nq + Nk (the entry points keep every tensor
+// below 2^31 bytes for the buffer descriptors and clamp wl and wr).
+FA_HD int tile_class32(int w0, int w1, int c0, int c1, int Nq, int Nk, int wl, int wr) {
     if (w1 <= w0 || c1 <= c0) return TILE_SKIP;
     const int d = Nk - Nq;
-    int ulo = 0, uhi = Nk;
-    if (causal && w1 + d < uhi) uhi = w1 + d;
-    if (window > 0 && w0 + d - window + 1 > ulo) ulo = w0 + d - window + 1;
-    if (c1 <= ulo || c0 >= uhi) return TILE_SKIP;
-    int ilo = 0, ihi = Nk;
-    if (causal && w0 + d + 1 < ihi) ihi = w0 + d + 1;
-    if (window > 0 && w1 + d - window > ilo) ilo = w1 + d - window;
+    int ulo = w0 + d - wl, uhi = w1 - 1 + d + wr + 1;
+    if (ulo < 0) ulo = 0;
+    if (uhi > Nk) uhi = Nk;
+    if (c1 <= ulo || c0 >= uhi || uhi <= ulo) return TILE_SKIP;
+    int ilo = w1 - 1 + d - wl, ihi = w0 + d + wr + 1;
+    if (ilo < 0) ilo = 0;
+    if (ihi > Nk) ihi = Nk;
     if (c0 >= ilo && c1 <= ihi) return TILE_FULL;
     return TILE_EDGE;
 }
@@ -105,18 +91,14 @@ FA_HD int tile_class32(int w0, int w1, int c0, int c1, int Nq, int Nk, int causa
 // two ranges of j: every pair visible for j in [*jf0, *jf1), at least one for
 // j in [*ju0, *ju1) (outside it the block is skipped). 32-bit arithmetic, under
 // the same limits as tile_class32.
-FA_HD void block_ranges32(int a0, int a1, int Nq, int Nk, int causal, int window, int* jf0, int* jf1, int* ju0,
-                          int* ju1) {
+FA_HD void block_ranges32(int a0, int a1, int Nq, int Nk, int wl, int wr, int* jf0, int* jf1, int* ju0, int* ju1) {
     const int d = Nk - Nq;
-    int ulo = 0, uhi = Nk, ilo = 0, ihi = Nk;   // union and intersection of the rows' key ranges
-    if (causal) {
-        if (a1 + d < uhi) uhi = a1 + d;
-        if (a0 + d + 1 < ihi) ihi = a0 + d + 1;
-    }
-    if (window > 0) {
-        if (a0 + d - window + 1 > ulo) ulo = a0 + d - window + 1;
-        if (a1 + d - window > ilo) ilo = a1 + d - window;
-    }
+    // union and intersection of the rows' key ranges
+    int ulo = a0 + d - wl, uhi = a1 - 1 + d + wr + 1, ilo = a1 - 1 + d - wl, ihi = a0 + d + wr + 1;
+    if (ulo < 0) ulo = 0;
+    if (uhi > Nk) uhi = Nk;
+    if (ilo < 0) ilo = 0;
+    if (ihi > Nk) ihi = Nk;
     if (a1 <= a0 || uhi <= ulo) {
         *jf0 = *jf1 = *ju0 = *ju1 = 0;
         return;
@@ -126,6 +108,14 @@ FA_HD void block_ranges32(int a0, int a1, int Nq, int Nk, int causal, int window
     *jf0 = (ilo + 31) / 32;               // first j with 32j >= ilo
     *jf1 = (ihi > 0) ? ihi / 32 : 0;      // past the last j with 32j + 32 <= ihi
     if (*jf1 < *jf0) *jf1 = *jf0;
+}
+
+// (causal, window) of fa_fwd as the interval extents: causal is wr = 0, a
+// window of w > 0 keys is wl = w - 1; unbounded sides become Nq + Nk.
+FA_HD void mask_extents(int causal, int window, int Nq, int Nk, int* wl, int* wr) {
+    const int big = Nq + Nk;
+    *wr = causal ? 0 : big;
+    *wl = (window > 0 && window - 1 < big) ? window - 1 : big;
 }
 
 // Hardware workgroup id -> (batch*head, query tile).

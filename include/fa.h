@@ -26,6 +26,13 @@
  *     window  > 0 : additionally j > i + (Nk - Nq) - window, i.e. the `window`
  *                   most recent keys including the diagonal. Needs causal.
  *     window == 0 : no window.
+ * fa_fwd_window takes the mask as one key interval per row instead: row i
+ * sees the keys j with
+ *     i' - window_left <= j <= i' + window_right,   i' = i + (Nk - Nq),
+ * where -1 leaves that side unbounded. (-1, 0) is the causal mask, (w-1, 0)
+ * the causal window above, (w, w) the sliding window |i - j| <= w of module
+ * 9's sparse-attention-patterns section (w keys on each side of the token),
+ * and (-1, -1) no mask.
  * A row that sees no key gets O = 0 and LSE = -inf.
  *
  * Streams: work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
@@ -60,7 +67,8 @@ enum {
                              max(Nq, Nk) * D * 4 >= 2^31 (one head's rows) */
     FA_ERR_HEADDIM = 3,   /* D is not 64 or 128 */
     FA_ERR_DTYPE = 4,     /* unknown dtype, or fa_fwd_fp8 with a non-e4m3 dtype */
-    FA_ERR_MASK = 5,      /* window < 0, or window > 0 without causal */
+    FA_ERR_MASK = 5,      /* window < 0, or window > 0 without causal; or a
+                             window extent below -1 (fa_fwd_window) */
     FA_ERR_SCALE = 6,     /* scale or a descale is not finite and positive */
     FA_ERR_ALIGN = 7,     /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_DEVICE = 8,    /* no HIP device, or the current device is not gfx950 */
@@ -99,6 +107,19 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int causal, int window, int dtype, void* stream,
                float descale_q, float descale_k, float descale_v);
 
+/*
+ * fa_fwd_window: as fa_fwd, with the mask given as the key interval
+ * [i' - window_left, i' + window_right] of each row (see the header comment;
+ * -1 leaves a side unbounded, larger extents than Nq + Nk act as unbounded).
+ * descale_q, descale_k, descale_v apply to FA_E4M3 inputs as in fa_fwd_fp8 and
+ * must be 1 for the other dtypes (FA_ERR_SCALE otherwise). Errors as fa_fwd;
+ * an extent below -1 is FA_ERR_MASK.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int D, float scale,
+                  int window_left, int window_right, int dtype, void* stream,
+                  float descale_q, float descale_k, float descale_v);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_str(int status);
 
@@ -127,6 +148,23 @@ int fa_plan_tile(int B, int H, int Nq, int Nk, int D, int causal, int window, in
  *   without a mask (every pair visible), 2 computed with the mask.
  */
 int fa_plan_block_class(int w0, int w1, int c0, int c1, int Nq, int Nk, int causal, int window);
+
+/*
+ * fa_plan_window_range: the keys [*kv_lo, *kv_hi) visible to at least one row
+ * of [r0, r1) under fa_fwd_window's mask -- the key range a workgroup owning
+ * those rows visits. Returns FA_OK, FA_ERR_MASK for an extent below -1,
+ * FA_ERR_SHAPE unless 0 <= r0 < r1 <= Nq and Nk >= 0, FA_ERR_NULL for a NULL
+ * output pointer.
+ */
+int fa_plan_window_range(int r0, int r1, int Nq, int Nk, int window_left, int window_right,
+                         int* kv_lo, int* kv_hi);
+
+/*
+ * fa_plan_block_class_window: as fa_plan_block_class under fa_fwd_window's
+ * mask; -1 for an extent below -1.
+ */
+int fa_plan_block_class_window(int w0, int w1, int c0, int c1, int Nq, int Nk,
+                               int window_left, int window_right);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ torch's conversion; e4m3 inputs follow the per-tensor recipe in
 from __future__ import annotations
 
 import math
+from typing import Optional
 from dataclasses import dataclass, field
 
 import torch
@@ -150,6 +151,10 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_mult: float = 1.0
     scale: float = field(default=0.0)
+    # The mask as key extents instead of (causal, window): row i keeps keys
+    # [i' - window_left, i' + window_right], i' = i + Nk - Nq, -1 an open side.
+    window_left: Optional[int] = None
+    window_right: Optional[int] = None
 
     def __post_init__(self):
         if self.scale == 0.0:
@@ -171,6 +176,10 @@ WORKLOADS = {
     "c4w": Workload("c4_window4096_B1H32N32768D128_bf16", 1, 32, 32768, 32768, 128, True, 4096, "bf16", "bf16", 4),
     "c5": Workload("c5_noncausal_B4H16N8192D128_e4m3", 4, 16, 8192, 8192, 128, False, 0, "e4m3", "bf16", 5,
                    outlier_frac=0.001, outlier_mult=20.0),
+    # The sliding window |i - j| <= w of the sparse-attention-patterns section
+    # at c3's shape, w = 1024 (the page's example uses w = n / 8).
+    "c3sw": Workload("c3_slidingwindow1024_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, False, 0, "bf16", "bf16", 3,
+                     window_left=1024, window_right=1024),
 }
 
 
@@ -209,7 +218,8 @@ def make_inputs(w: Workload) -> Inputs:
 
 
 def small_workload(name, B, H, Nq, Nk, D, causal, window, in_dtype, out_dtype, seed,
-                   outlier_frac=0.0, outlier_mult=1.0) -> Workload:
+                   outlier_frac=0.0, outlier_mult=1.0, window_left=None, window_right=None) -> Workload:
     """A workload of the same recipe at other sizes (parity and edge cases)."""
     return Workload(name, B, H, Nq, Nk, D, causal, window, in_dtype, out_dtype, seed,
-                    outlier_frac=outlier_frac, outlier_mult=outlier_mult)
+                    outlier_frac=outlier_frac, outlier_mult=outlier_mult,
+                    window_left=window_left, window_right=window_right)

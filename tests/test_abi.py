@@ -76,6 +76,17 @@ def test_fp8_entry_checks_dtype_and_descales():
     assert fa.fa_fwd_fp8(*args, fa.FA_E4M3, None, 1.0, float("nan"), 1.0) == fa.FA_ERR_SCALE
 
 
+def test_window_entry_checks_extents_and_descales():
+    args = (P, P, P, P, P, 1, 1, 64, 64, 64, 0.125)
+    assert fa.fa_fwd_window(*args, -2, 0, fa.FA_BF16, None) == fa.FA_ERR_MASK
+    assert fa.fa_fwd_window(*args, 0, -5, fa.FA_BF16, None) == fa.FA_ERR_MASK
+    assert fa.fa_fwd_window(*args, 4, 4, fa.FA_BF16, None, 2.0, 1.0, 1.0) == fa.FA_ERR_SCALE
+    assert fa.fa_fwd_window(*args, 4, 4, fa.FA_E4M3, None, 0.0, 1.0, 1.0) == fa.FA_ERR_SCALE
+    assert fa.fa_fwd_window(P, P, P, P, P, 1, 1, 64, 64, 96, 0.125, -2, 0, fa.FA_BF16, None) == fa.FA_ERR_HEADDIM
+    assert fa.fa_fwd_window(P, P, P, P, P, 0, 1, 64, 64, 64, 0.125, 4, 4, fa.FA_BF16, None) == fa.FA_OK
+    assert fa.fa_fwd_window(0, P, P, P, P, 1, 1, 64, 64, 64, 0.125, 4, 4, fa.FA_BF16, None) == fa.FA_ERR_NULL
+
+
 def test_empty_problems_need_no_device():
     assert call(B=0) == fa.FA_OK
     assert call(H=0, q=0, k=0, v=0, o=0, lse=0) == fa.FA_OK

@@ -36,14 +36,19 @@ def run_gpu(w: synth.Workload, inp: synth.Inputs, q=None, k=None, v=None):
     v = inp.v.to(DEV) if v is None else v
     descales = (inp.descale_q, inp.descale_k, inp.descale_v) if w.in_dtype == "e4m3" else None
     o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window,
-                          out_dtype=OUT_T[w.out_dtype], descales=descales)
+                          out_dtype=OUT_T[w.out_dtype], descales=descales,
+                          window_left=w.window_left, window_right=w.window_right)
     torch.cuda.synchronize()
     return o, lse
 
 
 def reference(w, inp, rows=None):
+    ext = {}
+    if w.window_left is not None or w.window_right is not None:
+        ext = dict(window_left=-1 if w.window_left is None else w.window_left,
+                   window_right=-1 if w.window_right is None else w.window_right)
     return oracle.attention(inp.q, inp.k, inp.v, w.scale, w.causal, w.window,
-                            descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows)
+                            descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows, **ext)
 
 
 def compare(w, O, L, Oref, Lref, label=""):
@@ -108,7 +113,7 @@ def test_workload_full(name):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-@pytest.mark.parametrize("name", ["c3", "c4c", "c4w", "c5"])
+@pytest.mark.parametrize("name", ["c3", "c4c", "c4w", "c5", "c3sw"])
 def test_workload_full_size_sampled_rows(name):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w)
@@ -182,6 +187,75 @@ def test_tile64_kernel_on_16bit_inputs(monkeypatch, B, H, Nq, Nk, causal, window
     o, lse = run_gpu(w, inp)
     Oref, Lref = reference(w, inp)
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+# --------------------------------------- masks given as key extents
+
+EXTENTS = [(1, 1), (16, 16), (100, 100), (0, 0), (5, 40), (40, 5), (-1, 37), (63, -1), (129, 0), (-1, -1)]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 2, 300, 300), (1, 2, 200, 333), (1, 2, 333, 200), (2, 1, 513, 513)])
+@pytest.mark.parametrize("wl,wr", EXTENTS)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("f16", "f32"), ("e4m3", "bf16")])
+def test_window_extents_small_shapes(B, H, Nq, Nk, wl, wr, D, din, dout):
+    seed = 4000 + B * 7 + H * 13 + Nq * 3 + Nk + D + 5 * wl + 11 * wr
+    w = synth.small_workload(f"ext_B{B}H{H}q{Nq}k{Nk}D{D}l{wl}r{wr}_{din}_{dout}", B, H, Nq, Nk, D, False, 0,
+                             din, dout, seed, outlier_frac=0.001 if din == "e4m3" else 0.0, outlier_mult=20.0,
+                             window_left=wl, window_right=wr)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("wl,wr", [(16, 16), (5, 40), (-1, 37), (100, 100)])
+@pytest.mark.parametrize("D,qb,kernel", [(64, "2", "1"), (64, "1", "0"), (64, "2", "0"), (128, "1", "0")])
+def test_window_extents_other_tile_shapes(monkeypatch, wl, wr, D, qb, kernel):
+    monkeypatch.setenv("FA_TILE_QB", qb)
+    monkeypatch.setenv("FA_KERNEL", kernel)
+    w = synth.small_workload(f"ext_qb{qb}_k{kernel}_D{D}_l{wl}r{wr}", 1, 2, 457, 457, D, False, 0, "bf16", "bf16",
+                             4500 + D + wl + 3 * wr, window_left=wl, window_right=wr)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("din,D", [("bf16", 64), ("f16", 128), ("e4m3", 128)])
+def test_sliding_window_masked_keys_are_reproduced_exactly(din, D):
+    # |i - j| <= win: rows i in [t + win, u - win) see neither keys j < t nor keys j >= u.
+    N, t, u, win = 600, 70, 530, 64
+    dout = "bf16" if din != "f16" else "f16"
+    w = synth.small_workload("sliding_exact", 1, 2, N, N, D, False, 0, din, dout, 68,
+                             window_left=win, window_right=win)
+    inp = synth.make_inputs(w)
+    o1, l1 = run_gpu(w, inp)
+    k2, v2 = inp.k.clone(), inp.v.clone()
+    for a, b in [(0, t), (u, N)]:
+        big = (torch.randn(1, 2, b - a, D) * 100)
+        big = big.clamp(-448, 448).to(k2.dtype) if din == "e4m3" else big.to(k2.dtype)
+        k2[:, :, a:b] = big
+        v2[:, :, a:b] = big
+    o2, l2 = run_gpu(w, inp, k=k2.to(DEV), v=v2.to(DEV))
+    r0, r1 = t + win, u - win
+    assert torch.equal(o1[:, :, r0:r1].cpu().view(torch.uint8), o2[:, :, r0:r1].cpu().view(torch.uint8))
+    assert torch.equal(l1[:, :, r0:r1].cpu(), l2[:, :, r0:r1].cpu())
+    assert not torch.equal(l1[:, :, :r0].cpu(), l2[:, :, :r0].cpu())
+
+
+def test_sliding_window_zero_queries_average_the_window():
+    N, D, win = 300, 64, 20
+    q = torch.zeros(1, 2, N, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(1, 2, N, D, device=DEV).to(torch.bfloat16)
+    vb = torch.randn(1, 2, N, D).to(torch.bfloat16)
+    o, lse = fa.attention(q, k, vb.to(DEV), window_left=win, window_right=win)
+    torch.cuda.synchronize()
+    for i in (0, 1, 19, 20, 21, 150, 279, 280, 299):
+        lo, hi = max(0, i - win), min(N, i + win + 1)
+        mean = vb[:, :, lo:hi].double().mean(dim=2)
+        assert (o[:, :, i].double().cpu() - mean).abs().max().item() <= 1e-2
+        assert abs(lse[0, 0, i].item() - math.log(hi - lo)) <= 1e-4 * max(1.0, math.log(hi - lo))
 
 
 # ----------------------------------------------------------- edge cases

@@ -77,6 +77,64 @@ def test_block_class_is_exact(Nq, Nk, causal, window):
                 assert cls == 2 and any(pairs) and not all(pairs)
 
 
+def vis_window(i, j, Nq, Nk, wl, wr):
+    """fa_fwd_window's predicate: i' - wl <= j <= i' + wr, a side with extent -1 open."""
+    ip = i + Nk - Nq
+    return 0 <= j < Nk and (wl < 0 or j >= ip - wl) and (wr < 0 or j <= ip + wr)
+
+
+EXTENTS = [(-1, -1), (-1, 0), (0, 0), (1, 1), (5, 0), (0, 9), (16, 16), (40, 3), (-1, 7), (12, -1), (500, 500)]
+
+
+@pytest.mark.parametrize("Nq,Nk", [(64, 64), (130, 97), (97, 130), (300, 300), (1, 50)])
+@pytest.mark.parametrize("wl,wr", EXTENTS)
+def test_window_range_is_the_tight_union_of_visible_keys(Nq, Nk, wl, wr):
+    for r0 in range(0, Nq, 37):
+        for r1 in {min(Nq, r0 + 1), min(Nq, r0 + 32), min(Nq, r0 + 128), Nq}:
+            lo, hi = fa.plan_window_range(r0, r1, Nq, Nk, wl, wr)
+            cols = [j for j in range(Nk) if any(vis_window(i, j, Nq, Nk, wl, wr) for i in range(r0, r1))]
+            if cols:
+                assert (lo, hi) == (min(cols), max(cols) + 1)
+                assert hi - lo == len(cols)   # the visible keys of a row range are contiguous
+            else:
+                assert lo == hi
+
+
+@pytest.mark.parametrize("Nq,Nk", [(64, 64), (100, 37), (37, 100), (128, 200)])
+@pytest.mark.parametrize("wl,wr", EXTENTS)
+def test_block_class_window_is_exact(Nq, Nk, wl, wr):
+    for w0, c0 in itertools.product(range(0, Nq, 13), range(0, Nk + 20, 17)):
+        for w1, c1 in [(w0 + 1, c0 + 1), (min(w0 + 32, Nq), c0 + 64), (min(w0 + 64, Nq), c0 + 9)]:
+            if w1 <= w0:
+                continue
+            cls = fa.plan_block_class_window(w0, w1, c0, c1, Nq, Nk, wl, wr)
+            pairs = [vis_window(i, j, Nq, Nk, wl, wr) for i in range(w0, w1) for j in range(c0, c1)]
+            if cls == 0:
+                assert not any(pairs)
+            elif cls == 1:
+                assert all(pairs)
+            else:
+                assert cls == 2 and any(pairs) and not all(pairs)
+
+
+def test_window_extents_reproduce_fa_fwd_masks():
+    """(causal, window) and their extents give the same ranges and classes."""
+    for Nq, Nk in [(64, 64), (100, 37), (37, 100)]:
+        for causal, window in MODES:
+            wl = window - 1 if window > 0 else -1
+            wr = 0 if causal else -1
+            for w0, c0 in itertools.product(range(0, Nq, 9), range(0, Nk + 20, 11)):
+                w1, c1 = min(w0 + 32, Nq), c0 + 32
+                assert fa.plan_block_class(w0, w1, c0, c1, Nq, Nk, causal, window) == \
+                    fa.plan_block_class_window(w0, w1, c0, c1, Nq, Nk, wl, wr)
+
+
+def test_window_extent_below_minus_one_is_rejected():
+    assert fa.plan_block_class_window(0, 32, 0, 32, 64, 64, -2, 0) == -1
+    with pytest.raises(fa.FaError):
+        fa.plan_window_range(0, 32, 64, 64, 0, -2)
+
+
 def test_heads_stay_on_one_xcd_and_tiles_go_heavy_first():
     # 48 heads (B4 H12), 32 query tiles: workgroups with the same id mod 8
     # (the same XCD under round-robin dispatch) cover 6 whole heads, and
@@ -98,8 +156,9 @@ def test_heads_stay_on_one_xcd_and_tiles_go_heavy_first():
 def test_32bit_block_class_equals_64bit(tmp_path):
     """The kernels classify blocks in 32-bit arithmetic, one block at a time or
     as ranges of 32-key sub-tiles; both must agree with the 64-bit classifier
-    everywhere the entry points allow (sizes below 2^30, window < Nk),
-    including the extremes of that range."""
+    everywhere the entry points allow (sizes below 2^28, extents clamped to
+    Nq + Nk), for fa_fwd's masks and fa_fwd_window's extents, including the
+    extremes of that range."""
     import subprocess
     src = tmp_path / "cls.cpp"
     hdr = fa.LIB_PATH.replace("libfa.so", "csrc/fa_sched.h")
@@ -111,23 +170,36 @@ def test_32bit_block_class_equals_64bit(tmp_path):
 int main() {{
     long long n = 0, bad = 0;
     const int sizes[] = {{1, 2, 31, 32, 33, 64, 100, 257, 1000}};
-    for (int Nq : sizes) for (int Nk : sizes) for (int causal = 0; causal < 2; ++causal)
-    for (int window = 0; window < Nk; window += (window < 3 ? 1 : 37)) {{
-        if (window > 0 && !causal) continue;
-        for (int w0 = 0; w0 < Nq; w0 += 7) for (int w1 = w0 + 1; w1 <= Nq; w1 += 13)
-        for (int c0 = 0; c0 < Nk + 40; c0 += 32) {{
-            const int a = fa::tile_class(w0, w1, c0, c0 + 32, Nq, Nk, causal, window);
-            const int b = fa::tile_class32(w0, w1, c0, c0 + 32, Nq, Nk, causal, window);
-            int jf0, jf1, ju0, ju1;
-            fa::block_ranges32(w0, w1, Nq, Nk, causal, window, &jf0, &jf1, &ju0, &ju1);
-            const int j = c0 / 32;
-            const int r = (j >= jf0 && j < jf1) ? 1 : ((j >= ju0 && j < ju1) ? 2 : 0);
-            ++n; if (a != b || a != r) {{ if (bad < 5) std::printf("mismatch %d %d %d %d %d %d %d: %d vs %d vs %d\\n", w0, w1, c0, Nq, Nk, causal, window, a, b, r); ++bad; }}
+    auto check = [&](int w0, int w1, int c0, int Nq, int Nk, int wl, int wr) {{
+        const int a = fa::tile_class(w0, w1, c0, c0 + 32, Nq, Nk, wl, wr);
+        const int b = fa::tile_class32(w0, w1, c0, c0 + 32, Nq, Nk, wl, wr);
+        int jf0, jf1, ju0, ju1;
+        fa::block_ranges32(w0, w1, Nq, Nk, wl, wr, &jf0, &jf1, &ju0, &ju1);
+        const int j = c0 / 32;
+        const int r = (j >= jf0 && j < jf1) ? 1 : ((j >= ju0 && j < ju1) ? 2 : 0);
+        ++n; if (a != b || a != r) {{ if (bad < 5) std::printf("mismatch %d %d %d %d %d %d %d: %d vs %d vs %d\\n", w0, w1, c0, Nq, Nk, wl, wr, a, b, r); ++bad; }}
+    }};
+    for (int Nq : sizes) for (int Nk : sizes) {{
+        // fa_fwd's (causal, window) masks
+        for (int causal = 0; causal < 2; ++causal)
+        for (int window = 0; window < Nk + 3; window += (window < 3 ? 1 : 37)) {{
+            if (window > 0 && !causal) continue;
+            int wl, wr;
+            fa::mask_extents(causal, window, Nq, Nk, &wl, &wr);
+            for (int w0 = 0; w0 < Nq; w0 += 7) for (int w1 = w0 + 1; w1 <= Nq; w1 += 13)
+            for (int c0 = 0; c0 < Nk + 40; c0 += 32) check(w0, w1, c0, Nq, Nk, wl, wr);
+        }}
+        // fa_fwd_window's extents, clamped as the entry point clamps them
+        for (int wl0 : {{-1, 0, 1, 5, 31, 32, 100}}) for (int wr0 : {{-1, 0, 1, 7, 33, 200}}) {{
+            const int big = Nq + Nk;
+            const int wl = (wl0 < 0 || wl0 > big) ? big : wl0, wr = (wr0 < 0 || wr0 > big) ? big : wr0;
+            for (int w0 = 0; w0 < Nq; w0 += 11) for (int w1 = w0 + 1; w1 <= Nq; w1 += 17)
+            for (int c0 = 0; c0 < Nk + 40; c0 += 32) check(w0, w1, c0, Nq, Nk, wl, wr);
         }}
     }}
-    // extremes: sizes near 2^30, a window just below Nk
-    const int big = (1 << 30) - 64;
-    const int ext[][4] = {{{{big, big, 1, big - 1}}, {{big, 64, 1, 63}}, {{64, big, 1, 0}}, {{big, big, 0, 0}}, {{big, big, 1, 0}}}};
+    // extremes: sizes near 2^28, extents up to Nq + Nk
+    const int big = (1 << 28) - 64;
+    const int ext[][4] = {{{{big, big, big - 2, 0}}, {{big, 64, 2 * big, 2 * big}}, {{64, big, 1, 2 * big}}, {{big, big, 0, 0}}, {{big, big, 2 * big, 0}}, {{big, big, 1000, 1000}}}};
     for (const auto& e : ext) for (int w0 : {{0, 64, e[0] - 64}}) for (int c0 : {{0, 32, e[1] - 32, e[1] - 64}}) {{
         if (w0 < 0 || c0 < 0) continue;
         const int w1 = w0 + 64 < e[0] ? w0 + 64 : e[0];
