@@ -45,6 +45,10 @@ def load(path: str = _LIB):
     fw = lib.oracle_attn_fwd_window
     fw.argtypes = [P, P, P, P, P, L, L, L, L, L, ctypes.c_double, L, L, P, L, ctypes.c_int]
     fw.restype = ctypes.c_int
+    fm = lib.oracle_attn_fwd_mod
+    fm.argtypes = [P, P, P, P, P, L, L, L, L, L, ctypes.c_double, L, L, ctypes.c_int, ctypes.c_double, P, P, L,
+                   ctypes.c_int]
+    fm.restype = ctypes.c_int
     return lib
 
 
@@ -73,8 +77,12 @@ def decode(x: torch.Tensor, descale: float = 1.0) -> torch.Tensor:
     return y.contiguous()
 
 
+MODS = {None: 0, "softcap": 1, "alibi": 2}
+
+
 def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
-              rows=None, threads=None, lib=None, window_left=None, window_right=None):
+              rows=None, threads=None, lib=None, window_left=None, window_right=None,
+              score_mod=None, softcap=0.0, alibi_slopes=None):
     """float64 O and LSE of softmax(scale * Q K^T) V.
 
     q [B,H,Nq,D], k and v [B,H,Nk,D] (CPU or device tensors of any float dtype).
@@ -84,9 +92,31 @@ def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
     The mask is (causal, window), or, when window_left or window_right is
     given, the keys [i' - window_left, i' + window_right] of row i (None or a
     negative extent: that side open); causal and window are then ignored.
+    score_mod: None, "softcap" (s <- softcap * tanh(s / softcap)) or "alibi"
+    (s <- s + alibi_slopes[h] * (j - i'), alibi_slopes a sequence of H floats).
     """
     lib = lib or _get()
-    if window_left is not None or window_right is not None:
+    if score_mod is not None:
+        mod = MODS[score_mod]
+        if window_left is not None or window_right is not None:
+            wl = -1 if window_left is None else int(window_left)
+            wr = -1 if window_right is None else int(window_right)
+        else:
+            wl = window - 1 if window > 0 else -1
+            wr = 0 if causal else -1
+        Hn = q.shape[1]
+        slopes_all = torch.zeros(Hn, dtype=torch.float64)
+        if mod == 2:
+            slopes_all = torch.as_tensor([float(x) for x in alibi_slopes], dtype=torch.float64)
+            assert slopes_all.numel() == Hn
+        cap = float(softcap)
+        cur = {"slopes": slopes_all}
+
+        def call(Qp, Kp, Vp, Op, Lp, B_, H_, rows_p, nrows):
+            sl = cur["slopes"].contiguous()
+            return lib.oracle_attn_fwd_mod(Qp, Kp, Vp, Op, Lp, B_, H_, Nq, Nk, D, scale64, wl, wr, mod, cap,
+                                           sl.data_ptr(), rows_p, nrows, threads)
+    elif window_left is not None or window_right is not None:
         wl = -1 if window_left is None else int(window_left)
         wr = -1 if window_right is None else int(window_right)
 
@@ -119,6 +149,8 @@ def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
     for bh in torch.unique(bh_of).tolist():
         sel = (bh_of == bh).nonzero().flatten()
         b, h = divmod(bh, H)
+        if score_mod is not None:
+            cur["slopes"] = slopes_all[h:h + 1]   # this head's slope, for a one-head call
         Q = decode(q[b, h], descales[0])
         K = decode(k[b, h], descales[1])
         V = decode(v[b, h], descales[2])

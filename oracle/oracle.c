@@ -32,6 +32,12 @@
  * max(0, i-w) .. min(n, i+w+1)-1 of row i), with the two sides allowed to
  * differ and a negative extent leaving a side open.
  *
+ * oracle_attn_fwd_mod adds a score modifier, applied to each visible s_j
+ * before the softmax (FLASHLIGHT's score_mod variants in the gist.science
+ * summary, Results: ALiBi and Softcap):
+ *   softcap: s_j <- cap * tanh(s_j / cap)
+ *   ALiBi:   s_j <- s_j + slope[h] * (j - i')      (h the head of the row)
+ *
  * Inputs are float64 arrays the caller decoded exactly from the storage
  * dtype. Layout: Q [B,H,Nq,D], K and V [B,H,Nk,D], contiguous.
  */
@@ -50,6 +56,9 @@ typedef struct {
     int causal;
     int extents;        /* 1: the mask is (wl, wr) below, not (causal, window) */
     long wl, wr;
+    int mod;            /* 0 none, 1 softcap, 2 ALiBi */
+    double cap;
+    const double *slopes;   /* [H] for ALiBi */
     const long *rows;   /* flattened (b*H + h)*Nq + i, or NULL for every row */
     long nrows;
     long next;          /* work counter, shared */
@@ -91,6 +100,13 @@ static int one_row(const job_t *jb, long flat, double *s, double *o_row, double 
         double dot = 0.0;
         for (long d = 0; d < D; ++d) dot += qi[d] * kj[d];
         s[j - lo] = jb->scale * dot;
+    }
+    /* Score modifier. */
+    if (jb->mod == 1) {
+        for (long j = lo; j < hi; ++j) s[j - lo] = jb->cap * tanh(s[j - lo] / jb->cap);
+    } else if (jb->mod == 2) {
+        const double slope = jb->slopes[bh % jb->H];
+        for (long j = lo; j < hi; ++j) s[j - lo] += slope * (double)(j - ip);
     }
     /* Softmax of the row: max, exponentials, sum, normalise. */
     double m = s[0];
@@ -177,6 +193,25 @@ int oracle_attn_fwd_window(const double *q, const double *k, const double *v, do
     jb.q = q; jb.k = k; jb.v = v; jb.o = o; jb.lse = lse;
     jb.B = B; jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.D = D;
     jb.scale = scale; jb.extents = 1; jb.wl = wl; jb.wr = wr;
+    jb.rows = rows; jb.nrows = nrows;
+    return run_job(&jb, nthreads);
+}
+
+/* The extents mask with a score modifier: mod 1 softcap (cap > 0), mod 2
+   ALiBi (slopes[H]). */
+int oracle_attn_fwd_mod(const double *q, const double *k, const double *v, double *o, double *lse,
+                        long B, long H, long Nq, long Nk, long D, double scale, long wl, long wr,
+                        int mod, double cap, const double *slopes,
+                        const long *rows, long nrows, int nthreads)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D <= 0 || nthreads <= 0) return -1;
+    if (mod < 0 || mod > 2 || (mod == 1 && !(cap > 0.0)) || (mod == 2 && !slopes)) return -1;
+    job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.q = q; jb.k = k; jb.v = v; jb.o = o; jb.lse = lse;
+    jb.B = B; jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.D = D;
+    jb.scale = scale; jb.extents = 1; jb.wl = wl; jb.wr = wr;
+    jb.mod = mod; jb.cap = cap; jb.slopes = slopes;
     jb.rows = rows; jb.nrows = nrows;
     return run_job(&jb, nthreads);
 }

@@ -192,6 +192,84 @@ def test_sliding_window_matches_the_pages_mask_example():
     assert oracle.pair_count_window(n, n, window, window) == int(keep.sum())
 
 
+# ------------------------------------------------------- score modifiers
+
+def alibi_bias(Nq, Nk, slopes):
+    """[H, Nq, Nk] additive ALiBi bias slope_h * (j - i'), built independently of the oracle."""
+    i = torch.arange(Nq, dtype=torch.float64).view(-1, 1) + (Nk - Nq)
+    j = torch.arange(Nk, dtype=torch.float64).view(1, -1)
+    return torch.stack([s * (j - i) for s in slopes])
+
+
+@pytest.mark.parametrize("Nq,Nk,D,wl,wr", [(65, 65, 64, -1, 0), (100, 64, 64, -1, 0), (64, 100, 128, -1, -1),
+                                           (129, 129, 64, 20, 20), (90, 90, 64, 10, 0)])
+def test_alibi_against_torch_sdpa_float_mask(Nq, Nk, D, wl, wr):
+    B, H = 1, 3
+    Q, K, V = rnd((B, H, Nq, D), 24, 0), rnd((B, H, Nk, D), 24, 1), rnd((B, H, Nk, D), 24, 2)
+    slopes = [0.5, 0.125, 0.03125]
+    s32 = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+    O, L = oracle.attention(Q, K, V, 1.0 / math.sqrt(D), window_left=wl, window_right=wr,
+                            score_mod="alibi", alibi_slopes=slopes)
+    keep = mask_matrix_window(Nq, Nk, wl, wr)
+    bias = alibi_bias(Nq, Nk, slopes).masked_fill(~keep, -math.inf).unsqueeze(0)
+    Oref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=bias, scale=s32)
+    Lref = torch.logsumexp(torch.matmul(Q, K.transpose(-1, -2)) * s32 + bias, dim=-1)
+    ok = keep.any(dim=1)
+    assert torch.allclose(O[:, :, ok], Oref[:, :, ok], rtol=0, atol=1e-12)
+    assert torch.allclose(L[:, :, ok], Lref[:, :, ok], rtol=1e-13, atol=1e-12)
+
+
+def test_alibi_zero_query_is_a_geometric_series():
+    """With Q = 0 the causal ALiBi weights of row i are e^(-slope*k), k = i - j: a geometric series."""
+    N, D, slope = 60, 64, 0.3
+    Q = torch.zeros(1, 1, N, D, dtype=torch.float64)
+    K, V = rnd((1, 1, N, D), 25, 1), rnd((1, 1, N, D), 25, 2)
+    O, L = oracle.attention(Q, K, V, 0.125, True, 0, score_mod="alibi", alibi_slopes=[slope])
+    r = math.exp(-slope)
+    for i in range(N):
+        lse = math.log((1 - r ** (i + 1)) / (1 - r))
+        assert abs(L[0, 0, i].item() - lse) <= 1e-13 * max(1.0, abs(lse))
+        w = torch.tensor([r ** (i - j) for j in range(i + 1)], dtype=torch.float64)
+        assert torch.allclose(O[0, 0, i], (w[:, None] * V[0, 0, : i + 1]).sum(0) / w.sum(), atol=1e-13)
+
+
+def test_alibi_with_zero_slope_and_softcap_limits_are_plain_attention():
+    N, D = 80, 64
+    Q, K, V = rnd((1, 2, N, D), 26, 0), rnd((1, 2, N, D), 26, 1), rnd((1, 2, N, D), 26, 2)
+    O0, L0 = oracle.attention(Q, K, V, 0.125, True, 0)
+    O1, L1 = oracle.attention(Q, K, V, 0.125, True, 0, score_mod="alibi", alibi_slopes=[0.0, 0.0])
+    assert torch.equal(O0, O1) and torch.equal(L0, L1)
+    O2, L2 = oracle.attention(Q, K, V, 0.125, True, 0, score_mod="softcap", softcap=1e7)
+    assert torch.allclose(O2, O0, atol=1e-10) and torch.allclose(L2, L0, atol=1e-10)
+    # a tiny cap flattens every score to (almost) the same value: the weights become uniform
+    O3, L3 = oracle.attention(Q, K, V, 0.125, True, 0, score_mod="softcap", softcap=1e-9)
+    cnt = torch.arange(1, N + 1, dtype=torch.float64)
+    assert torch.allclose(O3, V.cumsum(dim=2) / cnt.view(1, 1, N, 1), atol=1e-8)
+    assert torch.allclose(L3, torch.log(cnt).expand_as(L3), atol=1e-8)
+
+
+@pytest.mark.parametrize("Nq,Nk,D,causal,cap", [(4, 4, 3, True, 0.8), (5, 3, 4, True, 2.5), (3, 5, 3, False, 0.3)])
+def test_softcap_bruteforce_50_digits(Nq, Nk, D, causal, cap):
+    Q, K, V = rnd((1, 1, Nq, D), 27, 0) * 2.0, rnd((1, 1, Nk, D), 27, 1) * 1.5, rnd((1, 1, Nk, D), 27, 2)
+    scale = 0.61
+    O, L = oracle.attention(Q, K, V, scale, causal, 0, score_mod="softcap", softcap=cap)
+    mpmath.mp.dps = 50
+    keep = mask_matrix(Nq, Nk, causal, 0)
+    sc = mpmath.mpf(float(torch.tensor(scale, dtype=torch.float32)))
+    cp = mpmath.mpf(cap)
+    for i in range(Nq):
+        js = [j for j in range(Nk) if keep[i, j]]
+        if not js:
+            continue
+        s = {j: cp * mpmath.tanh(sc * mpmath.fsum(mpmath.mpf(float(Q[0, 0, i, d])) * mpmath.mpf(float(K[0, 0, j, d]))
+                                                   for d in range(D)) / cp) for j in js}
+        den = mpmath.fsum(mpmath.exp(s[j]) for j in js)
+        assert abs(L[0, 0, i].item() - float(mpmath.log(den))) <= 1e-13
+        for d in range(D):
+            ref = mpmath.fsum(mpmath.exp(s[j]) * mpmath.mpf(float(V[0, 0, j, d])) for j in js) / den
+            assert abs(O[0, 0, i, d].item() - float(ref)) <= 1e-13
+
+
 # ------------------------------------------------------------- closed forms
 
 @pytest.mark.parametrize("Nq,Nk,causal,window", [(40, 40, False, 0), (40, 40, True, 0), (40, 40, True, 7), (30, 50, True, 0)])
@@ -402,6 +480,12 @@ MUTANTS = {
                                 "if (jb->wr >= 0) hi = ip + jb->wr < Nk ? ip + jb->wr : Nk;"),
     "extents_swapped": ("if (jb->wl >= 0) lo = ip - jb->wl > 0 ? ip - jb->wl : 0;",
                         "if (jb->wr >= 0) lo = ip - jb->wr > 0 ? ip - jb->wr : 0;"),
+    "alibi_sign": ("s[j - lo] += slope * (double)(j - ip);", "s[j - lo] += slope * (double)(ip - j);"),
+    "alibi_top_left": ("s[j - lo] += slope * (double)(j - ip);", "s[j - lo] += slope * (double)(j - i);"),
+    "alibi_wrong_head": ("const double slope = jb->slopes[bh % jb->H];",
+                         "const double slope = jb->slopes[(bh + 1) % jb->H];"),
+    "softcap_no_outer": ("s[j - lo] = jb->cap * tanh(s[j - lo] / jb->cap);", "s[j - lo] = tanh(s[j - lo] / jb->cap);"),
+    "softcap_no_inner": ("s[j - lo] = jb->cap * tanh(s[j - lo] / jb->cap);", "s[j - lo] = jb->cap * tanh(s[j - lo]);"),
 }
 
 
@@ -446,6 +530,26 @@ def pin_suite(lib) -> bool:
                     continue
                 if abs(L[0, 0, i].item() - float(Lm[i])) > 1e-12:
                     return False
+        # ALiBi against torch's SDPA with the bias as an additive mask (two heads, Nq != Nk)
+        Qa, Ka, Va = rnd((1, 2, 5, 8), 15, 0), rnd((1, 2, 9, 8), 15, 1), rnd((1, 2, 9, 8), 15, 2)
+        slopes = [0.7, 0.2]
+        O, L = oracle.attention(Qa, Ka, Va, 0.5, True, 0, score_mod="alibi", alibi_slopes=slopes, lib=lib, threads=1)
+        keep = mask_matrix(5, 9, True, 0)
+        bias = alibi_bias(5, 9, slopes).masked_fill(~keep, -math.inf).unsqueeze(0)
+        Oref = torch.nn.functional.scaled_dot_product_attention(Qa, Ka, Va, attn_mask=bias, scale=0.5)
+        Lref = torch.logsumexp(torch.matmul(Qa, Ka.transpose(-1, -2)) * 0.5 + bias, dim=-1)
+        if not torch.allclose(O, Oref, atol=1e-12) or not torch.allclose(L, Lref, atol=1e-12):
+            return False
+        # softcap at 50 digits
+        O, L = oracle.attention(Q, K, V, 0.7, True, 0, score_mod="softcap", softcap=0.9, lib=lib, threads=1)
+        mpmath.mp.dps = 50
+        sc, cp = mpmath.mpf(float(torch.tensor(0.7, dtype=torch.float32))), mpmath.mpf(0.9)
+        for i in range(4):
+            js = [j for j in range(6) if mask_matrix(4, 6, True, 0)[i, j]]
+            sv = [cp * mpmath.tanh(sc * mpmath.fsum(mpmath.mpf(float(Q[0, 0, i, d])) * mpmath.mpf(float(K[0, 0, j, d]))
+                                                     for d in range(3)) / cp) for j in js]
+            if abs(L[0, 0, i].item() - float(mpmath.log(mpmath.fsum(mpmath.exp(x) for x in sv)))) > 1e-12:
+                return False
         return True
     except RuntimeError:
         return False
