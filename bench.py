@@ -94,6 +94,7 @@ def cpu_baseline(w, inp, target_s=15.0):
     """The oracle, as it is, on random rows of the workload, scaled to TFLOP/s."""
     import torch
     import oracle
+    import synth
     threads = oracle.default_threads()
     g = torch.Generator().manual_seed(1234)
     n_rows_total = w.B * w.H * w.Nq
@@ -102,6 +103,9 @@ def cpu_baseline(w, inp, target_s=15.0):
     wl = -1 if w.window_left is None else w.window_left
     wr = -1 if w.window_right is None else w.window_right
     mask = dict(window_left=wl, window_right=wr) if ext else {}
+    if w.score_mod is not None:
+        mask.update(score_mod=w.score_mod, softcap=w.softcap,
+                    alibi_slopes=synth.alibi_slopes(w.H) if w.score_mod == "alibi" else None)
 
     def row_pairs(rows):
         i = rows % w.Nq + (w.Nk - w.Nq)
@@ -134,7 +138,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw")
+    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw c3sc c3al")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (to scale the FETCH_SIZE/WRITE_SIZE "
@@ -168,10 +172,15 @@ def main():
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     descales = (inp.descale_q, inp.descale_k, inp.descale_v) if w.in_dtype == "e4m3" else None
     stream = torch.cuda.current_stream(dev)
+    mod = {}
+    if w.score_mod is not None:
+        mod = dict(score_mod=w.score_mod, softcap=w.softcap)
+        if w.score_mod == "alibi":
+            mod["alibi"] = torch.tensor(synth.alibi_slopes(w.H), dtype=torch.float32, device=dev)
 
     def step():
         fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window, out=o, lse=lse,
-                     window_left=w.window_left, window_right=w.window_right,
+                     window_left=w.window_left, window_right=w.window_right, **mod,
                      descales=descales, stream=stream.cuda_stream)
 
     for _ in range(args.warmup):
@@ -206,7 +215,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
                    "causal": w.causal, "window": w.window, "window_left": w.window_left,
-                   "window_right": w.window_right, "in": w.in_dtype, "out": w.out_dtype,
+                   "window_right": w.window_right, "score_mod": w.score_mod, "softcap": w.softcap,
+                   "in": w.in_dtype, "out": w.out_dtype,
                    "parallelism": "single GPU"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",

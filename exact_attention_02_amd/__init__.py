@@ -23,8 +23,10 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_F16, FA_BF16, FA_F16_F32OUT, FA_E4M3, FA_BF16_F32OUT = 1, 2, 3, 4, 5
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE = 0, 1, 2, 3, 4
 FA_ERR_MASK, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_DEVICE, FA_ERR_LAUNCH = 5, 6, 7, 8, 9
+FA_ERR_MOD = 10
+FA_MOD_NONE, FA_MOD_SOFTCAP, FA_MOD_ALIBI = 0, 1, 2
 
-EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_status_str", "fa_plan_grid", "fa_plan_tile",
+EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_mod", "fa_status_str", "fa_plan_grid", "fa_plan_tile",
            "fa_plan_block_class", "fa_plan_window_range", "fa_plan_block_class_window")
 
 _lib = None
@@ -52,6 +54,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_fp8.restype = I
     lib.fa_fwd_window.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, F, F, F]
     lib.fa_fwd_window.restype = I
+    lib.fa_fwd_mod.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, I, F, P]
+    lib.fa_fwd_mod.restype = I
     lib.fa_status_str.argtypes = [I]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_plan_grid.argtypes = [I, I, I, I, I, I, I, I, pLL, pI, pI, pI]
@@ -84,6 +88,17 @@ def fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_r
                   descale_q=1.0, descale_k=1.0, descale_v=1.0) -> int:
     return load().fa_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(window_left), int(window_right), dtype,
                                 stream, descale_q, descale_k, descale_v)
+
+
+def fa_fwd_mod(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_right, dtype, stream,
+               score_mod, softcap=0.0, alibi_slopes=None) -> int:
+    return load().fa_fwd_mod(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(window_left), int(window_right), dtype,
+                             stream, int(score_mod), float(softcap), alibi_slopes)
+
+
+def alibi_slopes(H: int):
+    """The geometric ALiBi slopes 2^(-8 (h+1) / H), h = 0 .. H-1, as a list of floats."""
+    return [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
 
 
 def fa_status_str(status: int) -> str:
@@ -143,7 +158,8 @@ def dtype_code(in_dtype, out_dtype) -> int:
 
 
 def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, out_dtype=None,
-              descales=None, stream=None, window_left=None, window_right=None):
+              descales=None, stream=None, window_left=None, window_right=None,
+              score_mod=None, softcap=0.0, alibi=None):
     """O [B,H,Nq,D] and LSE [B,H,Nq] (float32) of softmax(scale Q K^T) V via libfa.
 
     q [B,H,Nq,D], k and v [B,H,Nk,D]: contiguous device tensors of one dtype
@@ -153,6 +169,9 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
     window_right is given, the key interval [i' - window_left, i' + window_right]
     of fa_fwd_window (None or -1: that side unbounded; causal and window are then
     ignored).
+    score_mod: None, "softcap" (s <- softcap * tanh(s / softcap)) or "alibi"
+    (s <- s + slope_h * (j - i')); alibi is a float32 device tensor of H slopes
+    (default: alibi_slopes(H)). Score modifiers go through fa_fwd_mod.
     """
     import torch
     B, H, Nq, D = q.shape
@@ -176,6 +195,25 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    if score_mod is not None:
+        if window_left is not None or window_right is not None:
+            wl = -1 if window_left is None else int(window_left)
+            wr = -1 if window_right is None else int(window_right)
+        else:
+            wl = int(window) - 1 if window > 0 else -1
+            wr = 0 if causal else -1
+        mod = {"softcap": FA_MOD_SOFTCAP, "alibi": FA_MOD_ALIBI, "none": FA_MOD_NONE}[score_mod]
+        slopes_ptr = None
+        if mod == FA_MOD_ALIBI:
+            if alibi is None:
+                alibi = torch.tensor(alibi_slopes(H), dtype=torch.float32, device=q.device)
+            if alibi.dtype != torch.float32 or alibi.numel() != H or not alibi.is_contiguous():
+                raise ValueError("alibi must be a contiguous float32 tensor of H slopes")
+            slopes_ptr = alibi.data_ptr()
+        st = fa_fwd_mod(*ptrs, B, H, Nq, Nk, D, float(scale), wl, wr, code, stream, mod, float(softcap), slopes_ptr)
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_mod")
+        return out, lse
     if window_left is not None or window_right is not None:
         wl = -1 if window_left is None else int(window_left)
         wr = -1 if window_right is None else int(window_right)

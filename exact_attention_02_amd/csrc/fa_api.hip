@@ -85,7 +85,8 @@ bool window_extents(int window_left, int window_right, int Nq, int Nk, int* wl, 
 }
 
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
-        float scale, int wl, int wr, int dtype, void* stream, float dq, float dk, float dv) {
+        float scale, int wl, int wr, int dtype, void* stream, float dq, float dk, float dv,
+        int mod = FA_MOD_NONE, float cap = 0.f, const float* slopes = nullptr) {
     DtypeInfo di;
     const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
     if (st != FA_OK) return st;
@@ -100,7 +101,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const int dst = check_device();
     if (dst != FA_OK) return dst;
 
-    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq);
+    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq, mod);
     fa::Params p;
     p.q = (const uint8_t*)q;
     p.k = (const uint8_t*)k;
@@ -115,6 +116,11 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.n_qt = pl.n_qt;
     p.c = scale * dq * dk * 1.44269504088896341f;
     p.out_mul = dv;
+    p.H = H;
+    p.mod = mod;
+    p.mk1 = (mod == FA_MOD_SOFTCAP) ? 2.f * p.c / cap : 0.f;
+    p.mk2 = (mod == FA_MOD_SOFTCAP) ? cap * 1.44269504088896341f : 0.f;
+    p.slopes = slopes;
     if (std::getenv("FA_DEBUG"))
         std::fprintf(stderr, "fa_fwd: in=%d out=%d D=%d kernel=%d nw=%d qb=%d br=%d bc=%d n_qt=%d n_wg=%lld\n",
                      pl.in, pl.out, pl.D, pl.kernel, pl.nw, pl.qb, pl.br, pl.bc, pl.n_qt, pl.n_wg);
@@ -165,6 +171,25 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
     return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, descale_q, descale_k, descale_v);
 }
 
+int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+               int D, float scale, int window_left, int window_right, int dtype, void* stream, int score_mod,
+               float softcap, const float* alibi_slopes) {
+    DtypeInfo di;
+    const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
+    if (st != FA_OK) return st;
+    int wl, wr;
+    if (!window_extents(window_left, window_right, Nq, Nk, &wl, &wr)) return FA_ERR_MASK;
+    if (score_mod != FA_MOD_NONE && score_mod != FA_MOD_SOFTCAP && score_mod != FA_MOD_ALIBI) return FA_ERR_MOD;
+    if (score_mod != FA_MOD_NONE && di.in == fa::IN_E4M3) return FA_ERR_MOD;
+    if (score_mod == FA_MOD_SOFTCAP && !finite_positive(softcap)) return FA_ERR_MOD;
+    if (score_mod == FA_MOD_ALIBI && (long long)B * H * Nq > 0) {
+        if (!alibi_slopes) return FA_ERR_NULL;
+        if (!aligned(alibi_slopes, 4)) return FA_ERR_ALIGN;
+    }
+    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, 1.f, 1.f, 1.f, score_mod, softcap,
+               alibi_slopes);
+}
+
 const char* fa_status_str(int status) {
     switch (status) {
         case FA_OK: return "ok";
@@ -177,6 +202,7 @@ const char* fa_status_str(int status) {
         case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
         case FA_ERR_DEVICE: return "no gfx950 HIP device is current";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_MOD: return "unknown score modifier, a bad modifier parameter, or a modifier with e4m3 inputs";
         default: return "unknown status";
     }
 }

@@ -94,11 +94,12 @@ __device__ __forceinline__ int lds_pos(int x, int c) {
 #ifndef FA_WPS_D64
 #define FA_WPS_D64 3
 #endif
-template <int D, int QB>
-constexpr int waves_per_simd() { return (D == 64 && QB == 1) ? FA_WPS_D64 : 2; }
+// A score modifier needs more registers: two waves per SIMD.
+template <int D, int QB, int MOD>
+constexpr int waves_per_simd() { return (D == 64 && QB == 1 && MOD == MOD_NONE) ? FA_WPS_D64 : 2; }
 
-template <int IN, int OUT, int D, int NW, int QB>
-__global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_kernel(Params p) {
+template <int IN, int OUT, int D, int NW, int QB, int MOD>
+__global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fwd16_kernel(Params p) {
     constexpr int NT = 64 * NW;
     constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
@@ -163,6 +164,11 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
         lh[qb] = 0.f;
     }
     const float c2 = p.c;
+    // Score modifier (MOD_SOFTCAP, MOD_ALIBI): constants in base-2 units.
+    const float sc_k1 = p.mk1;   // softcap: e^(2|x|) = 2^(sc_k1 |s|), x = scale * s / cap
+    const float sc_k2 = p.mk2;   // softcap: cap * log2(e)
+    float slope2 = 0.f;          // ALiBi: this head's slope * log2(e)
+    if constexpr (MOD == MOD_ALIBI) slope2 = p.slopes[bh % p.H] * LOG2E;
 
     // ---- K/V copies: lane l of a wave fills the l-th 16-byte slot of a 1 KiB
     // run of the tile, fetching the global chunk that belongs there under the
@@ -273,10 +279,42 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
 
     // p = 2^(c*s - ms) for the 16 scores, their sum (a fixed pairwise order)
     // and p rounded to the MFMA type.
-    auto p_phase_pr = [&](const f32x16& S, float ms, float& ts, i32x4(&hi)[2], float(&pr)[16])
+    // The exponent argument of score s (element r of a lane's block) against
+    // the reference ref: the score in base-2 units, modified, minus ref.
+    //   none:    c * s - ref
+    //   ALiBi:   c * s + slope * log2(e) * (key - i') - ref; key - i' is
+    //            32j + 4hh - i' (in abase, with -ref) plus 8(r/4) + r%4
+    //   softcap: cap * log2(e) * tanh(scale * s / cap) - ref, with
+    //            tanh|x| = 1 - 2 / (e^(2|x|) + 1); a masked score stays -inf
+    auto alibi_base = [&](int j, int qb, float ref) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int ipq = w0 + 32 * qb + (ln & 31) + (Nk - Nq);
+        return fmaf(slope2, (float)(32 * j + 4 * (ln >> 5) - ipq), -ref);
+    };
+    auto earg = [&](float s, int r, float abase, float ref) __attribute__((always_inline)) {
+        if constexpr (MOD == MOD_ALIBI) {
+            return fmaf(s, c2, fmaf(slope2, (float)(8 * (r >> 2) + (r & 3)), abase));
+        } else if constexpr (MOD == MOD_SOFTCAP) {
+            const float u = __builtin_amdgcn_exp2f(fabsf(s) * sc_k1);
+            const float t = fmaf(-2.f, __builtin_amdgcn_rcpf(u + 1.f), 1.f);
+            const float a = fmaf(__builtin_copysignf(t, s), sc_k2, -ref);
+            return (s == -INFINITY) ? -INFINITY : a;
+        } else {
+            return fmaf(s, c2, -ref);
+        }
+    };
+    auto p_phase_pr = [&](const f32x16& S, float ms, float& ts, i32x4(&hi)[2], float(&pr)[16], int j, int qb)
         __attribute__((always_inline)) {
+        if constexpr (MOD == MOD_NONE) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+            for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+        } else {
+            float ab = 0.f;
+            if constexpr (MOD == MOD_ALIBI) ab = alibi_base(j, qb, ms);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(earg(S[r], r, ab, ms));
+        }
         float s8[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) s8[r] = pr[2 * r] + pr[2 * r + 1];
@@ -287,10 +325,6 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
             hi[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
                            pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
         }
-    };
-    auto p_phase = [&](const f32x16& S, float ms, float& ts, i32x4(&hi)[2]) __attribute__((always_inline)) {
-        float pr[16];
-        p_phase_pr(S, ms, ts, hi, pr);
     };
     // The rounding residual of the weights, lo = p - hi rounded to the MFMA
     // type (zero where on is false).
@@ -385,18 +419,29 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
                 // the weights so far saw every key of the sub-tile: mask, form
                 // them again, and decide on the visible keys alone
                 mask(j, qb, S);
-                p_phase_pr(S, ms, ts, hi, pr);
+                p_phase_pr(S, ms, ts, hi, pr, j, qb);
                 trig = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
             }
             if (__builtin_amdgcn_ballot_w64(trig) != 0) {
                 const unsigned tr = trig ? 1u : 0u;
                 auto pw = __builtin_amdgcn_permlane32_swap(tr, tr, false, false);
                 const bool row = (pw[0] | pw[1]) != 0;
-                float mx = S[0];
+                float mx;
+                if constexpr (MOD == MOD_NONE) {
+                    mx = S[0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-                mx = max_halves(mx);
-                const float mnew = row ? fmaxf(m[qb], mx * c2) : m[qb];
+                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+                    mx = max_halves(mx);
+                } else {
+                    float ab = 0.f;
+                    if constexpr (MOD == MOD_ALIBI) ab = alibi_base(j, qb, 0.f);
+                    mx = earg(S[0], 0, ab, 0.f);
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, earg(S[r], r, ab, 0.f));
+                    mx = max_halves(mx);
+                }
+                // the row max in base-2 units (the modified scores are already)
+                const float mnew = row ? fmaxf(m[qb], (MOD == MOD_NONE) ? mx * c2 : mx) : m[qb];
                 const bool mv = mnew != m[qb];
                 const float alpha = mv ? __builtin_amdgcn_exp2f(m[qb] - mnew) : 1.f;
                 m[qb] = mnew;
@@ -406,14 +451,21 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
                     for (int db = 0; db < ND; ++db) oacc[db][qb] *= alpha;
                 }
                 ms = (mnew == -INFINITY) ? 0.f : mnew;
-                p_phase_pr(S, ms, ts, hi, pr);
+                p_phase_pr(S, ms, ts, hi, pr, j, qb);
             }
             if constexpr (!EARLY) {
                 const bool sr = !skip & (ts * 3.f > lh[qb]);
                 if (__builtin_amdgcn_ballot_w64(sr) != 0) {
                     float pe[16];
+                    if constexpr (MOD == MOD_NONE) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+                        for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+                    } else {
+                        float ab = 0.f;
+                        if constexpr (MOD == MOD_ALIBI) ab = alibi_base(j, qb, ms);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(earg(S[r], r, ab, ms));
+                    }
                     i32x4 lo[2];
                     residual(pe, hi, sr, lo);
                     if constexpr (RA >= 1) {
@@ -486,7 +538,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
             scores(((jn >> 1) == t) ? lds_cur : lds_next, jn, qn, Sn);
         }
         float pr[16];
-        p_phase_pr(S, ms, ts, Pc, pr);
+        p_phase_pr(S, ms, ts, Pc, pr, j, qb);
         if constexpr (RA >= 1) pv(qpv, vb[KP ^ 1], Pp);
         else pv(qpv, va, Pp);
         if constexpr (RA == 2) {
@@ -636,19 +688,26 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB>())) void fa_fwd16_k
 
 // ---------------------------------------------------------------- host side
 
-template <int IN, int OUT, int D, int NW, int QB>
+template <int IN, int OUT, int D, int NW, int QB, int MOD>
 static int launch16_one(const Plan& pl, const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((fa_fwd16_kernel<IN, OUT, D, NW, QB>), dim3((unsigned)pl.n_wg), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((fa_fwd16_kernel<IN, OUT, D, NW, QB, MOD>), dim3((unsigned)pl.n_wg), dim3(64 * NW), 0, s, p);
     return (int)hipGetLastError();
+}
+
+template <int IN, int OUT, int D, int NW, int QB>
+static int launch16_mod(const Plan& pl, const Params& p, hipStream_t s) {
+    if (p.mod == MOD_SOFTCAP) return launch16_one<IN, OUT, D, NW, QB, MOD_SOFTCAP>(pl, p, s);
+    if (p.mod == MOD_ALIBI) return launch16_one<IN, OUT, D, NW, QB, MOD_ALIBI>(pl, p, s);
+    return launch16_one<IN, OUT, D, NW, QB, MOD_NONE>(pl, p, s);
 }
 
 template <int IN, int OUT>
 static int launch16_io(const Plan& pl, const Params& p, hipStream_t s) {
     if (pl.D == 64) {
-        if (pl.qb == 2) return launch16_one<IN, OUT, 64, 4, 2>(pl, p, s);
-        return launch16_one<IN, OUT, 64, 4, 1>(pl, p, s);
+        if (pl.qb == 2) return launch16_mod<IN, OUT, 64, 4, 2>(pl, p, s);
+        return launch16_mod<IN, OUT, 64, 4, 1>(pl, p, s);
     }
-    return launch16_one<IN, OUT, 128, 8, 1>(pl, p, s);
+    return launch16_mod<IN, OUT, 128, 8, 1>(pl, p, s);
 }
 
 int launch16(const Plan& pl, const Params& p, void* stream) {

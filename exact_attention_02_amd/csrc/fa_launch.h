@@ -11,6 +11,7 @@ enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
 // KERNEL_TILE64: 64-key tiles, one softmax per tile (all input types).
 // KERNEL_PIPE16: 16-bit inputs, scores of the next 32 keys formed during the
 // softmax of the current 32 (fa_fwd16.hip).
+enum ScoreMod { MOD_NONE = 0, MOD_SOFTCAP = 1, MOD_ALIBI = 2 };
 enum KernelKind { KERNEL_TILE64 = 0, KERNEL_PIPE16 = 1 };
 
 // Everything a workgroup needs; passed by value as the kernel argument.
@@ -23,6 +24,10 @@ struct Params {
     int Nq, Nk;
     int wl, wr;     // row i sees keys [i' - wl, i' + wr], i' = i + Nk - Nq (clamped to Nq + Nk)
     int n_bh;       // B * H
+    int H;          // heads (ALiBi: the head of bh is bh % H)
+    int mod;        // MOD_NONE, MOD_SOFTCAP or MOD_ALIBI (16-bit kernel only)
+    float mk1, mk2; // softcap constants: 2 * c / cap and cap * log2(e)
+    const float* slopes;  // ALiBi: [H] device array of per-head slopes
     int n_qt;       // query tiles per head
     float c;        // scale * descale_q * descale_k * log2(e): scores in base-2 units
     float out_mul;  // descale_v (1 unless e4m3)
@@ -41,7 +46,8 @@ struct Plan {
 };
 
 // Picks the tile shape for a problem. Pure host arithmetic.
-Plan make_plan(int in, int out, int D, int B, int H, int Nq);
+// mod != MOD_NONE needs the pipelined kernel (the only one with score modifiers).
+Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod = MOD_NONE);
 
 // Enqueues the kernel chosen by `plan` on `stream`; returns the hipError_t
 // value of hipGetLastError() after the launch (0 on success).

@@ -72,7 +72,16 @@ enum {
     FA_ERR_SCALE = 6,     /* scale or a descale is not finite and positive */
     FA_ERR_ALIGN = 7,     /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_DEVICE = 8,    /* no HIP device, or the current device is not gfx950 */
-    FA_ERR_LAUNCH = 9     /* the kernel launch failed (hipGetLastError) */
+    FA_ERR_LAUNCH = 9,    /* the kernel launch failed (hipGetLastError) */
+    FA_ERR_MOD = 10       /* fa_fwd_mod: unknown score modifier, softcap not finite
+                             and positive, or a modifier with FA_E4M3 inputs */
+};
+
+/* Score modifiers of fa_fwd_mod. */
+enum {
+    FA_MOD_NONE = 0,
+    FA_MOD_SOFTCAP = 1,   /* s <- softcap * tanh(s / softcap) */
+    FA_MOD_ALIBI = 2      /* s <- s + alibi_slopes[h] * (j - i'), i' = i + Nk - Nq */
 };
 
 /*
@@ -119,6 +128,26 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
                   int B, int H, int Nq, int Nk, int D, float scale,
                   int window_left, int window_right, int dtype, void* stream,
                   float descale_q, float descale_k, float descale_v);
+
+/*
+ * fa_fwd_mod: as fa_fwd_window, with a modifier applied to every visible
+ * scaled score s = scale * q_i . k_j before the softmax -- the score_mod
+ * variants FLASHLIGHT generates kernels for (gist.science summary of
+ * FLASHLIGHT, Results: ALiBi and Softcap among the variants):
+ *   FA_MOD_NONE    : none (the same results as fa_fwd_window);
+ *   FA_MOD_SOFTCAP : s <- softcap * tanh(s / softcap); softcap finite, > 0;
+ *   FA_MOD_ALIBI   : s <- s + alibi_slopes[h] * (j - i'), i' = i + (Nk - Nq),
+ *                    h the head; alibi_slopes is a device array of H float32
+ *                    (4-byte aligned) the caller owns.
+ * The LSE output is the log-sum-exp of the modified scores.
+ * fp16 and bf16 inputs only (FA_ERR_MOD for FA_E4M3 with a modifier).
+ * Errors as fa_fwd_window, plus FA_ERR_MOD, and FA_ERR_NULL for a NULL
+ * alibi_slopes with FA_MOD_ALIBI on a non-empty problem.
+ */
+int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Nq, int Nk, int D, float scale,
+               int window_left, int window_right, int dtype, void* stream,
+               int score_mod, float softcap, const float* alibi_slopes);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_str(int status);

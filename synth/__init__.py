@@ -155,6 +155,10 @@ class Workload:
     # [i' - window_left, i' + window_right], i' = i + Nk - Nq, -1 an open side.
     window_left: Optional[int] = None
     window_right: Optional[int] = None
+    # Score modifier: None, "softcap" (s <- softcap * tanh(s / softcap)) or
+    # "alibi" (s <- s + slope_h * (j - i') with the slopes alibi_slopes(H)).
+    score_mod: Optional[str] = None
+    softcap: float = 0.0
 
     def __post_init__(self):
         if self.scale == 0.0:
@@ -180,7 +184,17 @@ WORKLOADS = {
     # at c3's shape, w = 1024 (the page's example uses w = n / 8).
     "c3sw": Workload("c3_slidingwindow1024_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, False, 0, "bf16", "bf16", 3,
                      window_left=1024, window_right=1024),
+    # c3 with FLASHLIGHT's score_mod variants: softcap (cap 50) and ALiBi.
+    "c3sc": Workload("c3_causal_softcap50_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, True, 0, "bf16", "bf16", 3,
+                     score_mod="softcap", softcap=50.0),
+    "c3al": Workload("c3_causal_alibi_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, True, 0, "bf16", "bf16", 3,
+                     score_mod="alibi"),
 }
+
+
+def alibi_slopes(H: int):
+    """The geometric ALiBi slopes 2^(-8 (h+1) / H), h = 0 .. H-1 (an input of the alibi workloads)."""
+    return [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
 
 
 @dataclass
@@ -218,8 +232,9 @@ def make_inputs(w: Workload) -> Inputs:
 
 
 def small_workload(name, B, H, Nq, Nk, D, causal, window, in_dtype, out_dtype, seed,
-                   outlier_frac=0.0, outlier_mult=1.0, window_left=None, window_right=None) -> Workload:
+                   outlier_frac=0.0, outlier_mult=1.0, window_left=None, window_right=None,
+                   score_mod=None, softcap=0.0) -> Workload:
     """A workload of the same recipe at other sizes (parity and edge cases)."""
     return Workload(name, B, H, Nq, Nk, D, causal, window, in_dtype, out_dtype, seed,
                     outlier_frac=outlier_frac, outlier_mult=outlier_mult,
-                    window_left=window_left, window_right=window_right)
+                    window_left=window_left, window_right=window_right, score_mod=score_mod, softcap=softcap)

@@ -31,13 +31,14 @@ def test_enums_match_header():
     text = open(HEADER).read()
     for name in ["FA_F16", "FA_BF16", "FA_F16_F32OUT", "FA_E4M3", "FA_BF16_F32OUT", "FA_OK", "FA_ERR_NULL",
                  "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_DTYPE", "FA_ERR_MASK", "FA_ERR_SCALE",
-                 "FA_ERR_ALIGN", "FA_ERR_DEVICE", "FA_ERR_LAUNCH"]:
+                 "FA_ERR_ALIGN", "FA_ERR_DEVICE", "FA_ERR_LAUNCH", "FA_ERR_MOD", "FA_MOD_NONE", "FA_MOD_SOFTCAP",
+                 "FA_MOD_ALIBI"]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(fa, name), name
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         assert fa.fa_status_str(s) and fa.fa_status_str(s) != "unknown status"
     assert fa.fa_status_str(99) == "unknown status"
 
@@ -85,6 +86,23 @@ def test_window_entry_checks_extents_and_descales():
     assert fa.fa_fwd_window(P, P, P, P, P, 1, 1, 64, 64, 96, 0.125, -2, 0, fa.FA_BF16, None) == fa.FA_ERR_HEADDIM
     assert fa.fa_fwd_window(P, P, P, P, P, 0, 1, 64, 64, 64, 0.125, 4, 4, fa.FA_BF16, None) == fa.FA_OK
     assert fa.fa_fwd_window(0, P, P, P, P, 1, 1, 64, 64, 64, 0.125, 4, 4, fa.FA_BF16, None) == fa.FA_ERR_NULL
+
+
+def test_mod_entry_checks_modifier_and_parameters():
+    args = (P, P, P, P, P, 1, 1, 64, 64, 64, 0.125, -1, 0)
+    assert fa.fa_fwd_mod(*args, fa.FA_BF16, None, 3, 0.0, None) == fa.FA_ERR_MOD
+    assert fa.fa_fwd_mod(*args, fa.FA_BF16, None, -1, 0.0, None) == fa.FA_ERR_MOD
+    assert fa.fa_fwd_mod(*args, fa.FA_BF16, None, fa.FA_MOD_SOFTCAP, 0.0, None) == fa.FA_ERR_MOD
+    assert fa.fa_fwd_mod(*args, fa.FA_BF16, None, fa.FA_MOD_SOFTCAP, float("inf"), None) == fa.FA_ERR_MOD
+    assert fa.fa_fwd_mod(*args, fa.FA_E4M3, None, fa.FA_MOD_SOFTCAP, 30.0, None) == fa.FA_ERR_MOD
+    assert fa.fa_fwd_mod(*args, fa.FA_BF16, None, fa.FA_MOD_ALIBI, 0.0, None) == fa.FA_ERR_NULL
+    assert fa.fa_fwd_mod(*args, fa.FA_BF16, None, fa.FA_MOD_ALIBI, 0.0, P + 2) == fa.FA_ERR_ALIGN
+    assert fa.fa_fwd_mod(P, P, P, P, P, 1, 1, 64, 64, 64, 0.125, -3, 0, fa.FA_BF16, None, 0, 0.0, None) == \
+        fa.FA_ERR_MASK
+    assert fa.fa_fwd_mod(P, P, P, P, P, 1, 1, 64, 64, 96, 0.125, -1, 0, fa.FA_BF16, None, 9, 0.0, None) == \
+        fa.FA_ERR_HEADDIM
+    assert fa.fa_fwd_mod(P, P, P, P, P, 0, 1, 64, 64, 64, 0.125, -1, 0, fa.FA_BF16, None, fa.FA_MOD_ALIBI, 0.0,
+                         None) == fa.FA_OK
 
 
 def test_empty_problems_need_no_device():

@@ -35,9 +35,14 @@ def run_gpu(w: synth.Workload, inp: synth.Inputs, q=None, k=None, v=None):
     k = inp.k.to(DEV) if k is None else k
     v = inp.v.to(DEV) if v is None else v
     descales = (inp.descale_q, inp.descale_k, inp.descale_v) if w.in_dtype == "e4m3" else None
+    mod = {}
+    if w.score_mod is not None:
+        mod = dict(score_mod=w.score_mod, softcap=w.softcap)
+        if w.score_mod == "alibi":
+            mod["alibi"] = torch.tensor(synth.alibi_slopes(w.H), dtype=torch.float32, device=DEV)
     o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window,
                           out_dtype=OUT_T[w.out_dtype], descales=descales,
-                          window_left=w.window_left, window_right=w.window_right)
+                          window_left=w.window_left, window_right=w.window_right, **mod)
     torch.cuda.synchronize()
     return o, lse
 
@@ -47,6 +52,9 @@ def reference(w, inp, rows=None):
     if w.window_left is not None or w.window_right is not None:
         ext = dict(window_left=-1 if w.window_left is None else w.window_left,
                    window_right=-1 if w.window_right is None else w.window_right)
+    if w.score_mod is not None:
+        ext.update(score_mod=w.score_mod, softcap=w.softcap,
+                   alibi_slopes=synth.alibi_slopes(w.H) if w.score_mod == "alibi" else None)
     return oracle.attention(inp.q, inp.k, inp.v, w.scale, w.causal, w.window,
                             descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows, **ext)
 
@@ -113,7 +121,7 @@ def test_workload_full(name):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-@pytest.mark.parametrize("name", ["c3", "c4c", "c4w", "c5", "c3sw"])
+@pytest.mark.parametrize("name", ["c3", "c4c", "c4w", "c5", "c3sw", "c3sc", "c3al"])
 def test_workload_full_size_sampled_rows(name):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w)
@@ -256,6 +264,75 @@ def test_sliding_window_zero_queries_average_the_window():
         mean = vb[:, :, lo:hi].double().mean(dim=2)
         assert (o[:, :, i].double().cpu() - mean).abs().max().item() <= 1e-2
         assert abs(lse[0, 0, i].item() - math.log(hi - lo)) <= 1e-4 * max(1.0, math.log(hi - lo))
+
+
+# ----------------------------------------------------- score modifiers
+
+MOD_CASES = [("softcap", 50.0), ("softcap", 2.0), ("softcap", 0.5), ("alibi", 0.0)]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 3, 300, 300), (1, 2, 200, 333), (2, 2, 333, 200)])
+@pytest.mark.parametrize("mask", [(True, 0, None, None), (False, 0, None, None), (True, 100, None, None),
+                                  (False, 0, 40, 40)])
+@pytest.mark.parametrize("mod,cap", MOD_CASES)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32")])
+def test_score_mods_small_shapes(B, H, Nq, Nk, mask, mod, cap, D, din, dout):
+    causal, window, wl, wr = mask
+    seed = 5000 + B * 7 + H * 13 + Nq * 3 + Nk + D + int(cap * 10) + (17 if causal else 0) + window
+    w = synth.small_workload(f"mod_{mod}{cap}_B{B}H{H}q{Nq}k{Nk}D{D}m{mask}_{din}_{dout}", B, H, Nq, Nk, D, causal,
+                             window, din, dout, seed, window_left=wl, window_right=wr, score_mod=mod, softcap=cap)
+    inp = synth.make_inputs(w)
+    if mod == "softcap" and cap <= 2.0:
+        # larger scores, so the cap bends them
+        inp = synth.Inputs((inp.q.double() * 3.0).to(inp.q.dtype), inp.k, inp.v)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("mod,cap", [("softcap", 1.0), ("alibi", 0.0)])
+def test_score_mods_with_two_query_blocks_per_wave(monkeypatch, mod, cap):
+    monkeypatch.setenv("FA_TILE_QB", "2")
+    w = synth.small_workload(f"mod_qb2_{mod}", 1, 3, 700, 700, 64, True, 0, "bf16", "bf16", 5500,
+                             score_mod=mod, softcap=cap)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+def test_alibi_with_zero_slopes_is_bitwise_plain_attention():
+    w = synth.small_workload("alibi0", 1, 2, 333, 333, 64, True, 0, "bf16", "bf16", 5600)
+    inp = synth.make_inputs(w)
+    q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
+    o0, l0 = fa.attention(q, k, v, scale=w.scale, causal=True)
+    o1, l1 = fa.attention(q, k, v, scale=w.scale, causal=True, score_mod="alibi",
+                          alibi=torch.zeros(2, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
+
+
+@pytest.mark.parametrize("mod,cap", [("softcap", 3.0), ("alibi", 0.0)])
+def test_score_mod_masked_keys_are_reproduced_exactly(mod, cap):
+    N, t = 400, 150
+    w = synth.small_workload("mod_mask_exact", 1, 2, N, N, 64, True, 0, "bf16", "bf16", 5700, score_mod=mod,
+                             softcap=cap)
+    inp = synth.make_inputs(w)
+    o1, l1 = run_gpu(w, inp)
+    k2, v2 = inp.k.clone(), inp.v.clone()
+    big = (torch.randn(1, 2, N - t, 64) * 100).to(k2.dtype)
+    k2[:, :, t:] = big
+    v2[:, :, t:] = big
+    o2, l2 = run_gpu(w, inp, k=k2.to(DEV), v=v2.to(DEV))
+    assert torch.equal(o1[:, :, :t].cpu().view(torch.uint8), o2[:, :, :t].cpu().view(torch.uint8))
+    assert torch.equal(l1[:, :, :t].cpu(), l2[:, :, :t].cpu())
+
+
+def test_score_mod_with_e4m3_is_rejected():
+    q = torch.zeros(1, 1, 64, 128, device=DEV).to(torch.float8_e4m3fn)
+    with pytest.raises(fa.FaError):
+        fa.attention(q, q, q, causal=True, score_mod="softcap", softcap=30.0)
 
 
 # ----------------------------------------------------------- edge cases
