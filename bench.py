@@ -138,7 +138,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw c3sc c3al")
+    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw c3sc c3al c6")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (to scale the FETCH_SIZE/WRITE_SIZE "
@@ -177,6 +177,13 @@ def main():
         mod = dict(score_mod=w.score_mod, softcap=w.softcap)
         if w.score_mod == "alibi":
             mod["alibi"] = torch.tensor(synth.alibi_slopes(w.H), dtype=torch.float32, device=dev)
+    n_splits = 1
+    if w.splitkv:
+        code = fa.dtype_code(q.dtype, out_t)
+        n_splits = fa.splitkv_num_splits(w.B, w.H, w.Nq, w.Nk, w.D, code)
+        ws = torch.empty(max(16, fa.splitkv_workspace_bytes(w.B, w.H, w.Nq, w.D, n_splits)), dtype=torch.uint8,
+                         device=dev)
+        mod = dict(num_splits=n_splits, workspace=ws)
 
     def step():
         fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window, out=o, lse=lse,
@@ -226,8 +233,24 @@ def main():
                      "timing": "HIP events on the launch stream, mean over the timed steps"},
         "wall_s_timed_region": round(wall, 4),
     }
+    if w.splitkv:
+        # A decode step reads the whole K/V once for a handful of queries: HBM
+        # bound. The time covers both kernels of the call (splits and merge).
+        gbs = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
+        res.update({
+            "metric": f"attention decode GB/s (algorithmic HBM bytes / time), {w.name}",
+            "value": round(gbs, 1), "unit": "GB/s", "num_splits": n_splits,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(w.name),
+                         "kernel": "fa_fwd16_kernel + fa_combine_kernel",
+                         "algorithmic_hbm_bytes": algorithmic_bytes(w), "flop_per_launch": fl,
+                         "timing": "HIP events on the launch stream, mean over the timed steps"},
+        })
+        res.pop("pct_mfma_peak", None)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp)
+        if w.splitkv:
+            res["cpu_baseline"]["note"] = "TFLOP/s of the oracle on sampled rows"
     print(json.dumps(res), flush=True)
 
 

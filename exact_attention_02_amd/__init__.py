@@ -26,8 +26,9 @@ FA_ERR_MASK, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_DEVICE, FA_ERR_LAUNCH = 5, 6, 7,
 FA_ERR_MOD = 10
 FA_MOD_NONE, FA_MOD_SOFTCAP, FA_MOD_ALIBI = 0, 1, 2
 
-EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_mod", "fa_status_str", "fa_plan_grid", "fa_plan_tile",
-           "fa_plan_block_class", "fa_plan_window_range", "fa_plan_block_class_window")
+EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_mod", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes",
+           "fa_splitkv_num_splits", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class",
+           "fa_plan_window_range", "fa_plan_block_class_window")
 
 _lib = None
 
@@ -56,6 +57,12 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_window.restype = I
     lib.fa_fwd_mod.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, I, F, P]
     lib.fa_fwd_mod.restype = I
+    lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, I, P, LL]
+    lib.fa_fwd_splitkv.restype = I
+    lib.fa_splitkv_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_splitkv_workspace_bytes.restype = LL
+    lib.fa_splitkv_num_splits.argtypes = [I, I, I, I, I, I]
+    lib.fa_splitkv_num_splits.restype = I
     lib.fa_status_str.argtypes = [I]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_plan_grid.argtypes = [I, I, I, I, I, I, I, I, pLL, pI, pI, pI]
@@ -94,6 +101,20 @@ def fa_fwd_mod(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_righ
                score_mod, softcap=0.0, alibi_slopes=None) -> int:
     return load().fa_fwd_mod(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(window_left), int(window_right), dtype,
                              stream, int(score_mod), float(softcap), alibi_slopes)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_right, dtype, stream,
+                   num_splits, workspace, workspace_bytes) -> int:
+    return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(window_left), int(window_right), dtype,
+                                 stream, int(num_splits), workspace, int(workspace_bytes))
+
+
+def splitkv_workspace_bytes(B, H, Nq, D, num_splits) -> int:
+    return load().fa_splitkv_workspace_bytes(B, H, Nq, D, num_splits)
+
+
+def splitkv_num_splits(B, H, Nq, Nk, D, dtype) -> int:
+    return load().fa_splitkv_num_splits(B, H, Nq, Nk, D, dtype)
 
 
 def alibi_slopes(H: int):
@@ -159,7 +180,7 @@ def dtype_code(in_dtype, out_dtype) -> int:
 
 def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, out_dtype=None,
               descales=None, stream=None, window_left=None, window_right=None,
-              score_mod=None, softcap=0.0, alibi=None):
+              score_mod=None, softcap=0.0, alibi=None, num_splits=None, workspace=None):
     """O [B,H,Nq,D] and LSE [B,H,Nq] (float32) of softmax(scale Q K^T) V via libfa.
 
     q [B,H,Nq,D], k and v [B,H,Nk,D]: contiguous device tensors of one dtype
@@ -172,6 +193,9 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
     score_mod: None, "softcap" (s <- softcap * tanh(s / softcap)) or "alibi"
     (s <- s + slope_h * (j - i')); alibi is a float32 device tensor of H slopes
     (default: alibi_slopes(H)). Score modifiers go through fa_fwd_mod.
+    num_splits: split-KV through fa_fwd_splitkv ("auto": fa_splitkv_num_splits);
+    workspace: a uint8 device tensor of at least splitkv_workspace_bytes(...)
+    bytes (allocated here when None).
     """
     import torch
     B, H, Nq, D = q.shape
@@ -195,6 +219,24 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    if num_splits is not None:
+        if score_mod is not None:
+            raise ValueError("split-KV takes no score modifier")
+        if window_left is not None or window_right is not None:
+            wl = -1 if window_left is None else int(window_left)
+            wr = -1 if window_right is None else int(window_right)
+        else:
+            wl = int(window) - 1 if window > 0 else -1
+            wr = 0 if causal else -1
+        ns = splitkv_num_splits(B, H, Nq, Nk, D, code) if num_splits == "auto" else int(num_splits)
+        need = splitkv_workspace_bytes(B, H, Nq, D, ns)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        st = fa_fwd_splitkv(*ptrs, B, H, Nq, Nk, D, float(scale), wl, wr, code, stream, ns, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size())
+        if st != FA_OK:
+            raise FaError(st, "fa_fwd_splitkv")
+        return out, lse
     if score_mod is not None:
         if window_left is not None or window_right is not None:
             wl = -1 if window_left is None else int(window_left)

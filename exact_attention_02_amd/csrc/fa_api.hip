@@ -86,7 +86,8 @@ bool window_extents(int window_left, int window_right, int Nq, int Nk, int* wl, 
 
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
         float scale, int wl, int wr, int dtype, void* stream, float dq, float dk, float dv,
-        int mod = FA_MOD_NONE, float cap = 0.f, const float* slopes = nullptr) {
+        int mod = FA_MOD_NONE, float cap = 0.f, const float* slopes = nullptr, int n_split = 1,
+        void* workspace = nullptr) {
     DtypeInfo di;
     const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
     if (st != FA_OK) return st;
@@ -101,7 +102,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     const int dst = check_device();
     if (dst != FA_OK) return dst;
 
-    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq, mod);
+    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq, mod, n_split > 1);
     fa::Params p;
     p.q = (const uint8_t*)q;
     p.k = (const uint8_t*)k;
@@ -121,11 +122,15 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.mk1 = (mod == FA_MOD_SOFTCAP) ? 2.f * p.c / cap : 0.f;
     p.mk2 = (mod == FA_MOD_SOFTCAP) ? cap * 1.44269504088896341f : 0.f;
     p.slopes = slopes;
+    p.n_split = n_split;
+    p.ws_o = (float*)workspace;
+    p.ws_lse = workspace ? (float*)workspace + (size_t)B * H * n_split * Nq * D : nullptr;
     if (std::getenv("FA_DEBUG"))
         std::fprintf(stderr, "fa_fwd: in=%d out=%d D=%d kernel=%d nw=%d qb=%d br=%d bc=%d n_qt=%d n_wg=%lld\n",
                      pl.in, pl.out, pl.D, pl.kernel, pl.nw, pl.qb, pl.br, pl.bc, pl.n_qt, pl.n_wg);
     (void)hipGetLastError();  // clear a stale error left by the caller
-    const int err = fa::launch(pl, p, stream);
+    int err = fa::launch(pl, p, stream);
+    if (err == 0 && n_split > 1) err = fa::launch_combine(pl, p, stream);
     return err == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -188,6 +193,48 @@ int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
     }
     return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, 1.f, 1.f, 1.f, score_mod, softcap,
                alibi_slopes);
+}
+
+long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int D, int num_splits) {
+    if (B < 0 || H < 0 || Nq < 0 || D <= 0 || num_splits < 1) return -1;
+    if (num_splits == 1) return 0;
+    const long long rows = (long long)B * H * num_splits * Nq;
+    return rows * D * 4 + rows * 4;
+}
+
+int fa_splitkv_num_splits(int B, int H, int Nq, int Nk, int D, int dtype) {
+    DtypeInfo di;
+    if (check_shape(B, H, Nq, Nk, D, dtype, &di) != FA_OK || di.in == fa::IN_E4M3) return 1;
+    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq, fa::MOD_NONE, true);
+    const long long tiles = ((long long)Nk + pl.bc - 1) / pl.bc;
+    // enough workgroups to fill every CU twice over, with at least 4 key tiles per split
+    const long long want = 512;
+    long long s = pl.n_wg >= want ? 1 : (want + pl.n_wg - 1) / pl.n_wg;
+    if (s > tiles / 4) s = tiles / 4;
+    if (s > 256) s = 256;
+    return s < 1 ? 1 : (int)s;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                   int D, float scale, int window_left, int window_right, int dtype, void* stream, int num_splits,
+                   void* workspace, long long workspace_bytes) {
+    DtypeInfo di;
+    const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
+    if (st != FA_OK) return st;
+    if (di.in == fa::IN_E4M3) return FA_ERR_DTYPE;
+    int wl, wr;
+    if (!window_extents(window_left, window_right, Nq, Nk, &wl, &wr)) return FA_ERR_MASK;
+    if (num_splits < 1 || num_splits > 1024) return FA_ERR_SHAPE;
+    const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq, fa::MOD_NONE, true);
+    if (pl.n_wg * num_splits > 0x7fffffffLL) return FA_ERR_SHAPE;
+    const long long need = fa_splitkv_workspace_bytes(B, H, Nq, D, num_splits);
+    if ((long long)B * H * Nq > 0 && num_splits > 1) {
+        if (!workspace) return FA_ERR_NULL;
+        if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+        if (workspace_bytes < need) return FA_ERR_SHAPE;
+    }
+    return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, 1.f, 1.f, 1.f, FA_MOD_NONE, 0.f,
+               nullptr, num_splits, num_splits > 1 ? workspace : nullptr);
 }
 
 const char* fa_status_str(int status) {

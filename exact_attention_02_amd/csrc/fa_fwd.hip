@@ -419,7 +419,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
 
 // ---------------------------------------------------------------- host side
 
-Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod) {
+Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool pipe16) {
     Plan pl;
     pl.in = in;
     pl.out = out;
@@ -434,7 +434,7 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod) {
         const int f = atoi(e);
         if (f == KERNEL_TILE64 || (f == KERNEL_PIPE16 && in != IN_E4M3)) kernel = f;
     }
-    if (mod != MOD_NONE) kernel = KERNEL_PIPE16;
+    if (mod != MOD_NONE || pipe16) kernel = KERNEL_PIPE16;
     // 64-key-tile kernel: two 32-row query blocks per wave halve LDS traffic
     // per MFMA and the K/V re-reads per query; one block keeps the grid large
     // on small problems and keeps D = 128 within the register file.

@@ -124,14 +124,26 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
     const int g = lane >> 4, cl = lane & 15;   // 16-lane group of the transposing reads
 
     const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
-    int bh, qt;
-    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, &bh, &qt);
+    int bh, qt, split = 0;
+    long long wgid = blockIdx.x;
+    if (p.n_split > 1) {
+        split = (int)(wgid % p.n_split);
+        wgid /= p.n_split;
+    }
+    decode_wg(wgid, p.n_bh, p.n_qt, &bh, &qt);
     const int r0 = qt * BR;
     const int r1 = min(r0 + BR, Nq);
     int kv_lo, kv_hi;
     kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
-    const int t_lo = kv_lo / BC;
-    const int t_hi = (kv_hi > kv_lo) ? (kv_hi + BC - 1) / BC : t_lo;
+    int tl = kv_lo / BC, th = (kv_hi > kv_lo) ? (kv_hi + BC - 1) / BC : kv_lo / BC;
+    if (p.n_split > 1) {
+        // split s takes tiles [tl + nt*s/S, tl + nt*(s+1)/S) of the workgroup's range
+        const long long nt = th - tl;
+        const int a = tl + (int)(nt * split / p.n_split), b = tl + (int)(nt * (split + 1) / p.n_split);
+        tl = a;
+        th = b;
+    }
+    const int t_lo = tl, t_hi = th;
     const int w0 = r0 + wave * QW;
     const int w1 = min(w0 + QW, Nq);
 
@@ -662,7 +674,33 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
         }
     }
 
-    // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
+    // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l); a split writes both
+    // in fp32 to its slice of the workspace instead
+    if (p.n_split > 1) {
+        const size_t sl = (size_t)bh * p.n_split + split;
+        float* wo = p.ws_o + sl * Nq * D;
+        float* wlp = p.ws_lse + sl * Nq;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float lt = sum_halves(lh[qb]);
+            const int i = w0 + 32 * qb + l32;
+            if (i < w1) {
+                const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+                uint8_t* orow = (uint8_t*)(wo + (size_t)i * D);
+#pragma unroll
+                for (int db = 0; db < ND; ++db)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const f32x16& a = oacc[db][qb];
+                        const int d = 32 * db + 8 * r4 + 4 * hh;
+                        Out<OUT_F32>::store4(orow + d * 4, a[4 * r4] * inv, a[4 * r4 + 1] * inv, a[4 * r4 + 2] * inv,
+                                             a[4 * r4 + 3] * inv);
+                    }
+                if (hh == 0) wlp[i] = (lt > 0.f) ? (m[qb] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
+            }
+        }
+        return;
+    }
     uint8_t* op = p.o + (size_t)bh * Nq * D * Out<OUT>::EB;
     float* lp = p.lse + (size_t)bh * Nq;
 #pragma unroll
@@ -690,7 +728,8 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
 
 template <int IN, int OUT, int D, int NW, int QB, int MOD>
 static int launch16_one(const Plan& pl, const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((fa_fwd16_kernel<IN, OUT, D, NW, QB, MOD>), dim3((unsigned)pl.n_wg), dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((fa_fwd16_kernel<IN, OUT, D, NW, QB, MOD>), dim3((unsigned)(pl.n_wg * p.n_split)), dim3(64 * NW),
+                       0, s, p);
     return (int)hipGetLastError();
 }
 
@@ -708,6 +747,58 @@ static int launch16_io(const Plan& pl, const Params& p, hipStream_t s) {
         return launch16_mod<IN, OUT, 64, 4, 1>(pl, p, s);
     }
     return launch16_mod<IN, OUT, 128, 8, 1>(pl, p, s);
+}
+
+// Merge of the splits of each row (the online-softmax identity of the
+// FLASHLIGHT summary, Methodology item 3, across splits): with each split's
+// O_s (normalised by its own sum) and LSE_s,
+//   LSE = ln sum_s e^(LSE_s),   O = sum_s e^(LSE_s - LSE) O_s.
+// One thread per 4 consecutive columns of a row; rows whose splits all saw no
+// key get O = 0 and LSE = -inf.
+template <int OUT>
+__global__ __launch_bounds__(256) void fa_combine_kernel(Params p, int D) {
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    const int q4 = D / 4;
+    const long long rows = (long long)p.n_bh * p.Nq;
+    if (t >= rows * q4) return;
+    const long long row = t / q4;
+    const int d = (int)(t % q4) * 4;
+    const long long bh = row / p.Nq, i = row % p.Nq;
+    const int S = p.n_split;
+    const float* wl = p.ws_lse + (size_t)bh * S * p.Nq + i;
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, wl[(size_t)s * p.Nq]);
+    uint8_t* orow = p.o + (size_t)row * D * Out<OUT>::EB;
+    if (mx == -INFINITY) {
+        Out<OUT>::store4(orow + d * Out<OUT>::EB, 0.f, 0.f, 0.f, 0.f);
+        if (d == 0) p.lse[row] = -INFINITY;
+        return;
+    }
+    float wsum = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    const float* wo = p.ws_o + ((size_t)bh * S * p.Nq + i) * D + d;
+    for (int s = 0; s < S; ++s) {
+        const float w = expf(wl[(size_t)s * p.Nq] - mx);
+        const float4 v = *reinterpret_cast<const float4*>(wo + (size_t)s * p.Nq * D);
+        wsum += w;
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
+        o2 = fmaf(w, v.z, o2);
+        o3 = fmaf(w, v.w, o3);
+    }
+    const float inv = 1.f / wsum;
+    Out<OUT>::store4(orow + d * Out<OUT>::EB, o0 * inv, o1 * inv, o2 * inv, o3 * inv);
+    if (d == 0) p.lse[row] = mx + logf(wsum);
+}
+
+int launch_combine(const Plan& pl, const Params& p, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    const long long n = (long long)p.n_bh * p.Nq * (pl.D / 4);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (blocks == 0) return 0;
+    if (pl.out == OUT_F16) hipLaunchKernelGGL((fa_combine_kernel<OUT_F16>), dim3(blocks), dim3(256), 0, s, p, pl.D);
+    else if (pl.out == OUT_BF16) hipLaunchKernelGGL((fa_combine_kernel<OUT_BF16>), dim3(blocks), dim3(256), 0, s, p, pl.D);
+    else hipLaunchKernelGGL((fa_combine_kernel<OUT_F32>), dim3(blocks), dim3(256), 0, s, p, pl.D);
+    return (int)hipGetLastError();
 }
 
 int launch16(const Plan& pl, const Params& p, void* stream) {

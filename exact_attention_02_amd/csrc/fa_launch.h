@@ -28,6 +28,12 @@ struct Params {
     int mod;        // MOD_NONE, MOD_SOFTCAP or MOD_ALIBI (16-bit kernel only)
     float mk1, mk2; // softcap constants: 2 * c / cap and cap * log2(e)
     const float* slopes;  // ALiBi: [H] device array of per-head slopes
+    // Split-KV: each head's key tiles are split into n_split contiguous ranges,
+    // one workgroup each; a split writes its O (divided by its own sum) and its
+    // LSE in fp32 to ws_o [n_bh, n_split, Nq, D] and ws_lse [n_bh, n_split, Nq].
+    int n_split;    // 1: no split (O and LSE go to o and lse directly)
+    float* ws_o;
+    float* ws_lse;
     int n_qt;       // query tiles per head
     float c;        // scale * descale_q * descale_k * log2(e): scores in base-2 units
     float out_mul;  // descale_v (1 unless e4m3)
@@ -46,12 +52,15 @@ struct Plan {
 };
 
 // Picks the tile shape for a problem. Pure host arithmetic.
-// mod != MOD_NONE needs the pipelined kernel (the only one with score modifiers).
-Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod = MOD_NONE);
+// mod != MOD_NONE and pipe16 (split-KV) need the pipelined kernel, the only one
+// with score modifiers and splits.
+Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod = MOD_NONE, bool pipe16 = false);
 
 // Enqueues the kernel chosen by `plan` on `stream`; returns the hipError_t
 // value of hipGetLastError() after the launch (0 on success).
 int launch(const Plan& plan, const Params& p, void* stream);
 int launch16(const Plan& plan, const Params& p, void* stream);
+// The merge of the splits (p.n_split > 1): O and LSE from ws_o and ws_lse.
+int launch_combine(const Plan& plan, const Params& p, void* stream);
 
 }  // namespace fa

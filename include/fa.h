@@ -149,6 +149,36 @@ int fa_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
                int window_left, int window_right, int dtype, void* stream,
                int score_mod, float softcap, const float* alibi_slopes);
 
+/*
+ * Split-KV (decode-shaped problems, Nq << Nk): fa_fwd_splitkv splits the key
+ * range of every (batch, head, query tile) into num_splits contiguous parts,
+ * one workgroup each, so that a few long rows still spread over the whole
+ * chip. Each part writes its partial O (normalised by its own sum) and its
+ * LSE in fp32 to `workspace`; a second kernel on the same stream merges them
+ * with the online-softmax identity (gist.science summary of FLASHLIGHT,
+ * Methodology item 3):
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) * O_s.
+ * The result is the same attention as fa_fwd_window up to rounding.
+ *
+ * fa_splitkv_workspace_bytes: bytes of workspace fa_fwd_splitkv needs
+ *   (B*H*num_splits*Nq*(D+1)*4; 0 for num_splits == 1), or -1 for bad sizes.
+ * fa_splitkv_num_splits: a split count that gives about 512 workgroups,
+ *   with at least 4 key tiles of 64 per split (1 when splitting does not pay
+ *   or the arguments are invalid).
+ * fa_fwd_splitkv: as fa_fwd_window for fp16/bf16 inputs (FA_ERR_DTYPE for
+ *   FA_E4M3). workspace: device memory of at least workspace_bytes >=
+ *   fa_splitkv_workspace_bytes(...), 16-byte aligned, owned by the caller,
+ *   overwritten by the call; it must not be shared by calls that may run
+ *   concurrently. num_splits in [1, 1024] (FA_ERR_SHAPE otherwise, or when the
+ *   workspace is too small); num_splits == 1 needs no workspace.
+ */
+long long fa_splitkv_workspace_bytes(int B, int H, int Nq, int D, int num_splits);
+int fa_splitkv_num_splits(int B, int H, int Nq, int Nk, int D, int dtype);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int D, float scale,
+                   int window_left, int window_right, int dtype, void* stream,
+                   int num_splits, void* workspace, long long workspace_bytes);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_str(int status);
 

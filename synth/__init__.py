@@ -159,6 +159,7 @@ class Workload:
     # "alibi" (s <- s + slope_h * (j - i') with the slopes alibi_slopes(H)).
     score_mod: Optional[str] = None
     softcap: float = 0.0
+    splitkv: bool = False   # run through split-KV with the recommended split count
 
     def __post_init__(self):
         if self.scale == 0.0:
@@ -189,6 +190,10 @@ WORKLOADS = {
                      score_mod="softcap", softcap=50.0),
     "c3al": Workload("c3_causal_alibi_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, True, 0, "bf16", "bf16", 3,
                      score_mod="alibi"),
+    # Decode: one new query per sequence against a long context (LLaMa-3.2-1B
+    # serving: 32 heads of 64), run with split-KV. Seed 6.
+    "c6": Workload("c6_decode_B8H32Nq1Nk16384D64_bf16", 8, 32, 1, 16384, 64, True, 0, "bf16", "bf16", 6,
+                   splitkv=True),
 }
 
 

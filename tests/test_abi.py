@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+(?:\s+\w+)*\**\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_function():
@@ -103,6 +103,27 @@ def test_mod_entry_checks_modifier_and_parameters():
         fa.FA_ERR_HEADDIM
     assert fa.fa_fwd_mod(P, P, P, P, P, 0, 1, 64, 64, 64, 0.125, -1, 0, fa.FA_BF16, None, fa.FA_MOD_ALIBI, 0.0,
                          None) == fa.FA_OK
+
+
+def test_splitkv_entry_checks_and_workspace_size():
+    assert fa.splitkv_workspace_bytes(2, 3, 5, 64, 1) == 0
+    assert fa.splitkv_workspace_bytes(2, 3, 5, 64, 4) == 2 * 3 * 4 * 5 * (64 + 1) * 4
+    assert fa.splitkv_workspace_bytes(2, 3, 5, 64, 0) == -1
+    assert fa.splitkv_num_splits(1, 32, 1, 32768, 64, fa.FA_BF16) > 1
+    assert fa.splitkv_num_splits(4, 12, 8192, 8192, 64, fa.FA_BF16) == 1
+    assert fa.splitkv_num_splits(1, 1, 1, 100, 64, fa.FA_BF16) == 1      # too few key tiles to split
+    assert fa.splitkv_num_splits(1, 1, 1, 100000, 64, fa.FA_E4M3) == 1
+    need = fa.splitkv_workspace_bytes(1, 2, 1, 64, 8)
+    args = (P, P, P, P, P, 1, 2, 1, 4096, 64, 0.125, -1, 0)
+    assert fa.fa_fwd_splitkv(*args, fa.FA_BF16, None, 0, P, need) == fa.FA_ERR_SHAPE
+    assert fa.fa_fwd_splitkv(*args, fa.FA_BF16, None, 2000, P, need) == fa.FA_ERR_SHAPE
+    assert fa.fa_fwd_splitkv(*args, fa.FA_E4M3, None, 8, P, need) == fa.FA_ERR_DTYPE
+    assert fa.fa_fwd_splitkv(*args, fa.FA_BF16, None, 8, None, need) == fa.FA_ERR_NULL
+    assert fa.fa_fwd_splitkv(*args, fa.FA_BF16, None, 8, P + 8, need) == fa.FA_ERR_ALIGN
+    assert fa.fa_fwd_splitkv(*args, fa.FA_BF16, None, 8, P, need - 1) == fa.FA_ERR_SHAPE
+    assert fa.fa_fwd_splitkv(P, P, P, P, P, 1, 2, 1, 4096, 64, 0.125, -2, 0, fa.FA_BF16, None, 8, P, need) == \
+        fa.FA_ERR_MASK
+    assert fa.fa_fwd_splitkv(P, P, P, P, P, 0, 2, 1, 4096, 64, 0.125, -1, 0, fa.FA_BF16, None, 8, None, 0) == fa.FA_OK
 
 
 def test_empty_problems_need_no_device():

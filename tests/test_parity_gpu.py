@@ -40,6 +40,8 @@ def run_gpu(w: synth.Workload, inp: synth.Inputs, q=None, k=None, v=None):
         mod = dict(score_mod=w.score_mod, softcap=w.softcap)
         if w.score_mod == "alibi":
             mod["alibi"] = torch.tensor(synth.alibi_slopes(w.H), dtype=torch.float32, device=DEV)
+    if w.splitkv:
+        mod["num_splits"] = "auto"
     o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window,
                           out_dtype=OUT_T[w.out_dtype], descales=descales,
                           window_left=w.window_left, window_right=w.window_right, **mod)
@@ -112,7 +114,7 @@ def sample_rows(w, n_random=1500, seed=0):
 
 # ------------------------------------------------------ the five workloads
 
-@pytest.mark.parametrize("name", ["c1", "c2"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c6"])
 def test_workload_full(name):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w)
@@ -333,6 +335,64 @@ def test_score_mod_with_e4m3_is_rejected():
     q = torch.zeros(1, 1, 64, 128, device=DEV).to(torch.float8_e4m3fn)
     with pytest.raises(fa.FaError):
         fa.attention(q, q, q, causal=True, score_mod="softcap", softcap=30.0)
+
+
+# ------------------------------------------------------------ split-KV
+
+def run_split(w, inp, num_splits):
+    q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
+    ext = {}
+    if w.window_left is not None or w.window_right is not None:
+        ext = dict(window_left=w.window_left, window_right=w.window_right)
+    o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window, out_dtype=OUT_T[w.out_dtype],
+                          num_splits=num_splits, **ext)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", [(2, 3, 1, 4097), (1, 4, 7, 3000), (1, 2, 33, 2500), (1, 2, 130, 1000),
+                                       (3, 1, 1, 65)])
+@pytest.mark.parametrize("splits", [1, 2, 7, 16, 64])
+@pytest.mark.parametrize("mask", [(True, 0, None, None), (False, 0, None, None), (True, 500, None, None),
+                                  (False, 0, 300, 40)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D):
+    causal, window, wl, wr = mask
+    w = synth.small_workload(f"split{splits}_B{B}H{H}q{Nq}k{Nk}D{D}m{mask}", B, H, Nq, Nk, D, causal, window,
+                             "bf16", "bf16", 6000 + B + H * 3 + Nq * 7 + Nk + D + splits,
+                             window_left=wl, window_right=wr)
+    inp = synth.make_inputs(w)
+    o, lse = run_split(w, inp, splits)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("din,dout", [("f16", "f16"), ("f16", "f32"), ("bf16", "f32")])
+def test_splitkv_dtypes(din, dout):
+    w = synth.small_workload(f"split_dt_{din}_{dout}", 2, 4, 3, 5000, 64, True, 0, din, dout, 6100)
+    inp = synth.make_inputs(w)
+    o, lse = run_split(w, inp, "auto")
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+def test_one_split_is_bitwise_the_plain_call():
+    w = synth.small_workload("split_one", 2, 3, 5, 3000, 64, True, 0, "bf16", "bf16", 6200)
+    inp = synth.make_inputs(w)
+    o1, l1 = run_split(w, inp, 1)
+    o0, l0 = run_gpu(w, inp)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
+
+
+def test_splits_without_keys_give_zero_and_minus_inf():
+    # window (0, 0) with Nq > Nk: the first rows see nothing, and most splits of a row are empty
+    w = synth.small_workload("split_empty", 1, 2, 300, 200, 64, False, 0, "bf16", "bf16", 6300,
+                             window_left=0, window_right=0)
+    inp = synth.make_inputs(w)
+    o, lse = run_split(w, inp, 8)
+    Oref, Lref = reference(w, inp)
+    assert torch.isneginf(Lref[0, 0, :100]).all()
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
 # ----------------------------------------------------------- edge cases
