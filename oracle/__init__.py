@@ -49,6 +49,9 @@ def load(path: str = _LIB):
     fm.argtypes = [P, P, P, P, P, L, L, L, L, L, ctypes.c_double, L, L, ctypes.c_int, ctypes.c_double, P, P, L,
                    ctypes.c_int]
     fm.restype = ctypes.c_int
+    fb = lib.oracle_attn_bwd
+    fb.argtypes = [P, P, P, P, P, P, P, L, L, L, L, L, ctypes.c_double, L, L, ctypes.c_int]
+    fb.restype = ctypes.c_int
     return lib
 
 
@@ -164,6 +167,29 @@ def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
         O[sel] = Oh
         LSE[sel] = Lh
     return O, LSE
+
+
+def attention_bwd(q, k, v, dout, scale, window_left=-1, window_right=-1, threads=None, lib=None):
+    """float64 (dQ, dK, dV) of O = softmax(scale Q K^T) V under the extents mask, given dO.
+
+    q, dout [B,H,Nq,D]; k, v [B,H,Nk,D] (any float dtype, decoded exactly);
+    window_left/right as in attention() (-1: open side). scale is used as
+    float64(fp32(scale)).
+    """
+    lib = lib or _get()
+    threads = threads or default_threads()
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    scale64 = float(torch.tensor(scale, dtype=torch.float32))
+    Q, K, V, dO = decode(q), decode(k), decode(v), decode(dout)
+    dQ = torch.empty((B, H, Nq, D), dtype=torch.float64)
+    dK = torch.empty((B, H, Nk, D), dtype=torch.float64)
+    dV = torch.empty((B, H, Nk, D), dtype=torch.float64)
+    rc = lib.oracle_attn_bwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dO.data_ptr(), dQ.data_ptr(), dK.data_ptr(),
+                             dV.data_ptr(), B, H, Nq, Nk, D, scale64, int(window_left), int(window_right), threads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_bwd returned {rc}")
+    return dQ, dK, dV
 
 
 def visible_keys(i: int, Nq: int, Nk: int, causal: bool, window: int):

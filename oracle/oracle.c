@@ -230,3 +230,113 @@ static int run_job(job_t *jbp, int nthreads)
     pthread_mutex_destroy(&jb.lock);
     return jb.bad ? 1 : 0;
 }
+
+/*
+ * Backward pass (the gradients of O with respect to Q, K, V, contracted with
+ * an upstream gradient dO). The pages' method recomputes the softmax weights
+ * in the backward pass from Q, K and the stored normaliser instead of keeping
+ * them (aiinarabic.com flash-attention page, the recomputation paragraph);
+ * what it computes is the plain derivative of O = softmax(scale Q K^T) V:
+ *   P_j   = exp(s_j - LSE)                 the softmax row, s_j = scale q_i.k_j
+ *   dV_j += P_j dO_i
+ *   dP_j  = dO_i . V_j
+ *   Dv    = sum_j P_j dP_j                  (= dO_i . O_i)
+ *   dS_j  = P_j (dP_j - Dv)                 (the softmax Jacobian applied)
+ *   dQ_i  = scale sum_j dS_j K_j
+ *   dK_j += scale dS_j Q_i
+ * over the visible keys J_i of the extents mask (wl, wr; negative = open).
+ * Rows are taken in order within a head; heads run in parallel threads.
+ */
+typedef struct {
+    const double *q, *k, *v, *dout;
+    double *dq, *dk, *dv;
+    long B, H, Nq, Nk, D, wl, wr;
+    double scale;
+    long next;
+    pthread_mutex_t lock;
+} bjob_t;
+
+static void bwd_head(const bjob_t *jb, long bh, double *s, double *dp)
+{
+    const long D = jb->D, Nq = jb->Nq, Nk = jb->Nk;
+    const double *Q = jb->q + bh * Nq * D, *K = jb->k + bh * Nk * D, *V = jb->v + bh * Nk * D;
+    const double *dO = jb->dout + bh * Nq * D;
+    double *dQ = jb->dq + bh * Nq * D, *dK = jb->dk + bh * Nk * D, *dV = jb->dv + bh * Nk * D;
+    for (long x = 0; x < Nq * D; ++x) dQ[x] = 0.0;
+    for (long x = 0; x < Nk * D; ++x) { dK[x] = 0.0; dV[x] = 0.0; }
+    for (long i = 0; i < Nq; ++i) {
+        const long ip = i + Nk - Nq;
+        long lo = 0, hi = Nk;
+        if (jb->wl >= 0 && ip - jb->wl > 0) lo = ip - jb->wl;
+        if (jb->wr >= 0 && ip + jb->wr + 1 < Nk) hi = ip + jb->wr + 1;
+        if (hi <= lo) continue;
+        const double *qi = Q + i * D, *doi = dO + i * D;
+        /* the softmax row, materialised */
+        double m = -INFINITY;
+        for (long j = lo; j < hi; ++j) {
+            double dot = 0.0;
+            for (long d = 0; d < D; ++d) dot += qi[d] * K[j * D + d];
+            s[j - lo] = dot * jb->scale;
+            if (s[j - lo] > m) m = s[j - lo];
+        }
+        double l = 0.0;
+        for (long j = lo; j < hi; ++j) l += exp(s[j - lo] - m);
+        const double lse = m + log(l);
+        double dv_row = 0.0;
+        for (long j = lo; j < hi; ++j) {
+            const double p = exp(s[j - lo] - lse);
+            s[j - lo] = p;
+            double x = 0.0;
+            for (long d = 0; d < D; ++d) x += doi[d] * V[j * D + d];
+            dp[j - lo] = x;
+            dv_row += p * x;
+            for (long d = 0; d < D; ++d) dV[j * D + d] += p * doi[d];
+        }
+        for (long j = lo; j < hi; ++j) {
+            const double ds = s[j - lo] * (dp[j - lo] - dv_row);
+            for (long d = 0; d < D; ++d) {
+                dQ[i * D + d] += jb->scale * ds * K[j * D + d];
+                dK[j * D + d] += jb->scale * ds * qi[d];
+            }
+        }
+    }
+}
+
+static void *bwd_worker(void *arg)
+{
+    bjob_t *jb = (bjob_t *)arg;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(jb->Nk > 0 ? jb->Nk : 1));
+    double *dp = (double *)malloc(sizeof(double) * (size_t)(jb->Nk > 0 ? jb->Nk : 1));
+    for (;;) {
+        pthread_mutex_lock(&jb->lock);
+        const long bh = jb->next++;
+        pthread_mutex_unlock(&jb->lock);
+        if (bh >= jb->B * jb->H) break;
+        bwd_head(jb, bh, s, dp);
+    }
+    free(s);
+    free(dp);
+    return NULL;
+}
+
+/* dQ [B,H,Nq,D], dK and dV [B,H,Nk,D] of the extents-masked attention. */
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv, long B, long H, long Nq, long Nk, long D,
+                    double scale, long wl, long wr, int nthreads)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D <= 0 || nthreads <= 0) return -1;
+    bjob_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.q = q; jb.k = k; jb.v = v; jb.dout = dout; jb.dq = dq; jb.dk = dk; jb.dv = dv;
+    jb.B = B; jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.D = D; jb.wl = wl; jb.wr = wr; jb.scale = scale;
+    pthread_mutex_init(&jb.lock, NULL);
+    if (nthreads > 256) nthreads = 256;
+    pthread_t tid[256];
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&tid[started], NULL, bwd_worker, &jb) == 0) ++started;
+    bwd_worker(&jb);
+    for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
+    pthread_mutex_destroy(&jb.lock);
+    return 0;
+}

@@ -270,6 +270,66 @@ def test_softcap_bruteforce_50_digits(Nq, Nk, D, causal, cap):
             assert abs(O[0, 0, i, d].item() - float(ref)) <= 1e-13
 
 
+# ------------------------------------------------------------- backward
+
+def fwd_loss(Q, K, V, dO, scale, wl, wr):
+    """sum(dO * O) through the (pinned) forward oracle."""
+    O, _ = oracle.attention(Q, K, V, scale, window_left=wl, window_right=wr)
+    return float((O * dO).sum())
+
+
+@pytest.mark.parametrize("Nq,Nk,D,wl,wr", [(6, 6, 8, -1, 0), (5, 9, 8, -1, -1), (9, 5, 8, -1, 0), (8, 8, 4, 2, 1),
+                                           (7, 7, 16, 0, 0)])
+def test_bwd_matches_finite_differences_of_the_forward(Nq, Nk, D, wl, wr):
+    B, H = 1, 2
+    Q, K, V = rnd((B, H, Nq, D), 41, 0), rnd((B, H, Nk, D), 41, 1), rnd((B, H, Nk, D), 41, 2)
+    dO = rnd((B, H, Nq, D), 41, 3)
+    scale = 0.7
+    dQ, dK, dV = oracle.attention_bwd(Q, K, V, dO, scale, wl, wr)
+    h = 1e-5
+    for X, G, tid in [(Q, dQ, 4), (K, dK, 5), (V, dV, 6)]:
+        E = rnd(X.shape, 42, tid)
+        X0 = X.clone()
+        X.add_(h * E)
+        fp = fwd_loss(Q, K, V, dO, scale, wl, wr)
+        X.copy_(X0 - h * E)
+        fm = fwd_loss(Q, K, V, dO, scale, wl, wr)
+        X.copy_(X0)
+        fd = (fp - fm) / (2 * h)
+        an = float((G * E).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (tid, fd, an)
+
+
+@pytest.mark.parametrize("Nq,Nk,D,wl,wr", [(33, 33, 64, -1, 0), (40, 70, 64, -1, -1), (70, 40, 128, -1, 0),
+                                           (64, 64, 64, 10, 10), (50, 50, 64, 5, 0)])
+def test_bwd_matches_torch_autograd_float64(Nq, Nk, D, wl, wr):
+    B, H = 1, 2
+    Q, K, V = rnd((B, H, Nq, D), 43, 0), rnd((B, H, Nk, D), 43, 1), rnd((B, H, Nk, D), 43, 2)
+    dO = rnd((B, H, Nq, D), 43, 3)
+    scale = 1.0 / math.sqrt(D)
+    s32 = float(torch.tensor(scale, dtype=torch.float32))
+    dQ, dK, dV = oracle.attention_bwd(Q, K, V, dO, scale, wl, wr)
+    keep = mask_matrix_window(Nq, Nk, wl, wr)
+    Qg, Kg, Vg = (t.clone().requires_grad_(True) for t in (Q, K, V))
+    S = torch.matmul(Qg, Kg.transpose(-1, -2)) * s32
+    P = torch.softmax(S.masked_fill(~keep, -math.inf), dim=-1)
+    P = torch.nan_to_num(P, nan=0.0)   # rows with no visible key contribute nothing
+    O = torch.matmul(P, Vg)
+    O.backward(dO)
+    assert torch.allclose(dQ, Qg.grad, rtol=0, atol=1e-12)
+    assert torch.allclose(dK, Kg.grad, rtol=0, atol=1e-12)
+    assert torch.allclose(dV, Vg.grad, rtol=0, atol=1e-12)
+
+
+def test_bwd_uniform_weights_give_mean_upstream_for_dv():
+    """Q = 0 without a mask: every weight is 1/Nk, so dV_j is the mean of dO over the rows."""
+    Nq, Nk, D = 30, 20, 64
+    Q = torch.zeros(1, 1, Nq, D, dtype=torch.float64)
+    K, V, dO = rnd((1, 1, Nk, D), 44, 1), rnd((1, 1, Nk, D), 44, 2), rnd((1, 1, Nq, D), 44, 3)
+    dQ, dK, dV = oracle.attention_bwd(Q, K, V, dO, 0.125, -1, -1)
+    assert torch.allclose(dV[0, 0], dO[0, 0].sum(0, keepdim=True).expand(Nk, D) / Nk, atol=1e-13)
+
+
 # ------------------------------------------------------------- closed forms
 
 @pytest.mark.parametrize("Nq,Nk,causal,window", [(40, 40, False, 0), (40, 40, True, 0), (40, 40, True, 7), (30, 50, True, 0)])
@@ -486,6 +546,13 @@ MUTANTS = {
                          "const double slope = jb->slopes[(bh + 1) % jb->H];"),
     "softcap_no_outer": ("s[j - lo] = jb->cap * tanh(s[j - lo] / jb->cap);", "s[j - lo] = tanh(s[j - lo] / jb->cap);"),
     "softcap_no_inner": ("s[j - lo] = jb->cap * tanh(s[j - lo] / jb->cap);", "s[j - lo] = jb->cap * tanh(s[j - lo]);"),
+    "bwd_ds_sign": ("const double ds = s[j - lo] * (dp[j - lo] - dv_row);",
+                    "const double ds = s[j - lo] * (dv_row - dp[j - lo]);"),
+    "bwd_dq_no_scale": ("dQ[i * D + d] += jb->scale * ds * K[j * D + d];", "dQ[i * D + d] += ds * K[j * D + d];"),
+    "bwd_dk_uses_k": ("dK[j * D + d] += jb->scale * ds * qi[d];", "dK[j * D + d] += jb->scale * ds * K[j * D + d];"),
+    "bwd_dv_no_weight": ("for (long d = 0; d < D; ++d) dV[j * D + d] += p * doi[d];",
+                         "for (long d = 0; d < D; ++d) dV[j * D + d] += doi[d];"),
+    "bwd_rowsum_unweighted": ("dv_row += p * x;", "dv_row += x;"),
 }
 
 
@@ -549,6 +616,21 @@ def pin_suite(lib) -> bool:
             sv = [cp * mpmath.tanh(sc * mpmath.fsum(mpmath.mpf(float(Q[0, 0, i, d])) * mpmath.mpf(float(K[0, 0, j, d]))
                                                      for d in range(3)) / cp) for j in js]
             if abs(L[0, 0, i].item() - float(mpmath.log(mpmath.fsum(mpmath.exp(x) for x in sv)))) > 1e-12:
+                return False
+        # the backward against central differences of this build's forward
+        Qb, Kb, Vb, dOb = rnd((1, 1, 5, 4), 16, 0), rnd((1, 1, 6, 4), 16, 1), rnd((1, 1, 6, 4), 16, 2), \
+            rnd((1, 1, 5, 4), 16, 3)
+        dQ, dK, dV = oracle.attention_bwd(Qb, Kb, Vb, dOb, 0.7, -1, 0, lib=lib, threads=1)
+        for X, G, tid in [(Qb, dQ, 4), (Kb, dK, 5), (Vb, dV, 6)]:
+            E = rnd(X.shape, 17, tid)
+            X0 = X.clone()
+            vals = []
+            for sgn in (1, -1):
+                X.copy_(X0 + sgn * 1e-5 * E)
+                O, _ = oracle.attention(Qb, Kb, Vb, 0.7, window_left=-1, window_right=0, lib=lib, threads=1)
+                vals.append(float((O * dOb).sum()))
+            X.copy_(X0)
+            if abs((vals[0] - vals[1]) / 2e-5 - float((G * E).sum())) > 1e-6:
                 return False
         return True
     except RuntimeError:
