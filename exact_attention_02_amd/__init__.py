@@ -27,7 +27,7 @@ FA_ERR_MOD = 10
 FA_MOD_NONE, FA_MOD_SOFTCAP, FA_MOD_ALIBI = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_mod", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes",
-           "fa_splitkv_num_splits", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class",
+           "fa_splitkv_num_splits", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class",
            "fa_plan_window_range", "fa_plan_block_class_window")
 
 _lib = None
@@ -63,6 +63,10 @@ def load(path: str = LIB_PATH):
     lib.fa_splitkv_workspace_bytes.restype = LL
     lib.fa_splitkv_num_splits.argtypes = [I, I, I, I, I, I]
     lib.fa_splitkv_num_splits.restype = I
+    lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, P, LL]
+    lib.fa_bwd.restype = I
+    lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]
+    lib.fa_bwd_workspace_bytes.restype = LL
     lib.fa_status_str.argtypes = [I]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_plan_grid.argtypes = [I, I, I, I, I, I, I, I, pLL, pI, pI, pI]
@@ -115,6 +119,16 @@ def splitkv_workspace_bytes(B, H, Nq, D, num_splits) -> int:
 
 def splitkv_num_splits(B, H, Nq, Nk, D, dtype) -> int:
     return load().fa_splitkv_num_splits(B, H, Nq, Nk, D, dtype)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, scale, window_left, window_right, dtype, stream,
+           workspace, workspace_bytes) -> int:
+    return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, scale, int(window_left),
+                         int(window_right), dtype, stream, workspace, int(workspace_bytes))
+
+
+def bwd_workspace_bytes(B, H, Nq) -> int:
+    return load().fa_bwd_workspace_bytes(B, H, Nq)
 
 
 def alibi_slopes(H: int):
@@ -274,3 +288,52 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
     if st != FA_OK:
         raise FaError(st, where)
     return out, lse
+
+
+def attention_bwd(q, k, v, out, lse, dout, scale=None, causal=False, window_left=None, window_right=None,
+                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of O = softmax(scale Q K^T) V contracted with dout, via fa_bwd.
+
+    q, out, dout [B,H,Nq,D], k and v [B,H,Nk,D]: contiguous float16 or bfloat16
+    device tensors of one dtype; out and lse [B,H,Nq] (float32) are the
+    forward's outputs for the same arguments. The mask is causal (window_left
+    unbounded, window_right 0) or the extents of fa_fwd_window (None or -1:
+    unbounded). workspace: a uint8 device tensor of at least
+    bwd_workspace_bytes(B, H, Nq) bytes (allocated here when None).
+    """
+    import torch
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
+        raise ValueError("k and v must be [B,H,Nk,D] matching q")
+    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (B, H, Nq):
+        raise ValueError("out and dout must be [B,H,Nq,D] and lse [B,H,Nq]")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype) or lse.dtype != torch.float32:
+        raise ValueError("q, k, v, out, dout must share a dtype; lse must be float32")
+    for t in (q, k, v, out, dout, lse):
+        if not t.is_contiguous():
+            raise ValueError("every input must be contiguous")
+    code = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}.get(q.dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if window_left is not None or window_right is not None:
+        wl = -1 if window_left is None else int(window_left)
+        wr = -1 if window_right is None else int(window_right)
+    else:
+        wl, wr = -1, (0 if causal else -1)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_bytes(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, D, float(scale), wl, wr, code, stream,
+                workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -237,6 +237,63 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                nullptr, num_splits, num_splits > 1 ? workspace : nullptr);
 }
 
+long long fa_bwd_workspace_bytes(int B, int H, int Nq) {
+    if (B < 0 || H < 0 || Nq < 0) return -1;
+    const long long nqp = ((long long)Nq + 3) / 4 * 4;
+    return 2 * (long long)B * H * nqp * 4;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int Nq, int Nk, int D, float scale, int window_left, int window_right,
+           int dtype, void* stream, void* workspace, long long workspace_bytes) {
+    DtypeInfo di;
+    const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
+    if (st != FA_OK) return st;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    int wl, wr;
+    if (!window_extents(window_left, window_right, Nq, Nk, &wl, &wr)) return FA_ERR_MASK;
+    if (!finite_positive(scale)) return FA_ERR_SCALE;
+    const long long n_bh = (long long)B * H;
+    const long long n_qt = ((long long)Nq + 127) / 128, n_kt = ((long long)Nk + 127) / 128;
+    if (n_bh * n_qt > 0x7fffffffLL || n_bh * n_kt > 0x7fffffffLL) return FA_ERR_SHAPE;
+    const long long nqp = ((long long)Nq + 3) / 4 * 4;
+    if ((n_bh * nqp + 255) / 256 > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if (n_bh == 0 || (Nq == 0 && Nk == 0)) return FA_OK;  // nothing to write
+    if (Nq > 0 && (!q || !o || !dout || !lse || !dq || !workspace)) return FA_ERR_NULL;
+    if (Nk > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    if (Nq > 0 && workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq)) return FA_ERR_SHAPE;
+    const int dst = check_device();
+    if (dst != FA_OK) return dst;
+
+    fa::BwdParams p;
+    p.q = (const uint8_t*)q;
+    p.k = (const uint8_t*)k;
+    p.v = (const uint8_t*)v;
+    p.o = (const uint8_t*)o;
+    p.dout = (const uint8_t*)dout;
+    p.lse = lse;
+    p.dq = (uint8_t*)dq;
+    p.dk = (uint8_t*)dk;
+    p.dv = (uint8_t*)dv;
+    p.nqp = (int)nqp;
+    p.dvec = (float*)workspace;
+    p.l2 = workspace ? (float*)workspace + n_bh * nqp : nullptr;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.wl = wl;
+    p.wr = wr;
+    p.n_bh = (int)n_bh;
+    p.n_qt = (int)n_qt;
+    p.n_kt = (int)n_kt;
+    p.c = scale * 1.44269504088896341f;
+    p.scale = scale;
+    (void)hipGetLastError();
+    return fa::launch_bwd(di.in, D, p, stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_status_str(int status) {
     switch (status) {
         case FA_OK: return "ok";

@@ -1,0 +1,442 @@
+// Attention backward for 16-bit inputs on gfx950: dQ, dK and dV of
+// O = softmax(scale Q K^T) V, given the upstream gradient dO, the forward's O
+// and its log-sum-exp.
+//
+// The softmax weights are not stored by the forward; they are formed again
+// here from Q, K and the stored normaliser, tile by tile (aiinarabic.com
+// flash-attention page, the recomputation paragraph: the backward pass
+// recomputes the attention matrix instead of reading it from memory). With
+// P = exp(scale S - LSE):
+//   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - Dvec),
+//   dQ = scale dS K,   dK = scale dS^T Q,
+// where Dvec_i = dO_i . O_i is the row sum of P o dP.
+//
+// Three kernels:
+//   * fa_bwd_rowstat_kernel: Dvec and the LSE in base-2 units per row;
+//   * fa_bwd_dq_kernel: one workgroup per 128 query rows walks their keys.
+//     Scores are kept transposed as in the forward (lane = query): S^T = K Q^T
+//     and dP^T = V dO^T on MFMA, dS^T formed in registers, dQ^T += K^T dS^T
+//     with K^T read by transposing LDS reads;
+//   * fa_bwd_dkdv_kernel: one workgroup per 128 keys walks the query rows
+//     that see them, in the mirrored layout (lane = key): S = Q K^T and
+//     dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
+//     read by transposing LDS reads.
+// Both stream 64-row tiles through two LDS slots with direct-to-LDS copies,
+// in the layout of the forward kernels (swizzled 16-byte chunks), one barrier
+// per tile. P and dS are rounded to the input type for the MFMAs.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+#include "fa_sched.h"
+
+namespace fa {
+
+// ---------------------------------------------------------------- row statistics
+
+template <int IN, int D>
+__global__ __launch_bounds__(256) void fa_bwd_rowstat_kernel(BwdParams p) {
+    // one thread per padded row; the padding rows get dvec 0 and l2 +inf
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.n_bh * p.nqp) return;
+    const int bh = (int)(idx / p.nqp), i = (int)(idx % p.nqp);
+    float acc = 0.f, l2 = INFINITY;
+    if (i < p.Nq) {
+        const size_t row = (size_t)bh * p.Nq + i;
+        const uint8_t* orow = p.o + row * D * 2;
+        const uint8_t* drow = p.dout + row * D * 2;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const i32x4 a = *reinterpret_cast<const i32x4*>(orow + 16 * c);
+            const i32x4 b = *reinterpret_cast<const i32x4*>(drow + 16 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc = fmaf(unpack_lo<IN>(a[e]), unpack_lo<IN>(b[e]), acc);
+                acc = fmaf(unpack_hi<IN>(a[e]), unpack_hi<IN>(b[e]), acc);
+            }
+        }
+        const float l = p.lse[row];
+        // a row that sees no key: every weight of its row must come out 0
+        if (l != -INFINITY) l2 = l * LOG2E;
+    }
+    p.dvec[idx] = acc;
+    p.l2[idx] = l2;
+}
+
+// Shared pieces of the two tiled kernels: tile shape, the LDS row and
+// transposing reads of a 64-row tile (the forward's layout), the copies.
+template <int D>
+struct TileShape {
+    static constexpr int NW = 4;
+    static constexpr int NT = 64 * NW;
+    static constexpr int RB = D * 2;
+    static constexpr int CPR = RB / 16;
+    static constexpr int TILE = BC * RB;     // one tensor's 64-row tile
+    static constexpr int SLOT = 2 * TILE;    // two tensors
+    static constexpr int NKS = D / 16;
+    static constexpr int ND = D / 32;
+    static constexpr int NDMA = TILE / 16 / NT;
+};
+
+// ---------------------------------------------------------------- dQ
+
+template <int IN, int D>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
+    using T = TileShape<D>;
+    constexpr int RB = T::RB, CPR = T::CPR, TILE = T::TILE, SLOT = T::SLOT, NKS = T::NKS, ND = T::ND;
+    constexpr int NT = T::NT, NDMA = T::NDMA, BR = 32 * T::NW;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int g = lane >> 4, cl = lane & 15;
+    const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
+
+    int bh, qt;
+    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, &bh, &qt);
+    const int r0 = qt * BR, r1 = min(r0 + BR, Nq);
+    int kv_lo, kv_hi;
+    kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
+    const int t_lo = kv_lo / BC, t_hi = (kv_hi > kv_lo) ? (kv_hi + BC - 1) / BC : kv_lo / BC;
+    const int w0 = r0 + wave * 32, w1 = min(w0 + 32, Nq);
+    const int row = w0 + l32;
+
+    // Q and dO rows of the lane's query: B operands of S^T = K Q^T and dP^T = V dO^T
+    i32x4 qf[NKS], dof[NKS];
+    {
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(p.q + (size_t)bh * Nq * RB, (unsigned)(Nq * RB));
+        const __amdgpu_buffer_rsrc_t drs = make_rsrc(p.dout + (size_t)bh * Nq * RB, (unsigned)(Nq * RB));
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int off = row * RB + (16 * s + 8 * hh) * 2;
+            qf[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+            dof[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0));
+        }
+    }
+    const float l2 = (row < Nq) ? p.l2[(size_t)bh * p.nqp + row] : INFINITY;
+    const float dvv = (row < Nq) ? p.dvec[(size_t)bh * p.nqp + row] : 0.f;
+    const float c2 = p.c;
+
+    int jf0, jf1, ju0, ju1;
+    block_ranges32(w0, w1, Nq, Nk, wl, wr, &jf0, &jf1, &ju0, &ju1);
+
+    // K/V copies into slot t & 1
+    const i32x4 kwords = rsrc_words(p.k + (size_t)bh * Nk * RB, (unsigned)(Nk * RB));
+    const i32x4 vwords = rsrc_words(p.v + (size_t)bh * Nk * RB, (unsigned)(Nk * RB));
+    const unsigned smem_base = (unsigned)(unsigned long long)(lds_u8*)smem;
+    static_assert((NT / CPR) % 16 == 0, "copy rows");
+    const unsigned dma_voff = [&] {
+        const int slot = 64 * wave + lane;
+        const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
+        return (unsigned)(x * RB + c * 16);
+    }();
+    auto issue_tile = [&](int t) {
+        const unsigned kb = smem_base + (unsigned)((t & 1) * SLOT);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int run = 64 * wave + NT * i;
+            const unsigned soff = (unsigned)((t * BC + i * (NT / CPR)) * RB);
+            dma16(kwords, kb + run * 16, dma_voff, soff);
+            dma16(vwords, kb + TILE + run * 16, dma_voff, soff);
+        }
+    };
+
+    int kofs[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) kofs[s] = lds_pos<RB>(l32, 2 * s + hh);
+    int tofs[ND][2];   // transposing reads: rows 4hh + cl/4 and 8 rows further
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+        const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) tofs[db][h8] = lds_pos<RB>(4 * hh + (cl >> 2) + 8 * h8, ch) + 8 * (cl & 1);
+    }
+
+    f32x16 dq[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) dq[db] = f32x16{};
+
+    if (t_lo < t_hi) issue_tile(t_lo);
+    for (int t = t_lo; t < t_hi; ++t) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's copies of tile t (and the rows above) landed
+        __syncthreads();                       // ... and every wave's; tile t-1's slot is free
+        if (t + 1 < t_hi) issue_tile(t + 1);
+        const lds_u8* kt = (const lds_u8*)(smem + (t & 1) * SLOT);
+        const lds_u8* vt = kt + TILE;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int j = 2 * t + sub;
+            if ((unsigned)(j - ju0) >= (unsigned)(ju1 - ju0)) continue;   // no visible pair
+            const bool full = (unsigned)(j - jf0) < (unsigned)(jf1 - jf0);
+            f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const i32x4 ak = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+                    kt + 32 * sub * RB + kofs[s]);
+                const i32x4 av = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+                    vt + 32 * sub * RB + kofs[s]);
+                S = mfma16(IN, ak, qf[s], S);
+                dP = mfma16(IN, av, dof[s], dP);
+            }
+            if (!full) {
+                // element r of the lane holds key 32j + 8(r/4) + 4hh + r%4 against query row
+                const int ip = row + (Nk - Nq);
+                int klo = ip - wl, khi = ip + wr + 1;
+                klo = klo > 0 ? klo : 0;
+                khi = khi < Nk ? khi : Nk;
+                if (row >= w1) khi = klo;
+                const int a = klo - 32 * j - 4 * hh, b = khi - 32 * j - 4 * hh;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    S[r] = (off < a || off >= b) ? -INFINITY : S[r];
+                }
+            }
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -l2));
+                ds[r] = pr * (dP[r] - dvv);
+            }
+            i32x4 dsb[2];
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const int o = 8 * sp;
+                dsb[sp] = i32x4{pack2<IN>(ds[o + 0], ds[o + 1]), pack2<IN>(ds[o + 2], ds[o + 3]),
+                                pack2<IN>(ds[o + 4], ds[o + 5]), pack2<IN>(ds[o + 6], ds[o + 7])};
+            }
+            // dQ^T += K^T dS^T: K^T of the sub-tile in the key order dS^T has
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    const lds_u8* base = kt + (32 * sub + 16 * sp) * RB;
+                    const i32x2 u0 = read_tr16(base + tofs[db][0]);
+                    const i32x2 u1 = read_tr16(base + tofs[db][1]);
+                    dq[db] = mfma16(IN, i32x4{u0[0], u0[1], u1[0], u1[1]}, dsb[sp], dq[db]);
+                }
+        }
+    }
+
+    // dQ = scale * dQ^T, row `row`, columns 32db + 8r4 + 4hh .. +3
+    if (row < w1) {
+        uint8_t* orow = p.dq + ((size_t)bh * Nq + row) * RB;
+        const float sc = p.scale;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * hh;
+                Out<(IN == IN_BF16) ? OUT_BF16 : OUT_F16>::store4(orow + d * 2, dq[db][4 * r4] * sc,
+                                                                  dq[db][4 * r4 + 1] * sc, dq[db][4 * r4 + 2] * sc,
+                                                                  dq[db][4 * r4 + 3] * sc);
+            }
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+// D = 128 holds 128 accumulator registers for dK^T and dV^T: one wave per SIMD.
+template <int IN, int D>
+__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(BwdParams p) {
+    using T = TileShape<D>;
+    constexpr int RB = T::RB, CPR = T::CPR, TILE = T::TILE, SLOT = T::SLOT, NKS = T::NKS, ND = T::ND;
+    constexpr int NT = T::NT, NDMA = T::NDMA, BK = 32 * T::NW;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int g = lane >> 4, cl = lane & 15;
+    const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
+    const int dlt = Nk - Nq;
+
+    // key blocks in increasing order: under a causal mask the first ones see
+    // the most query rows, so the heaviest work starts first
+    int bh, kt;
+    decode_wg((long long)blockIdx.x, p.n_bh, p.n_kt, &bh, &kt);
+    kt = p.n_kt - 1 - kt;
+    const int c0 = kt * BK, c1 = min(c0 + BK, Nk);
+    // query rows that see a key of [c0, c1): key j is visible to row i when
+    // j - wr <= i' <= j + wl, i' = i + Nk - Nq
+    long long qlo = (long long)c0 - wr - dlt, qhi = (long long)(c1 - 1) + wl - dlt + 1;
+    if (qlo < 0) qlo = 0;
+    if (qhi > Nq) qhi = Nq;
+    if (qhi < qlo) qhi = qlo;
+    const int t_lo = (int)(qlo / BC), t_hi = (qhi > qlo) ? (int)((qhi + BC - 1) / BC) : t_lo;
+    const int kw0 = c0 + wave * 32, kw1 = min(kw0 + 32, Nk);
+    const int key = kw0 + l32;
+
+    // K and V rows of the lane's key: B operands of S = Q K^T and dP = dO V^T
+    i32x4 kf[NKS], vf[NKS];
+    {
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.k + (size_t)bh * Nk * RB, (unsigned)(Nk * RB));
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.v + (size_t)bh * Nk * RB, (unsigned)(Nk * RB));
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int off = key * RB + (16 * s + 8 * hh) * 2;
+            kf[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+            vf[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+        }
+    }
+    // per-row statistics through range-checked 16-byte loads: the head's rows
+    // start 16-byte aligned (padded to nqp), reads past them give 0, and only
+    // masked pairs ever read a padding or out-of-range row
+    const __amdgpu_buffer_rsrc_t l2rs = make_rsrc(p.l2 + (size_t)bh * p.nqp, (unsigned)(p.nqp * 4));
+    const __amdgpu_buffer_rsrc_t dvrs = make_rsrc(p.dvec + (size_t)bh * p.nqp, (unsigned)(p.nqp * 4));
+    const float c2 = p.c;
+    // the lane's key sees the rows [klo_q, khi_q)
+    int klo_q = key - wr - dlt, khi_q = key + wl - dlt + 1;
+    klo_q = klo_q > 0 ? klo_q : 0;
+    khi_q = khi_q < Nq ? khi_q : Nq;
+    if (key >= kw1) khi_q = klo_q;
+
+    const i32x4 qwords = rsrc_words(p.q + (size_t)bh * Nq * RB, (unsigned)(Nq * RB));
+    const i32x4 dwords = rsrc_words(p.dout + (size_t)bh * Nq * RB, (unsigned)(Nq * RB));
+    const unsigned smem_base = (unsigned)(unsigned long long)(lds_u8*)smem;
+    static_assert((NT / CPR) % 16 == 0, "copy rows");
+    const unsigned dma_voff = [&] {
+        const int slot = 64 * wave + lane;
+        const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
+        return (unsigned)(x * RB + c * 16);
+    }();
+    auto issue_tile = [&](int t) {
+        const unsigned qb = smem_base + (unsigned)((t & 1) * SLOT);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int run = 64 * wave + NT * i;
+            const unsigned soff = (unsigned)((t * BC + i * (NT / CPR)) * RB);
+            dma16(qwords, qb + run * 16, dma_voff, soff);
+            dma16(dwords, qb + TILE + run * 16, dma_voff, soff);
+        }
+    };
+
+    int rofs[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) rofs[s] = lds_pos<RB>(l32, 2 * s + hh);
+    int tofs[ND][2];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+        const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) tofs[db][h8] = lds_pos<RB>(4 * hh + (cl >> 2) + 8 * h8, ch) + 8 * (cl & 1);
+    }
+
+    f32x16 dk[ND], dv[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    if (t_lo < t_hi) issue_tile(t_lo);
+    for (int t = t_lo; t < t_hi; ++t) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (t + 1 < t_hi) issue_tile(t + 1);
+        const lds_u8* qt = (const lds_u8*)(smem + (t & 1) * SLOT);
+        const lds_u8* dt = qt + TILE;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int q0 = BC * t + 32 * sub;
+            if (q0 >= Nq) continue;
+            const int cls = tile_class32(q0, min(q0 + 32, Nq), kw0, kw1, Nq, Nk, wl, wr);
+            if (cls == TILE_SKIP) continue;
+            const bool full = cls == TILE_FULL && q0 + 32 <= Nq;
+            f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                const i32x4 aq = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+                    qt + 32 * sub * RB + rofs[s]);
+                const i32x4 ad = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+                    dt + 32 * sub * RB + rofs[s]);
+                S = mfma16(IN, aq, kf[s], S);
+                dP = mfma16(IN, ad, vf[s], dP);
+            }
+            // element r of the lane holds query q0 + 8(r/4) + 4hh + r%4 against the lane's key
+            const int a = klo_q - q0 - 4 * hh, b = khi_q - q0 - 4 * hh;
+            float pr[16], ds[16];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int qrow = q0 + 8 * gq + 4 * hh;
+                const f32x4v L = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(l2rs, qrow * 4, 0, 0));
+                const f32x4v Dv = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(dvrs, qrow * 4, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * gq + e, off = 8 * gq + e;
+                    const float s = (full || (off >= a && off < b)) ? S[r] : -INFINITY;
+                    pr[r] = __builtin_amdgcn_exp2f(fmaf(s, c2, -L[e]));
+                    ds[r] = pr[r] * (dP[r] - Dv[e]);
+                }
+            }
+            i32x4 pb[2], db2[2];
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const int o = 8 * sp;
+                pb[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
+                               pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
+                db2[sp] = i32x4{pack2<IN>(ds[o + 0], ds[o + 1]), pack2<IN>(ds[o + 2], ds[o + 3]),
+                                pack2<IN>(ds[o + 4], ds[o + 5]), pack2<IN>(ds[o + 6], ds[o + 7])};
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T in the query order P has
+#pragma unroll
+            for (int d0 = 0; d0 < ND; ++d0)
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    const int rowoff = (32 * sub + 16 * sp) * RB;
+                    const i32x2 o0 = read_tr16(dt + rowoff + tofs[d0][0]);
+                    const i32x2 o1 = read_tr16(dt + rowoff + tofs[d0][1]);
+                    const i32x2 u0 = read_tr16(qt + rowoff + tofs[d0][0]);
+                    const i32x2 u1 = read_tr16(qt + rowoff + tofs[d0][1]);
+                    dv[d0] = mfma16(IN, i32x4{o0[0], o0[1], o1[0], o1[1]}, pb[sp], dv[d0]);
+                    dk[d0] = mfma16(IN, i32x4{u0[0], u0[1], u1[0], u1[1]}, db2[sp], dk[d0]);
+                }
+        }
+    }
+
+    // dK = scale * dK^T, dV = dV^T: key row `key`, columns 32db + 8r4 + 4hh .. +3
+    if (key < kw1) {
+        uint8_t* krow = p.dk + ((size_t)bh * Nk + key) * RB;
+        uint8_t* vrow = p.dv + ((size_t)bh * Nk + key) * RB;
+        const float sc = p.scale;
+        constexpr int OT = (IN == IN_BF16) ? OUT_BF16 : OUT_F16;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * hh;
+                Out<OT>::store4(krow + d * 2, dk[db][4 * r4] * sc, dk[db][4 * r4 + 1] * sc, dk[db][4 * r4 + 2] * sc,
+                                dk[db][4 * r4 + 3] * sc);
+                Out<OT>::store4(vrow + d * 2, dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2],
+                                dv[db][4 * r4 + 3]);
+            }
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+template <int IN, int D>
+static int launch_bwd_d(const BwdParams& p, hipStream_t s) {
+    const long long rows = (long long)p.n_bh * p.nqp;
+    if (rows > 0)
+        hipLaunchKernelGGL((fa_bwd_rowstat_kernel<IN, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+    if (p.n_bh * (long long)p.n_qt > 0)
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<IN, D>), dim3((unsigned)(p.n_bh * (long long)p.n_qt)), dim3(256), 0, s, p);
+    if (p.n_bh * (long long)p.n_kt > 0)
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<IN, D>), dim3((unsigned)(p.n_bh * (long long)p.n_kt)), dim3(256), 0, s,
+                           p);
+    return (int)hipGetLastError();
+}
+
+int launch_bwd(int in, int D, const BwdParams& p, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (in == IN_BF16) return D == 64 ? launch_bwd_d<IN_BF16, 64>(p, s) : launch_bwd_d<IN_BF16, 128>(p, s);
+    if (in == IN_F16) return D == 64 ? launch_bwd_d<IN_F16, 64>(p, s) : launch_bwd_d<IN_F16, 128>(p, s);
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace fa

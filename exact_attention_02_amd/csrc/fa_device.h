@@ -13,6 +13,7 @@ namespace fa {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -158,6 +159,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, unsigned bytes) {
     const unsigned long long a = (unsigned long long)base;
     return i32x4{(int)(a & 0xffffffffu), (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// LDS layout of a K or V tile: row x of RB bytes holds its 16-byte chunk c at
+// position c ^ swz(x). LDS serves 256 bytes (64 banks of 4 bytes) per cycle:
+// a 16-lane group of 16-byte score-operand reads covers 16 consecutive rows
+// at one chunk, and a 32-lane half of the transposing V reads covers 4
+// consecutive rows at 4 aligned chunks. swz spreads both over distinct
+// banks: at 128-byte rows, two rows share a 256-byte bank cycle and
+// swz = ((x >> 1) & 1) << 2 | (x >> 2) & 3 separates rows x, x + 2 into
+// different groups of four chunks; at 256-byte rows, swz = (x & 3) << 2 |
+// (x >> 2) & 3 does the same for four consecutive rows. It depends on x mod
+// 16 only.
+template <int RB>
+__device__ __forceinline__ int swz16(int x) {
+    if constexpr (RB == 128) return (((x >> 1) & 1) << 2) | ((x >> 2) & 3);
+    else return ((x & 3) << 2) | ((x >> 2) & 3);
+}
+template <int RB>
+__device__ __forceinline__ int lds_pos(int x, int c) {
+    return x * RB + ((c ^ swz16<RB>(x)) << 4);
 }
 
 // HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS address

@@ -69,26 +69,6 @@ constexpr float SUM_LIMIT = 1024.f;
 #endif
 constexpr int EARLY_TILES = FA_EARLY_TILES;
 
-// LDS layout of a K or V tile: row x of RB bytes holds its 16-byte chunk c at
-// position c ^ swz(x). LDS serves 256 bytes (64 banks of 4 bytes) per cycle:
-// a 16-lane group of 16-byte score-operand reads covers 16 consecutive rows
-// at one chunk, and a 32-lane half of the transposing V reads covers 4
-// consecutive rows at 4 aligned chunks. swz spreads both over distinct
-// banks: at 128-byte rows, two rows share a 256-byte bank cycle and
-// swz = ((x >> 1) & 1) << 2 | (x >> 2) & 3 separates rows x, x + 2 into
-// different groups of four chunks; at 256-byte rows, swz = (x & 3) << 2 |
-// (x >> 2) & 3 does the same for four consecutive rows. It depends on x mod
-// 16 only.
-template <int RB>
-__device__ __forceinline__ int swz16(int x) {
-    if constexpr (RB == 128) return (((x >> 1) & 1) << 2) | ((x >> 2) & 3);
-    else return ((x & 3) << 2) | ((x >> 2) & 3);
-}
-template <int RB>
-__device__ __forceinline__ int lds_pos(int x, int c) {
-    return x * RB + ((c ^ swz16<RB>(x)) << 4);
-}
-
 // Waves per SIMD the register budget is sized for: three with one query
 // block per wave at D = 64 (three workgroups' LDS rings fit a CU), else two.
 #ifndef FA_WPS_D64

@@ -39,6 +39,35 @@ struct Params {
     float out_mul;  // descale_v (1 unless e4m3)
 };
 
+// The backward's arguments (16-bit inputs, D = 64 or 128). dvec and l2 are a
+// workspace of 2 * n_bh * nqp floats: per row, dO . O and the LSE in base-2
+// units (+inf for a row that sees no key), rows of a head padded to nqp, a
+// multiple of 4.
+struct BwdParams {
+    const uint8_t* q;
+    const uint8_t* k;
+    const uint8_t* v;
+    const uint8_t* o;
+    const uint8_t* dout;
+    const float* lse;
+    uint8_t* dq;
+    uint8_t* dk;
+    uint8_t* dv;
+    float* dvec;
+    float* l2;
+    int Nq, Nk;
+    int wl, wr;     // as in Params
+    int n_bh;
+    int nqp;        // Nq rounded up to a multiple of 4
+    int n_qt;       // 128-row query blocks per head (dQ kernel)
+    int n_kt;       // 128-key blocks per head (dK/dV kernel)
+    float c;        // scale * log2(e)
+    float scale;
+};
+
+// Enqueues the three backward kernels on `stream`; returns hipGetLastError().
+int launch_bwd(int in, int D, const BwdParams& p, void* stream);
+
 // Tile shape a launch uses.
 struct Plan {
     int in, out, D;

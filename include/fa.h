@@ -179,6 +179,39 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int window_left, int window_right, int dtype, void* stream,
                    int num_splits, void* workspace, long long workspace_bytes);
 
+/*
+ * Backward pass: the gradients dQ, dK, dV of O = softmax(scale Q K^T) V
+ * (with the mask of fa_fwd_window) contracted with an upstream gradient dO.
+ * The softmax weights are formed again from Q, K and the forward's LSE
+ * rather than read from memory (aiinarabic.com flash-attention page, the
+ * paragraph on recomputation: only the softmax normaliser is kept from the
+ * forward pass). With P = exp(scale S - LSE) and D_i = dO_i . O_i:
+ *     dV = P^T dO,  dS = P o (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * q, o, dout, dq: [B, H, Nq, D]; k, v, dk, dv: [B, H, Nk, D]; all
+ *   contiguous, of `dtype` (FA_F16 or FA_BF16; FA_ERR_DTYPE otherwise),
+ *   16-byte aligned device memory. o and lse are the forward's outputs for
+ *   the same q, k, v, scale and extents (lse: [B, H, Nq] float32, -inf for a
+ *   row that sees no key; such rows get dQ = 0 and add nothing to dK, dV).
+ * dq, dk, dv: outputs, overwritten (keys that no row sees get dK = dV = 0).
+ * window_left, window_right: the extents of fa_fwd_window.
+ * workspace: device memory of at least fa_bwd_workspace_bytes(B, H, Nq)
+ *   bytes, 16-byte aligned, owned by the caller and overwritten; calls that
+ *   may run concurrently must not share it (FA_ERR_SHAPE when too small,
+ *   FA_ERR_NULL when NULL and Nq > 0).
+ * Every kernel is enqueued on `stream`; the call does not synchronise.
+ * Errors as fa_fwd_window (scale must be finite and positive).
+ *
+ * fa_bwd_workspace_bytes: 8 * B * H * (Nq rounded up to a multiple of 4),
+ *   or -1 for negative sizes.
+ */
+long long fa_bwd_workspace_bytes(int B, int H, int Nq);
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int Nq, int Nk, int D, float scale,
+           int window_left, int window_right, int dtype, void* stream,
+           void* workspace, long long workspace_bytes);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_str(int status);
 

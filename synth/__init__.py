@@ -39,6 +39,7 @@ _MASK64 = (1 << 64) - 1
 # Tensor ids of the streams (fixed, never tuned).
 TID_Q, TID_K, TID_V = 0, 1, 2
 TID_OUTLIER_Q, TID_OUTLIER_K, TID_OUTLIER_V = 3, 4, 5
+TID_DOUT = 6
 
 E4M3_MAX = 448.0
 
@@ -160,6 +161,7 @@ class Workload:
     score_mod: Optional[str] = None
     softcap: float = 0.0
     splitkv: bool = False   # run through split-KV with the recommended split count
+    backward: bool = False  # the workload is the backward pass (dQ, dK, dV given dO)
 
     def __post_init__(self):
         if self.scale == 0.0:
@@ -194,6 +196,10 @@ WORKLOADS = {
     # serving: 32 heads of 64), run with split-KV. Seed 6.
     "c6": Workload("c6_decode_B8H32Nq1Nk16384D64_bf16", 8, 32, 1, 16384, 64, True, 0, "bf16", "bf16", 6,
                    splitkv=True),
+    # The backward pass at c3's shape: dQ, dK, dV of the causal forward given
+    # an upstream gradient dO (make_grad_out), O and the LSE.
+    "c3bwd": Workload("c3_backward_causal_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, True, 0, "bf16", "bf16", 3,
+                      backward=True),
 }
 
 
@@ -236,10 +242,18 @@ def make_inputs(w: Workload) -> Inputs:
     return Inputs(out[TID_Q], out[TID_K], out[TID_V], descales[TID_Q], descales[TID_K], descales[TID_V])
 
 
+def make_grad_out(w: Workload) -> torch.Tensor:
+    """The upstream gradient dO [B,H,Nq,D] of a backward workload: i.i.d.
+    N(0, 1) from stream (seed, TID_DOUT), on the host, in w.in_dtype."""
+    shp = (w.B, w.H, w.Nq, w.D)
+    return normal(w.seed, TID_DOUT, w.B * w.H * w.Nq * w.D).view(shp).to(DTYPES[w.in_dtype]).contiguous()
+
+
 def small_workload(name, B, H, Nq, Nk, D, causal, window, in_dtype, out_dtype, seed,
                    outlier_frac=0.0, outlier_mult=1.0, window_left=None, window_right=None,
-                   score_mod=None, softcap=0.0) -> Workload:
+                   score_mod=None, softcap=0.0, backward=False) -> Workload:
     """A workload of the same recipe at other sizes (parity and edge cases)."""
     return Workload(name, B, H, Nq, Nk, D, causal, window, in_dtype, out_dtype, seed,
                     outlier_frac=outlier_frac, outlier_mult=outlier_mult,
-                    window_left=window_left, window_right=window_right, score_mod=score_mod, softcap=softcap)
+                    window_left=window_left, window_right=window_right, score_mod=score_mod, softcap=softcap,
+                    backward=backward)

@@ -126,6 +126,56 @@ def test_splitkv_entry_checks_and_workspace_size():
     assert fa.fa_fwd_splitkv(P, P, P, P, P, 0, 2, 1, 4096, 64, 0.125, -1, 0, fa.FA_BF16, None, 8, None, 0) == fa.FA_OK
 
 
+def bwd_call(**kw):
+    a = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, H=2, Nq=64, Nk=96, D=64, scale=0.125,
+             wl=-1, wr=0, dtype=fa.FA_BF16, stream=None, ws=P, ws_bytes=fa.bwd_workspace_bytes(1, 2, 64))
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                     a["H"], a["Nq"], a["Nk"], a["D"], a["scale"], a["wl"], a["wr"], a["dtype"], a["stream"],
+                     a["ws"], a["ws_bytes"])
+
+
+def test_bwd_workspace_size():
+    assert fa.bwd_workspace_bytes(2, 3, 5) == 2 * 2 * 3 * 8 * 4      # rows padded to a multiple of 4
+    assert fa.bwd_workspace_bytes(1, 1, 8) == 2 * 8 * 4
+    assert fa.bwd_workspace_bytes(1, 1, 0) == 0
+    assert fa.bwd_workspace_bytes(-1, 1, 8) == -1
+    assert fa.bwd_workspace_bytes(4, 12, 8192) == 2 * 4 * 12 * 8192 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), fa.FA_ERR_SHAPE), (dict(Nk=-1), fa.FA_ERR_SHAPE), (dict(D=96), fa.FA_ERR_HEADDIM),
+    (dict(dtype=fa.FA_E4M3), fa.FA_ERR_DTYPE), (dict(dtype=fa.FA_F16_F32OUT), fa.FA_ERR_DTYPE),
+    (dict(dtype=fa.FA_BF16_F32OUT), fa.FA_ERR_DTYPE), (dict(dtype=0), fa.FA_ERR_DTYPE),
+    (dict(wl=-2), fa.FA_ERR_MASK), (dict(wr=-7), fa.FA_ERR_MASK),
+    (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=float("nan")), fa.FA_ERR_SCALE),
+    (dict(q=0), fa.FA_ERR_NULL), (dict(o=0), fa.FA_ERR_NULL), (dict(dout=0), fa.FA_ERR_NULL),
+    (dict(lse=0), fa.FA_ERR_NULL), (dict(dq=0), fa.FA_ERR_NULL), (dict(ws=0), fa.FA_ERR_NULL),
+    (dict(k=0), fa.FA_ERR_NULL), (dict(v=0), fa.FA_ERR_NULL), (dict(dk=0), fa.FA_ERR_NULL),
+    (dict(dv=0), fa.FA_ERR_NULL),
+    (dict(dout=P + 8), fa.FA_ERR_ALIGN), (dict(dk=P + 2), fa.FA_ERR_ALIGN), (dict(ws=P + 4), fa.FA_ERR_ALIGN),
+    (dict(lse=P + 2), fa.FA_ERR_ALIGN),
+    (dict(ws_bytes=fa.bwd_workspace_bytes(1, 2, 64) - 1), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 12, Nq=1 << 20), fa.FA_ERR_SHAPE),
+])
+def test_bwd_argument_errors_before_any_device_work(kw, code):
+    assert bwd_call(**kw) == code
+
+
+def test_bwd_empty_problems_need_no_device():
+    assert bwd_call(B=0) == fa.FA_OK
+    assert bwd_call(H=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, ws=0) == fa.FA_OK
+    assert bwd_call(Nq=0, Nk=0, q=0, k=0, v=0, ws=0) == fa.FA_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_bwd_valid_call_without_gpu_reports_device_error():
+    assert bwd_call() == fa.FA_ERR_DEVICE
+    # no rows: dK = dV = 0 must still be written, so the call needs the device
+    assert bwd_call(Nq=0, q=0, o=0, dout=0, lse=0, dq=0, ws=0, ws_bytes=0) == fa.FA_ERR_DEVICE
+    assert bwd_call(Nk=0, k=0, v=0, dk=0, dv=0) == fa.FA_ERR_DEVICE
+
+
 def test_empty_problems_need_no_device():
     assert call(B=0) == fa.FA_OK
     assert call(H=0, q=0, k=0, v=0, o=0, lse=0) == fa.FA_OK

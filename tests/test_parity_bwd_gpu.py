@@ -1,0 +1,197 @@
+"""Parity of the HIP backward (fa_bwd, through the C ABI) with the float64
+CPU oracle's dQ, dK, dV.
+
+Bound, derived from the kernel's arithmetic (u = 2^-8 for bfloat16, 2^-11 for
+float16, the unit roundoff of the input type). Every product in the kernel is
+formed by MFMA from stored 16-bit values and summed in fp32; the roundings
+that matter are:
+  * P rounded to the input type for dV = P^T dO (relative u per weight);
+  * dS rounded to the input type for dQ = scale dS K and dK = scale dS^T Q
+    (relative u per entry);
+  * D_i = dO_i . O_i formed from the forward's stored O, whose error per
+    element is at most about u (P|V|)_id + u |O_id| (the forward rounds P and
+    O), so |dD_i| <= u A_i with A_i = sum_d |dO_id| ((P|V|)_id + |O_id|); it
+    enters dS as P_ij dD_i;
+  * the outputs rounded to the input type (relative u).
+To first order, elementwise,
+  |dV - dV_ref| <= u (P^T|dO|) + u |dV_ref|
+  |dQ - dQ_ref| <= u scale (|dS||K| + A o (P|K|)) + u |dQ_ref|
+  |dK - dK_ref| <= u scale (|dS|^T|Q| + (P o A)^T |Q|) + u |dK_ref|
+fp32 accumulation and the fp32 exponential add terms below 1e-5 of these.
+The test allows twice the first-order bound plus 1e-6. The magnitude arrays
+P, dS, A are evaluated here in float64 from the inputs; they set the
+tolerance only, the expected values are the oracle's.
+
+Rows that see no key must give dQ = 0 exactly; keys that no row sees must give
+dK = dV = 0 exactly.
+"""
+import math
+
+import pytest
+import torch
+
+import exact_attention_02_amd as fa
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+UNIT = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def visible(Nq, Nk, wl, wr):
+    i = torch.arange(Nq)[:, None] + (Nk - Nq)
+    j = torch.arange(Nk)[None, :]
+    vis = torch.ones(Nq, Nk, dtype=torch.bool)
+    if wl >= 0:
+        vis &= j >= i - wl
+    if wr >= 0:
+        vis &= j <= i + wr
+    return vis
+
+
+def head_tolerance(Q, K, V, O, dO, dQr, dKr, dVr, scale, wl, wr, u):
+    """Elementwise allowed |error| of dQ, dK, dV for one head (float64 2-D inputs)."""
+    Nq, Nk = Q.shape[0], K.shape[0]
+    vis = visible(Nq, Nk, wl, wr)
+    S = (Q @ K.T) * scale
+    S = S.masked_fill(~vis, -math.inf)
+    m = S.max(dim=1, keepdim=True).values
+    m = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
+    E = torch.exp(S - m)
+    del S
+    P = E / E.sum(dim=1, keepdim=True).clamp_min(1e-300)
+    del E
+    dP = dO @ V.T
+    dS = P * (dP - (P * dP).sum(dim=1, keepdim=True))
+    del dP
+    A = (dO.abs() * (P @ V.abs() + O.abs())).sum(dim=1)
+    bV = P.T @ dO.abs()
+    bQ = scale * (dS.abs() @ K.abs() + A[:, None] * (P @ K.abs()))
+    bK = scale * (dS.abs().T @ Q.abs() + (P * A[:, None]).T @ Q.abs())
+    return [2.0 * u * (b + r.abs()) + 1e-6 for b, r in ((bQ, dQr), (bK, dKr), (bV, dVr))]
+
+
+def run(w, wl, wr, q, k, v, do):
+    """Forward (for O and LSE) then backward on the GPU; returns host tensors."""
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = fa.attention(qd, kd, vd, scale=w.scale, window_left=wl, window_right=wr)
+    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, window_left=wl, window_right=wr)
+    torch.cuda.synchronize()
+    return o.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check(w, wl, wr, q, k, v, do, o, dq, dk, dv, heads=None, ref=None):
+    """Compare (b, h) heads (default all) with the oracle under the derived bound."""
+    u = UNIT[w.in_dtype]
+    heads = heads or [(b, h) for b in range(w.B) for h in range(w.H)]
+    worst = 0.0
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        if ref is None:
+            dQr, dKr, dVr = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], w.scale, wl, wr)
+        else:
+            dQr, dKr, dVr = (t[sl] for t in ref)
+        dQr, dKr, dVr = dQr[0, 0], dKr[0, 0], dVr[0, 0]
+        Q, K, V, dO = (oracle.decode(t[b, h]) for t in (q, k, v, do))
+        tq, tk, tv = head_tolerance(Q, K, V, oracle.decode(o[b, h]), dO, dQr, dKr, dVr, w.scale, wl, wr, u)
+        for name, got, exp, tol in (("dQ", dq[b, h], dQr, tq), ("dK", dk[b, h], dKr, tk),
+                                    ("dV", dv[b, h], dVr, tv)):
+            err = (got.double() - exp).abs()
+            ratio = (err / tol).max().item() if err.numel() else 0.0
+            worst = max(worst, ratio)
+            assert torch.isfinite(got.double()).all(), f"{w.name} {name} ({b},{h}) not finite"
+            assert ratio <= 1.0, (f"{w.name} {name} head ({b},{h}): max err/tol {ratio:.3f}, "
+                                  f"max err {err.max().item():.3e}")
+        # exact zeros: rows that see no key, keys that no row sees
+        vis = visible(w.Nq, w.Nk, wl, wr)
+        empty_rows = ~vis.any(dim=1)
+        unseen = ~vis.any(dim=0)
+        assert (dq[b, h][empty_rows] == 0).all(), f"{w.name}: dQ of a row that sees no key"
+        assert (dk[b, h][unseen] == 0).all() and (dv[b, h][unseen] == 0).all(), \
+            f"{w.name}: dK/dV of a key that no row sees"
+    return worst
+
+
+# (name, B, H, Nq, Nk, D, window_left, window_right, dtype): several 128-row
+# blocks and 64-row tiles with ragged tails, every mask family, both dtypes,
+# both head dims, and the degenerate shapes.
+CASES = [
+    ("causal_sq", 1, 2, 300, 300, 64, -1, 0, "bf16"),
+    ("causal_sq_f16", 1, 2, 300, 300, 64, -1, 0, "f16"),
+    ("full_d128", 1, 2, 300, 300, 128, -1, -1, "bf16"),
+    ("causal_d128_f16", 2, 1, 257, 257, 128, -1, 0, "f16"),
+    ("causal_nq_lt_nk", 2, 1, 200, 333, 64, -1, 0, "bf16"),
+    ("causal_nq_gt_nk", 1, 1, 333, 200, 64, -1, 0, "bf16"),       # 133 rows see no key
+    ("window_sym_f16", 1, 2, 400, 400, 64, 50, 50, "f16"),
+    ("window_causal_d128", 1, 2, 400, 400, 128, 63, 0, "bf16"),
+    ("diagonal", 1, 1, 130, 130, 64, 0, 0, "bf16"),
+    ("left_only_f16", 1, 1, 300, 280, 64, 10, -1, "f16"),
+    ("unseen_keys", 1, 2, 100, 400, 64, 10, 0, "bf16"),          # keys below 290 are seen by no row
+    ("one_row", 1, 3, 1, 1000, 64, -1, 0, "bf16"),
+    ("one_key", 1, 2, 150, 1, 64, -1, -1, "bf16"),
+    ("one_by_one_f16", 1, 1, 1, 1, 64, -1, -1, "f16"),
+    ("ragged_batch", 3, 2, 129, 65, 64, -1, -1, "bf16"),
+    ("causal_1k", 1, 2, 1100, 1100, 64, -1, 0, "bf16"),
+    ("causal_1k_d128_f16", 1, 1, 1100, 1100, 128, -1, 0, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_bwd_parity(case):
+    name, B, H, Nq, Nk, D, wl, wr, dt = case
+    w = synth.small_workload("bwd_" + name, B, H, Nq, Nk, D, False, 0, dt, dt, 31 + len(name), backward=True)
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w)
+    print(f"case {name} B{B} H{H} Nq{Nq} Nk{Nk} D{D} wl{wl} wr{wr} {dt}", flush=True)
+    o, dq, dk, dv = run(w, wl, wr, inp.q, inp.k, inp.v, do)
+    ref = oracle.attention_bwd(inp.q, inp.k, inp.v, do, w.scale, wl, wr)
+    check(w, wl, wr, inp.q, inp.k, inp.v, do, o, dq, dk, dv, ref=ref)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(0, 70), (70, 0)])
+def test_bwd_empty_sides(Nq, Nk):
+    """No rows: dK = dV = 0 (nothing flows back). No keys: dQ = 0."""
+    w = synth.small_workload("bwd_empty", 1, 2, Nq, Nk, 64, False, 0, "bf16", "bf16", 5, backward=True)
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w)
+    q, k, v, dod = (t.to(DEV) for t in (inp.q, inp.k, inp.v, do))
+    o = torch.zeros_like(q)
+    lse = torch.full((1, 2, Nq), -math.inf, device=DEV)
+    dq = torch.full_like(q, 7.0)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    fa.attention_bwd(q, k, v, o, lse, dod, scale=w.scale, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
+
+
+def test_bwd_workspace_contents_do_not_matter_and_calls_repeat_bitwise():
+    """The workspace is fully written before it is read (padding rows included),
+    and the kernels use no atomics: a NaN-filled workspace gives the same bits."""
+    w = synth.small_workload("bwd_ws", 2, 3, 203, 190, 64, False, 0, "bf16", "bf16", 9, backward=True)
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w)
+    q, k, v, dod = (t.to(DEV) for t in (inp.q, inp.k, inp.v, do))
+    o, lse = fa.attention(q, k, v, scale=w.scale, causal=True)
+    need = fa.bwd_workspace_bytes(w.B, w.H, w.Nq)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    a = fa.attention_bwd(q, k, v, o, lse, dod, scale=w.scale, causal=True, workspace=ws)
+    b = fa.attention_bwd(q, k, v, o, lse, dod, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+        assert torch.isfinite(x.float()).all()
+
+
+def test_bwd_full_size_sampled_heads():
+    """The backward workload at full size (causal B4 H12 N8192 D64 bf16) in the
+    launch configuration the benchmark times; two heads compared in full."""
+    w = synth.WORKLOADS["c3bwd"]
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w)
+    wl, wr = -1, 0
+    print(f"full size {w.name}", flush=True)
+    o, dq, dk, dv = run(w, wl, wr, inp.q, inp.k, inp.v, do)
+    check(w, wl, wr, inp.q, inp.k, inp.v, do, o, dq, dk, dv, heads=[(0, 0), (w.B - 1, w.H - 1)])
