@@ -14,6 +14,10 @@ HBM. Prints one JSON line:
              is the one those counters were taken on
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
              workload's rows, on this host's cores (reported, not a target)
+
+The backward workload (--workload c3bwd) times one fa_bwd call (its three
+kernels) given O and the LSE of one earlier forward call: 10*D flops per
+visible pair (the recomputed Q K^T, dO V^T, P^T dO, dS K and dS^T Q).
 """
 import argparse
 import hashlib
@@ -63,6 +67,10 @@ def flops(w):
     return 4.0 * w.D * w.B * w.H * pairs(w)
 
 
+def flops_bwd(w):
+    return 10.0 * w.D * w.B * w.H * pairs(w)
+
+
 def algorithmic_bytes(w):
     eb = {"f16": 2, "bf16": 2, "e4m3": 1}[w.in_dtype]
     ob = {"f32": 4, "f16": 2, "bf16": 2}[w.out_dtype]
@@ -72,7 +80,7 @@ def algorithmic_bytes(w):
 
 def kernel_hash():
     h = hashlib.sha256()
-    for name in ("fa_fwd.hip", "fa_fwd16.hip", "fa_device.h", "fa_sched.h", "fa_launch.h"):
+    for name in ("fa_fwd.hip", "fa_fwd16.hip", "fa_bwd.hip", "fa_device.h", "fa_sched.h", "fa_launch.h"):
         with open(os.path.join(ROOT, "exact_attention_02_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -133,12 +141,34 @@ def cpu_baseline(w, inp, target_s=15.0):
         n = min(n_rows_total, max(2 * n, int(n * target_s / max(dt, 1e-3))))
 
 
+def cpu_baseline_bwd(w, inp, dout, target_s=15.0):
+    """The oracle's backward, as it is, on whole heads of the workload, scaled to TFLOP/s."""
+    import oracle
+    threads = oracle.default_threads()
+    wl = -1 if w.window_left is None else w.window_left
+    wr = -1 if w.window_right is None else w.window_right
+    if w.window_left is None and w.window_right is None:
+        wl, wr = (w.window - 1 if w.window > 0 else -1), (0 if w.causal else -1)
+    n_heads, spent = 0, 0.0
+    while spent < 0.5 * target_s and n_heads < w.B * w.H:
+        b, h = divmod(n_heads, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t0 = time.perf_counter()
+        oracle.attention_bwd(inp.q[sl], inp.k[sl], inp.v[sl], dout[sl], w.scale, wl, wr, threads=threads)
+        spent += time.perf_counter() - t0
+        n_heads += 1
+    fl = 10.0 * w.D * n_heads * visible_pairs_window(w.Nq, w.Nk, wl, wr)
+    return {"value": fl / spent / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{n_heads} whole (batch, head) slices of the workload ({fl / 1e9:.1f} GFLOP), float64, "
+                      f"{spent:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw c3sc c3al c6")
+    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw c3sc c3al c6 c3bwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (to scale the FETCH_SIZE/WRITE_SIZE "
@@ -189,6 +219,19 @@ def main():
         fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window, out=o, lse=lse,
                      window_left=w.window_left, window_right=w.window_right, **mod,
                      descales=descales, stream=stream.cuda_stream)
+
+    if w.backward:
+        # O and the LSE come from one forward call outside the timed region.
+        step()
+        dout = synth.make_grad_out(w)
+        do_d = dout.to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_b = torch.empty(max(16, fa.bwd_workspace_bytes(w.B, w.H, w.Nq)), dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.attention_bwd(q, k, v, o, lse, do_d, scale=w.scale, causal=w.causal,
+                             window_left=w.window_left, window_right=w.window_right,
+                             dq=dq, dk=dk, dv=dv, workspace=ws_b, stream=stream.cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -247,7 +290,21 @@ def main():
                          "timing": "HIP events on the launch stream, mean over the timed steps"},
         })
         res.pop("pct_mfma_peak", None)
-    if not args.no_cpu_baseline:
+    if w.backward:
+        fl = flops_bwd(w)
+        tflops = fl / (ms * 1e-3) / 1e12
+        res.update({
+            "metric": f"attention bwd TFLOPS (10*D flops per visible pair / time), {w.name}",
+            "value": round(tflops, 2), "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(tflops / peak, 4), "traffic": traffic_for(w.name),
+                         "kernel": "fa_bwd_rowstat_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one call)",
+                         "flop_per_launch": fl,
+                         "timing": "HIP events on the launch stream, mean over the timed steps"},
+        })
+    if not args.no_cpu_baseline and w.backward:
+        res["cpu_baseline"] = cpu_baseline_bwd(w, inp, dout)
+    elif not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp)
         if w.splitkv:
             res["cpu_baseline"]["note"] = "TFLOP/s of the oracle on sampled rows"
