@@ -279,7 +279,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     p.dk = (uint8_t*)dk;
     p.dv = (uint8_t*)dv;
     p.nqp = (int)nqp;
-    p.dvec = (float*)workspace;
+    p.ndvec = (float*)workspace;
     p.l2 = workspace ? (float*)workspace + n_bh * nqp : nullptr;
     p.Nq = Nq;
     p.Nk = Nk;

@@ -12,7 +12,7 @@
 // where Dvec_i = dO_i . O_i is the row sum of P o dP.
 //
 // Three kernels:
-//   * fa_bwd_rowstat_kernel: Dvec and the LSE in base-2 units per row;
+//   * fa_bwd_rowstat_kernel: -Dvec and the LSE in base-2 units per row;
 //   * fa_bwd_dq_kernel: one workgroup per 128 query rows walks their keys.
 //     Scores are kept transposed as in the forward (lane = query): S^T = K Q^T
 //     and dP^T = V dO^T on MFMA, dS^T formed in registers, dQ^T += K^T dS^T
@@ -24,6 +24,13 @@
 // Both stream 64-row tiles through two LDS slots with direct-to-LDS copies,
 // in the layout of the forward kernels (swizzled 16-byte chunks), one barrier
 // per tile. P and dS are rounded to the input type for the MFMAs.
+//
+// On this chip the MFMAs and the vector ALU work of the waves on one SIMD do
+// not overlap, so the loops are shaped to issue few vector instructions per
+// MFMA: the dP accumulator starts at -Dvec (dP - Dvec comes out of the MFMA),
+// masks are applied only on edge blocks, and the tile loop is unrolled over
+// the two LDS slots so that every LDS address is a loop-invariant register
+// plus an immediate.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,36 +40,47 @@
 #include "fa_launch.h"
 #include "fa_sched.h"
 
+// dQ kernel: 1 starts each dP^T accumulator at -Dvec from 16 loop-invariant
+// registers (no subtraction per score); 0 subtracts per score.
+#ifndef FA_BWD_DQ_DINIT
+#define FA_BWD_DQ_DINIT 1
+#endif
+
 namespace fa {
 
 // ---------------------------------------------------------------- row statistics
 
+// TPR threads per row, each reading 16 bytes of O and of dO per step; the
+// padding rows of a head (Nq <= i < nqp) get -Dvec = 0 and l2 = +inf.
 template <int IN, int D>
 __global__ __launch_bounds__(256) void fa_bwd_rowstat_kernel(BwdParams p) {
-    // one thread per padded row; the padding rows get dvec 0 and l2 +inf
-    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long long)p.n_bh * p.nqp) return;
-    const int bh = (int)(idx / p.nqp), i = (int)(idx % p.nqp);
-    float acc = 0.f, l2 = INFINITY;
+    constexpr int TPR = D / 8;
+    constexpr int RPB = 256 / TPR;
+    const int sub = threadIdx.x % TPR;
+    const long long idx = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+    const bool live = idx < (long long)p.n_bh * p.nqp;
+    const int bh = live ? (int)(idx / p.nqp) : 0, i = live ? (int)(idx % p.nqp) : p.Nq;
+    float acc = 0.f;
     if (i < p.Nq) {
         const size_t row = (size_t)bh * p.Nq + i;
-        const uint8_t* orow = p.o + row * D * 2;
-        const uint8_t* drow = p.dout + row * D * 2;
+        const i32x4 a = *reinterpret_cast<const i32x4*>(p.o + row * D * 2 + 16 * sub);
+        const i32x4 b = *reinterpret_cast<const i32x4*>(p.dout + row * D * 2 + 16 * sub);
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const i32x4 a = *reinterpret_cast<const i32x4*>(orow + 16 * c);
-            const i32x4 b = *reinterpret_cast<const i32x4*>(drow + 16 * c);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc = fmaf(unpack_lo<IN>(a[e]), unpack_lo<IN>(b[e]), acc);
-                acc = fmaf(unpack_hi<IN>(a[e]), unpack_hi<IN>(b[e]), acc);
-            }
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(unpack_lo<IN>(a[e]), unpack_lo<IN>(b[e]), acc);
+            acc = fmaf(unpack_hi<IN>(a[e]), unpack_hi<IN>(b[e]), acc);
         }
-        const float l = p.lse[row];
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+    if (!live || sub != 0) return;
+    float l2 = INFINITY;
+    if (i < p.Nq) {
+        const float l = p.lse[(size_t)bh * p.Nq + i];
         // a row that sees no key: every weight of its row must come out 0
         if (l != -INFINITY) l2 = l * LOG2E;
     }
-    p.dvec[idx] = acc;
+    p.ndvec[idx] = -acc;
     p.l2[idx] = l2;
 }
 
@@ -80,6 +98,16 @@ struct TileShape {
     static constexpr int ND = D / 32;
     static constexpr int NDMA = TILE / 16 / NT;
 };
+
+using Slot0 = std::integral_constant<int, 0>;
+using Slot1 = std::integral_constant<int, 1>;
+
+__device__ __forceinline__ i32x4 lds_read16(const lds_u8* a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(a);
+}
+__device__ __forceinline__ f32x4v lds_readf4(const lds_u8* a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) f32x4v*>(a);
+}
 
 // ---------------------------------------------------------------- dQ
 
@@ -118,13 +146,17 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
         }
     }
     const float l2 = (row < Nq) ? p.l2[(size_t)bh * p.nqp + row] : INFINITY;
-    const float dvv = (row < Nq) ? p.dvec[(size_t)bh * p.nqp + row] : 0.f;
+    const float ndv = (row < Nq) ? p.ndvec[(size_t)bh * p.nqp + row] : 0.f;
     const float c2 = p.c;
+#if FA_BWD_DQ_DINIT
+    f32x16 dinit;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dinit[r] = ndv;
+#endif
 
     int jf0, jf1, ju0, ju1;
     block_ranges32(w0, w1, Nq, Nk, wl, wr, &jf0, &jf1, &ju0, &ju1);
 
-    // K/V copies into slot t & 1
     const i32x4 kwords = rsrc_words(p.k + (size_t)bh * Nk * RB, (unsigned)(Nk * RB));
     const i32x4 vwords = rsrc_words(p.v + (size_t)bh * Nk * RB, (unsigned)(Nk * RB));
     const unsigned smem_base = (unsigned)(unsigned long long)(lds_u8*)smem;
@@ -134,8 +166,9 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
         const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
         return (unsigned)(x * RB + c * 16);
     }();
-    auto issue_tile = [&](int t) {
-        const unsigned kb = smem_base + (unsigned)((t & 1) * SLOT);
+    // K and V tile t into LDS slot `slot`
+    auto issue_tile = [&](int t, int slot) {
+        const unsigned kb = smem_base + (unsigned)(slot * SLOT);
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
             const int run = 64 * wave + NT * i;
@@ -145,6 +178,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
         }
     };
 
+    const lds_u8* lds = (const lds_u8*)smem;
     int kofs[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) kofs[s] = lds_pos<RB>(l32, 2 * s + hh);
@@ -160,27 +194,27 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < ND; ++db) dq[db] = f32x16{};
 
-    if (t_lo < t_hi) issue_tile(t_lo);
-    for (int t = t_lo; t < t_hi; ++t) {
+    auto tile = [&](int t, auto slot_c) {
+        constexpr int SL = decltype(slot_c)::value;
         __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's copies of tile t (and the rows above) landed
-        __syncthreads();                       // ... and every wave's; tile t-1's slot is free
-        if (t + 1 < t_hi) issue_tile(t + 1);
-        const lds_u8* kt = (const lds_u8*)(smem + (t & 1) * SLOT);
-        const lds_u8* vt = kt + TILE;
+        __syncthreads();                       // ... and every wave's; the other slot is free
+        if (t + 1 < t_hi) issue_tile(t + 1, 1 - SL);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int j = 2 * t + sub;
             if ((unsigned)(j - ju0) >= (unsigned)(ju1 - ju0)) continue;   // no visible pair
             const bool full = (unsigned)(j - jf0) < (unsigned)(jf1 - jf0);
-            f32x16 S = f32x16{}, dP = f32x16{};
+            constexpr int KB = SL * SLOT, VB = SL * SLOT + TILE;
+            f32x16 S = f32x16{};
+#if FA_BWD_DQ_DINIT
+            f32x16 dP = dinit;   // dP^T - Dvec
+#else
+            f32x16 dP = f32x16{};
+#endif
 #pragma unroll
             for (int s = 0; s < NKS; ++s) {
-                const i32x4 ak = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
-                    kt + 32 * sub * RB + kofs[s]);
-                const i32x4 av = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
-                    vt + 32 * sub * RB + kofs[s]);
-                S = mfma16(IN, ak, qf[s], S);
-                dP = mfma16(IN, av, dof[s], dP);
+                S = mfma16(IN, lds_read16(lds + kofs[s] + (KB + 32 * sub * RB)), qf[s], S);
+                dP = mfma16(IN, lds_read16(lds + kofs[s] + (VB + 32 * sub * RB)), dof[s], dP);
             }
             if (!full) {
                 // element r of the lane holds key 32j + 8(r/4) + 4hh + r%4 against query row
@@ -200,7 +234,11 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float pr = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -l2));
-                ds[r] = pr * (dP[r] - dvv);
+#if FA_BWD_DQ_DINIT
+                ds[r] = pr * dP[r];
+#else
+                ds[r] = pr * (dP[r] + ndv);
+#endif
             }
             i32x4 dsb[2];
 #pragma unroll
@@ -214,12 +252,18 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
             for (int db = 0; db < ND; ++db)
 #pragma unroll
                 for (int sp = 0; sp < 2; ++sp) {
-                    const lds_u8* base = kt + (32 * sub + 16 * sp) * RB;
-                    const i32x2 u0 = read_tr16(base + tofs[db][0]);
-                    const i32x2 u1 = read_tr16(base + tofs[db][1]);
+                    const int base = KB + (32 * sub + 16 * sp) * RB;
+                    const i32x2 u0 = read_tr16(lds + tofs[db][0] + base);
+                    const i32x2 u1 = read_tr16(lds + tofs[db][1] + base);
                     dq[db] = mfma16(IN, i32x4{u0[0], u0[1], u1[0], u1[1]}, dsb[sp], dq[db]);
                 }
         }
+    };
+
+    if (t_lo < t_hi) issue_tile(t_lo, 0);
+    for (int t = t_lo; t < t_hi; t += 2) {
+        tile(t, Slot0{});
+        if (t + 1 < t_hi) tile(t + 1, Slot1{});
     }
 
     // dQ = scale * dQ^T, row `row`, columns 32db + 8r4 + 4hh .. +3
@@ -246,7 +290,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
     using T = TileShape<D>;
     constexpr int RB = T::RB, CPR = T::CPR, TILE = T::TILE, SLOT = T::SLOT, NKS = T::NKS, ND = T::ND;
     constexpr int NT = T::NT, NDMA = T::NDMA, BK = 32 * T::NW;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
+    // a slot: the Q tile, the dO tile, then the tile rows' -Dvec and base-2 LSE
+    // (1 KB each: one 64-lane copy, of which the first 256 bytes are the rows')
+    constexpr int SLOTK = SLOT + 2048;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOTK];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -283,11 +330,14 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
             vf[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
         }
     }
-    // per-row statistics through range-checked 16-byte loads: the head's rows
-    // start 16-byte aligned (padded to nqp), reads past them give 0, and only
-    // masked pairs ever read a padding or out-of-range row
-    const __amdgpu_buffer_rsrc_t l2rs = make_rsrc(p.l2 + (size_t)bh * p.nqp, (unsigned)(p.nqp * 4));
-    const __amdgpu_buffer_rsrc_t dvrs = make_rsrc(p.dvec + (size_t)bh * p.nqp, (unsigned)(p.nqp * 4));
+    // The per-row statistics of a tile's 64 rows go to LDS with the tile: wave
+    // 0 copies -Dvec, wave 1 the base-2 LSE, lanes 0-15 4 rows each. The head's
+    // rows start 16-byte aligned (padded to nqp); lanes 16-63 and rows past
+    // the head read 0 (their offsets lie beyond the descriptor's range: 2^30
+    // plus at most 4 Nq < 2^25 bytes). Only masked pairs use a row past Nq.
+    const i32x4 swords = (wave == 0) ? rsrc_words(p.ndvec + (size_t)bh * p.nqp, (unsigned)(p.nqp * 4))
+                                     : rsrc_words(p.l2 + (size_t)bh * p.nqp, (unsigned)(p.nqp * 4));
+    const unsigned stat_voff = (lane < 16) ? (unsigned)(16 * lane) : (1u << 30);
     const float c2 = p.c;
     // the lane's key sees the rows [klo_q, khi_q)
     int klo_q = key - wr - dlt, khi_q = key + wl - dlt + 1;
@@ -304,8 +354,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
         const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
         return (unsigned)(x * RB + c * 16);
     }();
-    auto issue_tile = [&](int t) {
-        const unsigned qb = smem_base + (unsigned)((t & 1) * SLOT);
+    // Q, dO and the statistics of tile t into LDS slot `slot`
+    auto issue_tile = [&](int t, int slot) {
+        const unsigned qb = smem_base + (unsigned)(slot * SLOTK);
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
             const int run = 64 * wave + NT * i;
@@ -313,8 +364,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
             dma16(qwords, qb + run * 16, dma_voff, soff);
             dma16(dwords, qb + TILE + run * 16, dma_voff, soff);
         }
+        if (wave < 2) dma16(swords, qb + SLOT + 1024 * wave, stat_voff, (unsigned)(t * BC * 4));
     };
 
+    const lds_u8* lds = (const lds_u8*)smem;
     int rofs[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) rofs[s] = lds_pos<RB>(l32, 2 * s + hh);
@@ -325,6 +378,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) tofs[db][h8] = lds_pos<RB>(4 * hh + (cl >> 2) + 8 * h8, ch) + 8 * (cl & 1);
     }
+    const int sofs = 16 * hh;   // the lane half's 4 rows in each group of 8
 
     f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -333,13 +387,12 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
         dv[db] = f32x16{};
     }
 
-    if (t_lo < t_hi) issue_tile(t_lo);
-    for (int t = t_lo; t < t_hi; ++t) {
+    auto tile = [&](int t, auto slot_c) {
+        constexpr int SL = decltype(slot_c)::value;
+        constexpr int QB = SL * SLOTK, DB = SL * SLOTK + TILE, SB = SL * SLOTK + SLOT;
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        if (t + 1 < t_hi) issue_tile(t + 1);
-        const lds_u8* qt = (const lds_u8*)(smem + (t & 1) * SLOT);
-        const lds_u8* dt = qt + TILE;
+        if (t + 1 < t_hi) issue_tile(t + 1, 1 - SL);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int q0 = BC * t + 32 * sub;
@@ -347,30 +400,37 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
             const int cls = tile_class32(q0, min(q0 + 32, Nq), kw0, kw1, Nq, Nk, wl, wr);
             if (cls == TILE_SKIP) continue;
             const bool full = cls == TILE_FULL && q0 + 32 <= Nq;
-            f32x16 S = f32x16{}, dP = f32x16{};
+            // element r of the lane holds query q0 + 8(r/4) + 4hh + r%4 against the lane's key;
+            // dP - Dvec: the accumulator starts at each element's -Dvec
+            f32x16 S = f32x16{}, dP;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4v nd = lds_readf4(lds + sofs + (SB + 4 * (32 * sub + 8 * gq)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dP[4 * gq + e] = nd[e];
+            }
 #pragma unroll
             for (int s = 0; s < NKS; ++s) {
-                const i32x4 aq = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
-                    qt + 32 * sub * RB + rofs[s]);
-                const i32x4 ad = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
-                    dt + 32 * sub * RB + rofs[s]);
-                S = mfma16(IN, aq, kf[s], S);
-                dP = mfma16(IN, ad, vf[s], dP);
+                S = mfma16(IN, lds_read16(lds + rofs[s] + (QB + 32 * sub * RB)), kf[s], S);
+                dP = mfma16(IN, lds_read16(lds + rofs[s] + (DB + 32 * sub * RB)), vf[s], dP);
             }
-            // element r of the lane holds query q0 + 8(r/4) + 4hh + r%4 against the lane's key
-            const int a = klo_q - q0 - 4 * hh, b = khi_q - q0 - 4 * hh;
+            if (!full) {
+                const int a = klo_q - q0 - 4 * hh, b = khi_q - q0 - 4 * hh;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    S[r] = (off < a || off >= b) ? -INFINITY : S[r];
+                }
+            }
             float pr[16], ds[16];
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int qrow = q0 + 8 * gq + 4 * hh;
-                const f32x4v L = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(l2rs, qrow * 4, 0, 0));
-                const f32x4v Dv = __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(dvrs, qrow * 4, 0, 0));
+                const f32x4v L = lds_readf4(lds + sofs + (SB + 1024 + 4 * (32 * sub + 8 * gq)));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * gq + e, off = 8 * gq + e;
-                    const float s = (full || (off >= a && off < b)) ? S[r] : -INFINITY;
-                    pr[r] = __builtin_amdgcn_exp2f(fmaf(s, c2, -L[e]));
-                    ds[r] = pr[r] * (dP[r] - Dv[e]);
+                    const int r = 4 * gq + e;
+                    pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -L[e]));
+                    ds[r] = pr[r] * dP[r];
                 }
             }
             i32x4 pb[2], db2[2];
@@ -388,14 +448,20 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
 #pragma unroll
                 for (int sp = 0; sp < 2; ++sp) {
                     const int rowoff = (32 * sub + 16 * sp) * RB;
-                    const i32x2 o0 = read_tr16(dt + rowoff + tofs[d0][0]);
-                    const i32x2 o1 = read_tr16(dt + rowoff + tofs[d0][1]);
-                    const i32x2 u0 = read_tr16(qt + rowoff + tofs[d0][0]);
-                    const i32x2 u1 = read_tr16(qt + rowoff + tofs[d0][1]);
+                    const i32x2 o0 = read_tr16(lds + tofs[d0][0] + (DB + rowoff));
+                    const i32x2 o1 = read_tr16(lds + tofs[d0][1] + (DB + rowoff));
+                    const i32x2 u0 = read_tr16(lds + tofs[d0][0] + (QB + rowoff));
+                    const i32x2 u1 = read_tr16(lds + tofs[d0][1] + (QB + rowoff));
                     dv[d0] = mfma16(IN, i32x4{o0[0], o0[1], o1[0], o1[1]}, pb[sp], dv[d0]);
                     dk[d0] = mfma16(IN, i32x4{u0[0], u0[1], u1[0], u1[1]}, db2[sp], dk[d0]);
                 }
         }
+    };
+
+    if (t_lo < t_hi) issue_tile(t_lo, 0);
+    for (int t = t_lo; t < t_hi; t += 2) {
+        tile(t, Slot0{});
+        if (t + 1 < t_hi) tile(t + 1, Slot1{});
     }
 
     // dK = scale * dK^T, dV = dV^T: key row `key`, columns 32db + 8r4 + 4hh .. +3
@@ -422,8 +488,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
 template <int IN, int D>
 static int launch_bwd_d(const BwdParams& p, hipStream_t s) {
     const long long rows = (long long)p.n_bh * p.nqp;
+    constexpr int RPB = 256 / (D / 8);
     if (rows > 0)
-        hipLaunchKernelGGL((fa_bwd_rowstat_kernel<IN, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((fa_bwd_rowstat_kernel<IN, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s,
+                           p);
     if (p.n_bh * (long long)p.n_qt > 0)
         hipLaunchKernelGGL((fa_bwd_dq_kernel<IN, D>), dim3((unsigned)(p.n_bh * (long long)p.n_qt)), dim3(256), 0, s, p);
     if (p.n_bh * (long long)p.n_kt > 0)

@@ -39,10 +39,10 @@ struct Params {
     float out_mul;  // descale_v (1 unless e4m3)
 };
 
-// The backward's arguments (16-bit inputs, D = 64 or 128). dvec and l2 are a
-// workspace of 2 * n_bh * nqp floats: per row, dO . O and the LSE in base-2
-// units (+inf for a row that sees no key), rows of a head padded to nqp, a
-// multiple of 4.
+// The backward's arguments (16-bit inputs, D = 64 or 128). ndvec and l2 are
+// a workspace of 2 * n_bh * nqp floats: per row, -(dO . O) and the LSE in
+// base-2 units (+inf for a row that sees no key), rows of a head padded to
+// nqp, a multiple of 4.
 struct BwdParams {
     const uint8_t* q;
     const uint8_t* k;
@@ -53,7 +53,7 @@ struct BwdParams {
     uint8_t* dq;
     uint8_t* dk;
     uint8_t* dv;
-    float* dvec;
+    float* ndvec;
     float* l2;
     int Nq, Nk;
     int wl, wr;     // as in Params
