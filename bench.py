@@ -34,7 +34,6 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}
 HBM_PEAK_GBS = 8000.0
 METRIC = "attention fwd TFLOPS + % MFMA peak, B4 H12 N8192 D64 causal bf16"
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_02_amd", "csrc", "fa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -78,22 +77,27 @@ def algorithmic_bytes(w):
     return n_bh * (w.Nq * w.D * eb + 2 * w.Nk * w.D * eb + w.Nq * w.D * ob + w.Nq * 4)
 
 
-def kernel_hash():
+FWD_SOURCES = ("fa_fwd.hip", "fa_fwd16.hip", "fa_device.h", "fa_sched.h", "fa_launch.h")
+BWD_SOURCES = ("fa_bwd.hip", "fa_device.h", "fa_sched.h", "fa_launch.h")
+
+
+def kernel_hash(backward=False):
+    """Hash of the kernel sources a workload runs (the forward's or the backward's)."""
     h = hashlib.sha256()
-    for name in ("fa_fwd.hip", "fa_fwd16.hip", "fa_bwd.hip", "fa_device.h", "fa_sched.h", "fa_launch.h"):
+    for name in (BWD_SOURCES if backward else FWD_SOURCES):
         with open(os.path.join(ROOT, "exact_attention_02_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload_name):
+def traffic_for(w):
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(workload_name)
-    if not e or e.get("kernel_sha") != kernel_hash():
+    e = t.get(w.name)
+    if not e or e.get("kernel_sha") != kernel_hash(w.backward):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -270,7 +274,7 @@ def main():
                    "parallelism": "single GPU"},
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic_for(w.name),
+                     "frac": round(tflops / peak, 4), "traffic": traffic_for(w),
                      "kernel": "fa_fwd_kernel" if w.in_dtype == "e4m3" else "fa_fwd16_kernel", "flop_per_launch": fl,
                      "algorithmic_hbm_bytes": algorithmic_bytes(w),
                      "timing": "HIP events on the launch stream, mean over the timed steps"},
@@ -284,7 +288,7 @@ def main():
             "metric": f"attention decode GB/s (algorithmic HBM bytes / time), {w.name}",
             "value": round(gbs, 1), "unit": "GB/s", "num_splits": n_splits,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(w.name),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(w),
                          "kernel": "fa_fwd16_kernel + fa_combine_kernel",
                          "algorithmic_hbm_bytes": algorithmic_bytes(w), "flop_per_launch": fl,
                          "timing": "HIP events on the launch stream, mean over the timed steps"},
@@ -297,7 +301,7 @@ def main():
             "metric": f"attention bwd TFLOPS (10*D flops per visible pair / time), {w.name}",
             "value": round(tflops, 2), "pct_mfma_peak": round(100.0 * tflops / peak, 2),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                         "frac": round(tflops / peak, 4), "traffic": traffic_for(w.name),
+                         "frac": round(tflops / peak, 4), "traffic": traffic_for(w),
                          "kernel": "fa_bwd_rowstat_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one call)",
                          "flop_per_launch": fl,
                          "timing": "HIP events on the launch stream, mean over the timed steps"},

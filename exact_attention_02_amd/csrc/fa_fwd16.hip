@@ -161,6 +161,8 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
     const float sc_k2 = p.mk2;   // softcap: cap * log2(e)
     float slope2 = 0.f;          // ALiBi: this head's slope * log2(e)
     if constexpr (MOD == MOD_ALIBI) slope2 = p.slopes[bh % p.H] * LOG2E;
+    // ALiBi with a nonzero slope presets the reference (wave-uniform)
+    const bool alibi_ref = (MOD == MOD_ALIBI) && slope2 != 0.f;
 
     // ---- K/V copies: lane l of a wave fills the l-th 16-byte slot of a 1 KiB
     // run of the tile, fetching the global chunk that belongs there under the
@@ -397,12 +399,25 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
     // In the first sub-tiles of a row (EARLY) the residual pass is taken by
     // every lane from the weights pr kept by the step; later it is taken by
     // the rows whose new weight exceeds a quarter of their sum so far.
+    // "No reference yet" and the share of the row's sum above which a block
+    // takes the residual pass. Normally a lane half with no weight has no
+    // reference, and the share is of the lane half's sum so far. With an
+    // ALiBi reference preset from the largest-bias block (alibi_ref below),
+    // the blocks before it may have weights that round to 0 against it:
+    // "no reference" is then m = -inf, and since the row's final sum is at
+    // least 1 against that reference, shares are of max(sum so far, 1).
+    auto no_ref = [&](int qb) __attribute__((always_inline)) {
+        return alibi_ref ? (m[qb] == -INFINITY) : (lh[qb] == 0.f);
+    };
+    auto res_floor = [&](int qb) __attribute__((always_inline)) {
+        return alibi_ref ? fmaxf(lh[qb], 1.f) : lh[qb];
+    };
     auto tail = [&](auto early, int j, int qb, bool skip, float& ms, float& ts, i32x4(&hi)[2], float(&pr)[16])
         __attribute__((always_inline)) {
         constexpr bool EARLY = decltype(early)::value;
         const bool edge = !skip & !block_full(j, qb);
-        const bool first = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
-        const bool flag = !skip & (EARLY ? first : (first | (ts * 3.f > lh[qb])));
+        const bool first = no_ref(qb) | !(ts <= SUM_LIMIT);
+        const bool flag = !skip & (EARLY ? first : (first | (ts * 3.f > res_floor(qb))));
         if (edge || __builtin_amdgcn_ballot_w64(flag) != 0) {
             f32x16 S;
             scores(lds_cur, j, qb, S);
@@ -412,7 +427,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
                 // them again, and decide on the visible keys alone
                 mask(j, qb, S);
                 p_phase_pr(S, ms, ts, hi, pr, j, qb);
-                trig = (lh[qb] == 0.f) | !(ts <= SUM_LIMIT);
+                trig = no_ref(qb) | !(ts <= SUM_LIMIT);
             }
             if (__builtin_amdgcn_ballot_w64(trig) != 0) {
                 const unsigned tr = trig ? 1u : 0u;
@@ -446,7 +461,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
                 p_phase_pr(S, ms, ts, hi, pr, j, qb);
             }
             if constexpr (!EARLY) {
-                const bool sr = !skip & (ts * 3.f > lh[qb]);
+                const bool sr = !skip & (ts * 3.f > res_floor(qb));
                 if (__builtin_amdgcn_ballot_w64(sr) != 0) {
                     float pe[16];
                     if constexpr (MOD == MOD_NONE) {
@@ -547,6 +562,37 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
         }
         tail(early, j, qb, skip, ms, ts, Pc, pr);
     };
+
+    // ---- ALiBi: under a bias that grows with the key index the row max climbs
+    // by slope * 32 per sub-tile, so a reference taken from the first block
+    // would be passed, and the exact redo taken, on nearly every block. The
+    // reference starts instead at the row max of the modified scores of the
+    // query block's last visible sub-tile, where the bias is largest (K read
+    // straight from HBM; the same scores, bit for bit, as the loop forms for
+    // that sub-tile). Rows that see no key of it keep m = -inf.
+    if constexpr (MOD == MOD_ALIBI) {
+        if (alibi_ref) {
+            const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)(Nk * RB));
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                if (ju1[qb] <= ju0[qb] || ju1[qb] - 1 < 2 * t_lo || ju1[qb] - 1 >= 2 * t_hi) continue;
+                const int jl = ju1[qb] - 1;
+                i32x4 a[NKS];
+#pragma unroll
+                for (int s = 0; s < NKS; ++s)
+                    a[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        krs, (32 * jl + l32) * RB + (16 * s + 8 * hh) * 2, 0, 0));
+                f32x16 S;
+                s_mfma(a, qb, S);
+                mask(jl, qb, S);
+                const float ab = alibi_base(jl, qb, 0.f);
+                float mx = earg(S[0], 0, ab, 0.f);
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, earg(S[r], r, ab, 0.f));
+                m[qb] = max_halves(mx);
+            }
+        }
+    }
 
     // ---- prologue: Q and tile t_lo land, tile t_lo+1 is requested (with
     // RA == 2 it lands too and tile t_lo+2 is requested), the first block's
