@@ -30,7 +30,9 @@
 // MFMA: the dP accumulator starts at -Dvec (dP - Dvec comes out of the MFMA),
 // masks are applied only on edge blocks, and the tile loop is unrolled over
 // the two LDS slots so that every LDS address is a loop-invariant register
-// plus an immediate.
+// plus an immediate. Each sub-tile runs its scores, softmax and products in
+// turn; holding two sub-tiles' scores to overlap one's softmax with the
+// other's MFMAs costs a wave per SIMD (3 -> 2 at D = 64) and measured slower.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,6 +47,7 @@
 #ifndef FA_BWD_DQ_DINIT
 #define FA_BWD_DQ_DINIT 1
 #endif
+
 
 namespace fa {
 
@@ -387,74 +390,102 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
         dv[db] = f32x16{};
     }
 
+    // Pieces of one 32-row sub-tile `sub` of the tile in slot SL.
+    // -Dvec of the sub-tile's rows, the starting value of its dP accumulator:
+    // element r of the lane holds query q0 + 8(r/4) + 4hh + r%4 against the lane's key
+    auto dp_init = [&](auto slot_c, int sub) __attribute__((always_inline)) {
+        constexpr int SB = decltype(slot_c)::value * SLOTK + SLOT;
+        f32x16 d;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const f32x4v nd = lds_readf4(lds + sofs + (SB + 4 * (32 * sub + 8 * gq)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[4 * gq + e] = nd[e];
+        }
+        return d;
+    };
+    // S = Q K^T and dP - Dvec = dO V^T - Dvec of the sub-tile
+    auto scores = [&](auto slot_c, int sub, f32x16& S, f32x16& dP) __attribute__((always_inline)) {
+        constexpr int QB = decltype(slot_c)::value * SLOTK, DB = QB + TILE;
+        S = f32x16{};
+        dP = dp_init(slot_c, sub);
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            S = mfma16(IN, lds_read16(lds + rofs[s] + (QB + 32 * sub * RB)), kf[s], S);
+            dP = mfma16(IN, lds_read16(lds + rofs[s] + (DB + 32 * sub * RB)), vf[s], dP);
+        }
+    };
+    auto mask = [&](int q0, f32x16& S) __attribute__((always_inline)) {
+        const int a = klo_q - q0 - 4 * hh, b = khi_q - q0 - 4 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            S[r] = (off < a || off >= b) ? -INFINITY : S[r];
+        }
+    };
+    // P = 2^(c S - LSE) and dS = P (dP - Dvec), rounded to the MFMA type
+    auto softmax = [&](auto slot_c, int sub, const f32x16& S, const f32x16& dP, i32x4(&pb)[2], i32x4(&db2)[2])
+        __attribute__((always_inline)) {
+        constexpr int SB = decltype(slot_c)::value * SLOTK + SLOT;
+        float pr[16], ds[16];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const f32x4v L = lds_readf4(lds + sofs + (SB + 1024 + 4 * (32 * sub + 8 * gq)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * gq + e;
+                pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -L[e]));
+                ds[r] = pr[r] * dP[r];
+            }
+        }
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            const int o = 8 * sp;
+            pb[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
+                           pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
+            db2[sp] = i32x4{pack2<IN>(ds[o + 0], ds[o + 1]), pack2<IN>(ds[o + 2], ds[o + 3]),
+                            pack2<IN>(ds[o + 4], ds[o + 5]), pack2<IN>(ds[o + 6], ds[o + 7])};
+        }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T in the query order P has
+    auto accumulate = [&](auto slot_c, int sub, const i32x4(&pb)[2], const i32x4(&db2)[2])
+        __attribute__((always_inline)) {
+        constexpr int QB = decltype(slot_c)::value * SLOTK, DB = QB + TILE;
+#pragma unroll
+        for (int d0 = 0; d0 < ND; ++d0)
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const int rowoff = (32 * sub + 16 * sp) * RB;
+                const i32x2 o0 = read_tr16(lds + tofs[d0][0] + (DB + rowoff));
+                const i32x2 o1 = read_tr16(lds + tofs[d0][1] + (DB + rowoff));
+                const i32x2 u0 = read_tr16(lds + tofs[d0][0] + (QB + rowoff));
+                const i32x2 u1 = read_tr16(lds + tofs[d0][1] + (QB + rowoff));
+                dv[d0] = mfma16(IN, i32x4{o0[0], o0[1], o1[0], o1[1]}, pb[sp], dv[d0]);
+                dk[d0] = mfma16(IN, i32x4{u0[0], u0[1], u1[0], u1[1]}, db2[sp], dk[d0]);
+            }
+    };
+    auto sub_class = [&](int q0) __attribute__((always_inline)) {
+        if (q0 >= Nq) return (int)TILE_SKIP;
+        const int cls = tile_class32(q0, min(q0 + 32, Nq), kw0, kw1, Nq, Nk, wl, wr);
+        return (cls == TILE_FULL && q0 + 32 > Nq) ? (int)TILE_EDGE : cls;
+    };
+
     auto tile = [&](int t, auto slot_c) {
         constexpr int SL = decltype(slot_c)::value;
-        constexpr int QB = SL * SLOTK, DB = SL * SLOTK + TILE, SB = SL * SLOTK + SLOT;
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (t + 1 < t_hi) issue_tile(t + 1, 1 - SL);
+        const int cls0 = sub_class(BC * t), cls1 = sub_class(BC * t + 32);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-            const int q0 = BC * t + 32 * sub;
-            if (q0 >= Nq) continue;
-            const int cls = tile_class32(q0, min(q0 + 32, Nq), kw0, kw1, Nq, Nk, wl, wr);
+            const int cls = sub ? cls1 : cls0;
             if (cls == TILE_SKIP) continue;
-            const bool full = cls == TILE_FULL && q0 + 32 <= Nq;
-            // element r of the lane holds query q0 + 8(r/4) + 4hh + r%4 against the lane's key;
-            // dP - Dvec: the accumulator starts at each element's -Dvec
-            f32x16 S = f32x16{}, dP;
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4v nd = lds_readf4(lds + sofs + (SB + 4 * (32 * sub + 8 * gq)));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dP[4 * gq + e] = nd[e];
-            }
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                S = mfma16(IN, lds_read16(lds + rofs[s] + (QB + 32 * sub * RB)), kf[s], S);
-                dP = mfma16(IN, lds_read16(lds + rofs[s] + (DB + 32 * sub * RB)), vf[s], dP);
-            }
-            if (!full) {
-                const int a = klo_q - q0 - 4 * hh, b = khi_q - q0 - 4 * hh;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = 8 * (r >> 2) + (r & 3);
-                    S[r] = (off < a || off >= b) ? -INFINITY : S[r];
-                }
-            }
-            float pr[16], ds[16];
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4v L = lds_readf4(lds + sofs + (SB + 1024 + 4 * (32 * sub + 8 * gq)));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * gq + e;
-                    pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -L[e]));
-                    ds[r] = pr[r] * dP[r];
-                }
-            }
+            f32x16 S, dP;
             i32x4 pb[2], db2[2];
-#pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
-                const int o = 8 * sp;
-                pb[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
-                               pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
-                db2[sp] = i32x4{pack2<IN>(ds[o + 0], ds[o + 1]), pack2<IN>(ds[o + 2], ds[o + 3]),
-                                pack2<IN>(ds[o + 4], ds[o + 5]), pack2<IN>(ds[o + 6], ds[o + 7])};
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T in the query order P has
-#pragma unroll
-            for (int d0 = 0; d0 < ND; ++d0)
-#pragma unroll
-                for (int sp = 0; sp < 2; ++sp) {
-                    const int rowoff = (32 * sub + 16 * sp) * RB;
-                    const i32x2 o0 = read_tr16(lds + tofs[d0][0] + (DB + rowoff));
-                    const i32x2 o1 = read_tr16(lds + tofs[d0][1] + (DB + rowoff));
-                    const i32x2 u0 = read_tr16(lds + tofs[d0][0] + (QB + rowoff));
-                    const i32x2 u1 = read_tr16(lds + tofs[d0][1] + (QB + rowoff));
-                    dv[d0] = mfma16(IN, i32x4{o0[0], o0[1], o1[0], o1[1]}, pb[sp], dv[d0]);
-                    dk[d0] = mfma16(IN, i32x4{u0[0], u0[1], u1[0], u1[1]}, db2[sp], dk[d0]);
-                }
+            scores(slot_c, sub, S, dP);
+            if (cls != TILE_FULL) mask(BC * t + 32 * sub, S);
+            softmax(slot_c, sub, S, dP, pb, db2);
+            accumulate(slot_c, sub, pb, db2);
         }
     };
 
