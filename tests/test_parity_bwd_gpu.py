@@ -111,6 +111,7 @@ def check(w, wl, wr, q, k, v, do, o, dq, dk, dv, heads=None, ref=None):
         assert (dq[b, h][empty_rows] == 0).all(), f"{w.name}: dQ of a row that sees no key"
         assert (dk[b, h][unseen] == 0).all() and (dv[b, h][unseen] == 0).all(), \
             f"{w.name}: dK/dV of a key that no row sees"
+    print(f"{w.name}: worst error / tolerance {worst:.3f}", flush=True)
     return worst
 
 
@@ -195,3 +196,34 @@ def test_bwd_full_size_sampled_heads():
     print(f"full size {w.name}", flush=True)
     o, dq, dk, dv = run(w, wl, wr, inp.q, inp.k, inp.v, do)
     check(w, wl, wr, inp.q, inp.k, inp.v, do, o, dq, dk, dv, heads=[(0, 0), (w.B - 1, w.H - 1)])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_bwd_masked_positions_are_exact(dt):
+    """Masked pairs contribute exactly nothing: under a causal mask, scaling the
+    K and V rows that rows 0..150 cannot see leaves their dQ bitwise unchanged,
+    and scaling the Q and dO rows 0..99 (which cannot see keys 100..) leaves dK
+    and dV of those keys bitwise unchanged."""
+    w = synth.small_workload("bwd_maskexact", 1, 2, 300, 300, 64, True, 0, dt, dt, 12, backward=True)
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w)
+
+    def grads(q, k, v, dout):
+        qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, dout))
+        o, lse = fa.attention(qd, kd, vd, scale=w.scale, causal=True)
+        g = fa.attention_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, causal=True)
+        torch.cuda.synchronize()
+        return [t.cpu() for t in g]
+
+    base = grads(inp.q, inp.k, inp.v, do)
+    k2, v2 = inp.k.clone(), inp.v.clone()
+    k2[:, :, 151:] = (k2[:, :, 151:].float() * 100).to(k2.dtype)
+    v2[:, :, 151:] = (v2[:, :, 151:].float() * 100).to(v2.dtype)
+    pk = grads(inp.q, k2, v2, do)
+    assert torch.equal(base[0][:, :, :151].view(torch.int16), pk[0][:, :, :151].view(torch.int16))
+    q2, do2 = inp.q.clone(), do.clone()
+    q2[:, :, :100] = (q2[:, :, :100].float() * 100).to(q2.dtype)
+    do2[:, :, :100] = (do2[:, :, :100].float() * 100).to(do2.dtype)
+    pq = grads(q2, inp.k, inp.v, do2)
+    for a, b in ((base[1], pq[1]), (base[2], pq[2])):
+        assert torch.equal(a[:, :, 100:].view(torch.int16), b[:, :, 100:].view(torch.int16))
