@@ -464,10 +464,16 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
                 dk[d0] = mfma16(IN, i32x4{u0[0], u0[1], u1[0], u1[1]}, db2[sp], dk[d0]);
             }
     };
-    auto sub_class = [&](int q0) __attribute__((always_inline)) {
-        if (q0 >= Nq) return (int)TILE_SKIP;
-        const int cls = tile_class32(q0, min(q0 + 32, Nq), kw0, kw1, Nq, Nk, wl, wr);
-        return (cls == TILE_FULL && q0 + 32 > Nq) ? (int)TILE_EDGE : cls;
+    // Class of 32-row sub-tile n (rows 32n .. 32n+31) against the wave's keys,
+    // from two ranges of n computed once: the mask read with keys as rows --
+    // key j sees the rows i with i + Nk - Nq in [j - wr, j + wl] -- is the
+    // forward's with (Nq, Nk) and (wl, wr) swapped. A full sub-tile lies
+    // inside [0, Nq).
+    int nf0, nf1, nu0, nu1;
+    block_ranges32(kw0, kw1, Nk, Nq, wr, wl, &nf0, &nf1, &nu0, &nu1);
+    auto sub_class = [&](int n) __attribute__((always_inline)) {
+        if ((unsigned)(n - nu0) >= (unsigned)(nu1 - nu0)) return (int)TILE_SKIP;
+        return ((unsigned)(n - nf0) < (unsigned)(nf1 - nf0)) ? (int)TILE_FULL : (int)TILE_EDGE;
     };
 
     auto tile = [&](int t, auto slot_c) {
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (t + 1 < t_hi) issue_tile(t + 1, 1 - SL);
-        const int cls0 = sub_class(BC * t), cls1 = sub_class(BC * t + 32);
+        const int cls0 = sub_class(2 * t), cls1 = sub_class(2 * t + 1);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int cls = sub ? cls1 : cls0;

@@ -179,6 +179,27 @@ int main() {{
         const int r = (j >= jf0 && j < jf1) ? 1 : ((j >= ju0 && j < ju1) ? 2 : 0);
         ++n; if (a != b || a != r) {{ if (bad < 5) std::printf("mismatch %d %d %d %d %d %d %d: %d vs %d vs %d\\n", w0, w1, c0, Nq, Nk, wl, wr, a, b, r); ++bad; }}
     }};
+    // The backward's key-parallel kernel classifies 32-row sub-tiles n against
+    // its keys [k0, k1) from block_ranges32 with (Nq, Nk) and (wl, wr)
+    // swapped; a sub-tile that reaches past Nq must not count as full.
+    auto check_t = [&](int k0, int k1, int Nq, int Nk, int wl, int wr) {{
+        int nf0, nf1, nu0, nu1;
+        fa::block_ranges32(k0, k1, Nk, Nq, wr, wl, &nf0, &nf1, &nu0, &nu1);
+        for (int q0 = 0; q0 < Nq + 64; q0 += 32) {{
+            int a = (q0 >= Nq) ? 0 : fa::tile_class(q0, q0 + 32 < Nq ? q0 + 32 : Nq, k0, k1, Nq, Nk, wl, wr);
+            if (a == 1 && q0 + 32 > Nq) a = 2;
+            const int nn = q0 / 32;
+            const int r = (nn >= nf0 && nn < nf1) ? 1 : ((nn >= nu0 && nn < nu1) ? 2 : 0);
+            ++n; if (a != r) {{ if (bad < 5) std::printf("transposed mismatch %d %d %d %d %d %d %d: %d vs %d\\n", k0, k1, q0, Nq, Nk, wl, wr, a, r); ++bad; }}
+        }}
+    }};
+    for (int Nq : sizes) for (int Nk : sizes) {{
+        for (int wl0 : {{-1, 0, 1, 5, 31, 32, 100}}) for (int wr0 : {{-1, 0, 1, 7, 33, 200}}) {{
+            const int big = Nq + Nk;
+            const int wl = (wl0 < 0 || wl0 > big) ? big : wl0, wr = (wr0 < 0 || wr0 > big) ? big : wr0;
+            for (int k0 = 0; k0 < Nk; k0 += 32) check_t(k0, k0 + 32 < Nk ? k0 + 32 : Nk, Nq, Nk, wl, wr);
+        }}
+    }}
     for (int Nq : sizes) for (int Nk : sizes) {{
         // fa_fwd's (causal, window) masks
         for (int causal = 0; causal < 2; ++causal)
