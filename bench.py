@@ -179,8 +179,8 @@ def main():
                          "counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(head-parallel sharding across GPUs is described, not built)"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 "
+                                   "(sharding the heads across GPUs is not implemented)"}))
         sys.exit(2)
 
     import torch

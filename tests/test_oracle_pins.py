@@ -617,7 +617,7 @@ def pin_suite(lib) -> bool:
                                                      for d in range(3)) / cp) for j in js]
             if abs(L[0, 0, i].item() - float(mpmath.log(mpmath.fsum(mpmath.exp(x) for x in sv)))) > 1e-12:
                 return False
-        # the backward against central differences of this build's forward
+        # the backward against central differences of the (possibly mutated) oracle forward
         Qb, Kb, Vb, dOb = rnd((1, 1, 5, 4), 16, 0), rnd((1, 1, 6, 4), 16, 1), rnd((1, 1, 6, 4), 16, 2), \
             rnd((1, 1, 5, 4), 16, 3)
         dQ, dK, dV = oracle.attention_bwd(Qb, Kb, Vb, dOb, 0.7, -1, 0, lib=lib, threads=1)
