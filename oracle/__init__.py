@@ -52,6 +52,10 @@ def load(path: str = _LIB):
     fb = lib.oracle_attn_bwd
     fb.argtypes = [P, P, P, P, P, P, P, L, L, L, L, L, ctypes.c_double, L, L, ctypes.c_int]
     fb.restype = ctypes.c_int
+    fbm = lib.oracle_attn_bwd_mod
+    fbm.argtypes = [P, P, P, P, P, P, P, L, L, L, L, L, ctypes.c_double, L, L, ctypes.c_int, ctypes.c_double, P,
+                    ctypes.c_int]
+    fbm.restype = ctypes.c_int
     return lib
 
 
@@ -169,12 +173,14 @@ def attention(q, k, v, scale, causal=False, window=0, descales=(1.0, 1.0, 1.0),
     return O, LSE
 
 
-def attention_bwd(q, k, v, dout, scale, window_left=-1, window_right=-1, threads=None, lib=None):
-    """float64 (dQ, dK, dV) of O = softmax(scale Q K^T) V under the extents mask, given dO.
+def attention_bwd(q, k, v, dout, scale, window_left=-1, window_right=-1, threads=None, lib=None,
+                  score_mod=None, softcap=0.0, alibi_slopes=None):
+    """float64 (dQ, dK, dV) of O = softmax(f(scale Q K^T)) V under the extents mask, given dO.
 
     q, dout [B,H,Nq,D]; k, v [B,H,Nk,D] (any float dtype, decoded exactly);
     window_left/right as in attention() (-1: open side). scale is used as
-    float64(fp32(scale)).
+    float64(fp32(scale)). score_mod: None, "softcap" or "alibi" as in
+    attention() (f the modifier; its derivative enters by the chain rule).
     """
     lib = lib or _get()
     threads = threads or default_threads()
@@ -185,8 +191,20 @@ def attention_bwd(q, k, v, dout, scale, window_left=-1, window_right=-1, threads
     dQ = torch.empty((B, H, Nq, D), dtype=torch.float64)
     dK = torch.empty((B, H, Nk, D), dtype=torch.float64)
     dV = torch.empty((B, H, Nk, D), dtype=torch.float64)
-    rc = lib.oracle_attn_bwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dO.data_ptr(), dQ.data_ptr(), dK.data_ptr(),
-                             dV.data_ptr(), B, H, Nq, Nk, D, scale64, int(window_left), int(window_right), threads)
+    if score_mod is None:
+        rc = lib.oracle_attn_bwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dO.data_ptr(), dQ.data_ptr(),
+                                 dK.data_ptr(), dV.data_ptr(), B, H, Nq, Nk, D, scale64, int(window_left),
+                                 int(window_right), threads)
+    else:
+        mod = MODS[score_mod]
+        sl = torch.zeros(max(H, 1), dtype=torch.float64)
+        if mod == 2:
+            sl = torch.as_tensor([float(x) for x in alibi_slopes], dtype=torch.float64)
+            assert sl.numel() == H
+        sl = sl.contiguous()
+        rc = lib.oracle_attn_bwd_mod(Q.data_ptr(), K.data_ptr(), V.data_ptr(), dO.data_ptr(), dQ.data_ptr(),
+                                     dK.data_ptr(), dV.data_ptr(), B, H, Nq, Nk, D, scale64, int(window_left),
+                                     int(window_right), mod, float(softcap), sl.data_ptr(), threads)
     if rc != 0:
         raise RuntimeError(f"oracle_attn_bwd returned {rc}")
     return dQ, dK, dV

@@ -245,6 +245,11 @@ static int run_job(job_t *jbp, int nthreads)
  *   dQ_i  = scale sum_j dS_j K_j
  *   dK_j += scale dS_j Q_i
  * over the visible keys J_i of the extents mask (wl, wr; negative = open).
+ * With a score modifier s_j <- f(s_j) (softcap or ALiBi, as in the forward),
+ * P_j is the softmax of the modified scores and the chain rule multiplies the
+ * softmax gradient by f'(s_j):
+ *   softcap: f(x) = cap tanh(x / cap),  f'(x) = 1 - tanh(x / cap)^2
+ *   ALiBi:   f(x) = x + slope[h] (j - i'),  f'(x) = 1
  * Rows are taken in order within a head; heads run in parallel threads.
  */
 typedef struct {
@@ -252,11 +257,14 @@ typedef struct {
     double *dq, *dk, *dv;
     long B, H, Nq, Nk, D, wl, wr;
     double scale;
+    int mod;                /* 0 none, 1 softcap, 2 ALiBi */
+    double cap;
+    const double *slopes;   /* [H] for ALiBi */
     long next;
     pthread_mutex_t lock;
 } bjob_t;
 
-static void bwd_head(const bjob_t *jb, long bh, double *s, double *dp)
+static void bwd_head(const bjob_t *jb, long bh, double *s, double *dp, double *g)
 {
     const long D = jb->D, Nq = jb->Nq, Nk = jb->Nk;
     const double *Q = jb->q + bh * Nq * D, *K = jb->k + bh * Nk * D, *V = jb->v + bh * Nk * D;
@@ -271,12 +279,20 @@ static void bwd_head(const bjob_t *jb, long bh, double *s, double *dp)
         if (jb->wr >= 0 && ip + jb->wr + 1 < Nk) hi = ip + jb->wr + 1;
         if (hi <= lo) continue;
         const double *qi = Q + i * D, *doi = dO + i * D;
-        /* the softmax row, materialised */
+        /* the softmax row of the modified scores, materialised, and f' */
         double m = -INFINITY;
         for (long j = lo; j < hi; ++j) {
             double dot = 0.0;
             for (long d = 0; d < D; ++d) dot += qi[d] * K[j * D + d];
             s[j - lo] = dot * jb->scale;
+            g[j - lo] = 1.0;
+            if (jb->mod == 1) {
+                const double t = tanh(s[j - lo] / jb->cap);
+                s[j - lo] = jb->cap * t;
+                g[j - lo] = 1.0 - t * t;
+            } else if (jb->mod == 2) {
+                s[j - lo] += jb->slopes[bh % jb->H] * (double)(j - ip);
+            }
             if (s[j - lo] > m) m = s[j - lo];
         }
         double l = 0.0;
@@ -293,7 +309,8 @@ static void bwd_head(const bjob_t *jb, long bh, double *s, double *dp)
             for (long d = 0; d < D; ++d) dV[j * D + d] += p * doi[d];
         }
         for (long j = lo; j < hi; ++j) {
-            const double ds = s[j - lo] * (dp[j - lo] - dv_row);
+            const double dsm = s[j - lo] * (dp[j - lo] - dv_row);   /* w.r.t. the modified score */
+            const double ds = dsm * g[j - lo];                       /* w.r.t. scale q.k */
             for (long d = 0; d < D; ++d) {
                 dQ[i * D + d] += jb->scale * ds * K[j * D + d];
                 dK[j * D + d] += jb->scale * ds * qi[d];
@@ -307,28 +324,34 @@ static void *bwd_worker(void *arg)
     bjob_t *jb = (bjob_t *)arg;
     double *s = (double *)malloc(sizeof(double) * (size_t)(jb->Nk > 0 ? jb->Nk : 1));
     double *dp = (double *)malloc(sizeof(double) * (size_t)(jb->Nk > 0 ? jb->Nk : 1));
+    double *g = (double *)malloc(sizeof(double) * (size_t)(jb->Nk > 0 ? jb->Nk : 1));
     for (;;) {
         pthread_mutex_lock(&jb->lock);
         const long bh = jb->next++;
         pthread_mutex_unlock(&jb->lock);
         if (bh >= jb->B * jb->H) break;
-        bwd_head(jb, bh, s, dp);
+        bwd_head(jb, bh, s, dp, g);
     }
     free(s);
     free(dp);
+    free(g);
     return NULL;
 }
 
-/* dQ [B,H,Nq,D], dK and dV [B,H,Nk,D] of the extents-masked attention. */
-int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
-                    double *dq, double *dk, double *dv, long B, long H, long Nq, long Nk, long D,
-                    double scale, long wl, long wr, int nthreads)
+/* dQ [B,H,Nq,D], dK and dV [B,H,Nk,D] of the extents-masked attention with
+   a score modifier: mod 0 none, 1 softcap (cap > 0), 2 ALiBi (slopes[H]). */
+int oracle_attn_bwd_mod(const double *q, const double *k, const double *v, const double *dout,
+                        double *dq, double *dk, double *dv, long B, long H, long Nq, long Nk, long D,
+                        double scale, long wl, long wr, int mod, double cap, const double *slopes,
+                        int nthreads)
 {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || D <= 0 || nthreads <= 0) return -1;
+    if (mod < 0 || mod > 2 || (mod == 1 && !(cap > 0.0)) || (mod == 2 && !slopes)) return -1;
     bjob_t jb;
     memset(&jb, 0, sizeof jb);
     jb.q = q; jb.k = k; jb.v = v; jb.dout = dout; jb.dq = dq; jb.dk = dk; jb.dv = dv;
     jb.B = B; jb.H = H; jb.Nq = Nq; jb.Nk = Nk; jb.D = D; jb.wl = wl; jb.wr = wr; jb.scale = scale;
+    jb.mod = mod; jb.cap = cap; jb.slopes = slopes;
     pthread_mutex_init(&jb.lock, NULL);
     if (nthreads > 256) nthreads = 256;
     pthread_t tid[256];
@@ -339,4 +362,13 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
     for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
     pthread_mutex_destroy(&jb.lock);
     return 0;
+}
+
+/* The same without a score modifier. */
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv, long B, long H, long Nq, long Nk, long D,
+                    double scale, long wl, long wr, int nthreads)
+{
+    return oracle_attn_bwd_mod(q, k, v, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, wl, wr, 0, 0.0, NULL,
+                               nthreads);
 }

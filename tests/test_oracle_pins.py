@@ -330,6 +330,73 @@ def test_bwd_uniform_weights_give_mean_upstream_for_dv():
     assert torch.allclose(dV[0, 0], dO[0, 0].sum(0, keepdim=True).expand(Nk, D) / Nk, atol=1e-13)
 
 
+def fwd_loss_mod(Q, K, V, dO, scale, wl, wr, **mod):
+    """sum(dO * O) through the (pinned) forward oracle with a score modifier."""
+    O, _ = oracle.attention(Q, K, V, scale, window_left=wl, window_right=wr, **mod)
+    return float((O * dO).sum())
+
+
+BWD_MODS = [dict(score_mod="softcap", softcap=0.9), dict(score_mod="softcap", softcap=3.0),
+            dict(score_mod="alibi", alibi_slopes=[0.7, 0.05])]
+
+
+@pytest.mark.parametrize("mod", BWD_MODS, ids=["softcap0.9", "softcap3", "alibi"])
+@pytest.mark.parametrize("Nq,Nk,D,wl,wr", [(6, 6, 8, -1, 0), (5, 9, 8, -1, -1), (9, 5, 8, 2, 1)])
+def test_bwd_mod_matches_finite_differences_of_the_forward(mod, Nq, Nk, D, wl, wr):
+    B, H = 1, 2
+    Q, K, V = rnd((B, H, Nq, D), 45, 0), rnd((B, H, Nk, D), 45, 1), rnd((B, H, Nk, D), 45, 2)
+    dO = rnd((B, H, Nq, D), 45, 3)
+    scale = 0.7
+    dQ, dK, dV = oracle.attention_bwd(Q, K, V, dO, scale, wl, wr, **mod)
+    h = 1e-5
+    for X, G, tid in [(Q, dQ, 4), (K, dK, 5), (V, dV, 6)]:
+        E = rnd(X.shape, 46, tid)
+        X0 = X.clone()
+        X.add_(h * E)
+        fp = fwd_loss_mod(Q, K, V, dO, scale, wl, wr, **mod)
+        X.copy_(X0 - h * E)
+        fm = fwd_loss_mod(Q, K, V, dO, scale, wl, wr, **mod)
+        X.copy_(X0)
+        fd = (fp - fm) / (2 * h)
+        an = float((G * E).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (tid, fd, an)
+
+
+@pytest.mark.parametrize("mod", BWD_MODS, ids=["softcap0.9", "softcap3", "alibi"])
+@pytest.mark.parametrize("Nq,Nk,D,wl,wr", [(33, 33, 64, -1, 0), (40, 70, 64, -1, -1), (70, 40, 128, 5, 3)])
+def test_bwd_mod_matches_torch_autograd_float64(mod, Nq, Nk, D, wl, wr):
+    """The modifier written out in torch (cap tanh(S / cap); S + slope (j - i')) and differentiated by autograd."""
+    B, H = 1, 2
+    Q, K, V = rnd((B, H, Nq, D), 47, 0), rnd((B, H, Nk, D), 47, 1), rnd((B, H, Nk, D), 47, 2)
+    dO = rnd((B, H, Nq, D), 47, 3)
+    scale = 1.0 / math.sqrt(D)
+    s32 = float(torch.tensor(scale, dtype=torch.float32))
+    dQ, dK, dV = oracle.attention_bwd(Q, K, V, dO, scale, wl, wr, **mod)
+    keep = mask_matrix_window(Nq, Nk, wl, wr)
+    Qg, Kg, Vg = (t.clone().requires_grad_(True) for t in (Q, K, V))
+    S = torch.matmul(Qg, Kg.transpose(-1, -2)) * s32
+    if mod["score_mod"] == "softcap":
+        S = mod["softcap"] * torch.tanh(S / mod["softcap"])
+    else:
+        S = S + alibi_bias(Nq, Nk, mod["alibi_slopes"]).unsqueeze(0)
+    P = torch.nan_to_num(torch.softmax(S.masked_fill(~keep, -math.inf), dim=-1), nan=0.0)
+    torch.matmul(P, Vg).backward(dO)
+    for a, b in ((dQ, Qg.grad), (dK, Kg.grad), (dV, Vg.grad)):
+        assert torch.allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_bwd_mod_limits_reduce_to_plain_attention():
+    """Zero ALiBi slopes give the plain gradients bit for bit; a cap far above every score gives them to rounding."""
+    Q, K, V, dO = rnd((1, 2, 20, 16), 48, 0), rnd((1, 2, 25, 16), 48, 1), rnd((1, 2, 25, 16), 48, 2), \
+        rnd((1, 2, 20, 16), 48, 3)
+    plain = oracle.attention_bwd(Q, K, V, dO, 0.3, -1, 0)
+    zero = oracle.attention_bwd(Q, K, V, dO, 0.3, -1, 0, score_mod="alibi", alibi_slopes=[0.0, 0.0])
+    big = oracle.attention_bwd(Q, K, V, dO, 0.3, -1, 0, score_mod="softcap", softcap=1e8)
+    for a, b, c in zip(plain, zero, big):
+        assert torch.equal(a, b)
+        assert torch.allclose(a, c, rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------- closed forms
 
 @pytest.mark.parametrize("Nq,Nk,causal,window", [(40, 40, False, 0), (40, 40, True, 0), (40, 40, True, 7), (30, 50, True, 0)])
@@ -546,8 +613,14 @@ MUTANTS = {
                          "const double slope = jb->slopes[(bh + 1) % jb->H];"),
     "softcap_no_outer": ("s[j - lo] = jb->cap * tanh(s[j - lo] / jb->cap);", "s[j - lo] = tanh(s[j - lo] / jb->cap);"),
     "softcap_no_inner": ("s[j - lo] = jb->cap * tanh(s[j - lo] / jb->cap);", "s[j - lo] = jb->cap * tanh(s[j - lo]);"),
-    "bwd_ds_sign": ("const double ds = s[j - lo] * (dp[j - lo] - dv_row);",
-                    "const double ds = s[j - lo] * (dv_row - dp[j - lo]);"),
+    "bwd_ds_sign": ("const double dsm = s[j - lo] * (dp[j - lo] - dv_row);",
+                    "const double dsm = s[j - lo] * (dv_row - dp[j - lo]);"),
+    "bwd_softcap_no_chain": ("g[j - lo] = 1.0 - t * t;", "g[j - lo] = 1.0;"),
+    "bwd_softcap_chain_sign": ("g[j - lo] = 1.0 - t * t;", "g[j - lo] = 1.0 + t * t;"),
+    "bwd_softcap_no_outer": ("s[j - lo] = jb->cap * t;", "s[j - lo] = t;"),
+    "bwd_alibi_dropped": ("s[j - lo] += jb->slopes[bh % jb->H] * (double)(j - ip);", "s[j - lo] += 0.0;"),
+    "bwd_alibi_sign": ("s[j - lo] += jb->slopes[bh % jb->H] * (double)(j - ip);",
+                       "s[j - lo] += jb->slopes[bh % jb->H] * (double)(ip - j);"),
     "bwd_dq_no_scale": ("dQ[i * D + d] += jb->scale * ds * K[j * D + d];", "dQ[i * D + d] += ds * K[j * D + d];"),
     "bwd_dk_uses_k": ("dK[j * D + d] += jb->scale * ds * qi[d];", "dK[j * D + d] += jb->scale * ds * K[j * D + d];"),
     "bwd_dv_no_weight": ("for (long d = 0; d < D; ++d) dV[j * D + d] += p * doi[d];",
@@ -632,6 +705,21 @@ def pin_suite(lib) -> bool:
             X.copy_(X0)
             if abs((vals[0] - vals[1]) / 2e-5 - float((G * E).sum())) > 1e-6:
                 return False
+        # the backward with each score modifier against central differences of the modified forward
+        for mod in (dict(score_mod="softcap", softcap=0.9), dict(score_mod="alibi", alibi_slopes=[0.7])):
+            dQ, dK, dV = oracle.attention_bwd(Qb, Kb, Vb, dOb, 0.7, -1, 0, lib=lib, threads=1, **mod)
+            for X, G, tid in [(Qb, dQ, 4), (Kb, dK, 5), (Vb, dV, 6)]:
+                E = rnd(X.shape, 18, tid)
+                X0 = X.clone()
+                vals = []
+                for sgn in (1, -1):
+                    X.copy_(X0 + sgn * 1e-5 * E)
+                    O, _ = oracle.attention(Qb, Kb, Vb, 0.7, window_left=-1, window_right=0, lib=lib, threads=1,
+                                            **mod)
+                    vals.append(float((O * dOb).sum()))
+                X.copy_(X0)
+                if abs((vals[0] - vals[1]) / 2e-5 - float((G * E).sum())) > 1e-6:
+                    return False
         return True
     except RuntimeError:
         return False
