@@ -148,6 +148,7 @@ def cpu_baseline(w, inp, target_s=15.0):
 def cpu_baseline_bwd(w, inp, dout, target_s=15.0):
     """The oracle's backward, as it is, on whole heads of the workload, scaled to TFLOP/s."""
     import oracle
+    import synth
     threads = oracle.default_threads()
     wl = -1 if w.window_left is None else w.window_left
     wr = -1 if w.window_right is None else w.window_right
@@ -158,7 +159,11 @@ def cpu_baseline_bwd(w, inp, dout, target_s=15.0):
         b, h = divmod(n_heads, w.H)
         sl = (slice(b, b + 1), slice(h, h + 1))
         t0 = time.perf_counter()
-        oracle.attention_bwd(inp.q[sl], inp.k[sl], inp.v[sl], dout[sl], w.scale, wl, wr, threads=threads)
+        om = {}
+        if w.score_mod is not None:
+            om = dict(score_mod=w.score_mod, softcap=w.softcap,
+                      alibi_slopes=[synth.alibi_slopes(w.H)[h]] if w.score_mod == "alibi" else None)
+        oracle.attention_bwd(inp.q[sl], inp.k[sl], inp.v[sl], dout[sl], w.scale, wl, wr, threads=threads, **om)
         spent += time.perf_counter() - t0
         n_heads += 1
     fl = 10.0 * w.D * n_heads * visible_pairs_window(w.Nq, w.Nk, wl, wr)
@@ -172,7 +177,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw c3sc c3al c6 c3bwd")
+    ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw c3sc c3al c6 c3bwd c3scbwd c3albwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (to scale the FETCH_SIZE/WRITE_SIZE "
@@ -232,10 +237,14 @@ def main():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws_b = torch.empty(max(16, fa.bwd_workspace_bytes(w.B, w.H, w.Nq)), dtype=torch.uint8, device=dev)
 
+        bmod = {}
+        if w.score_mod is not None:
+            bmod = dict(score_mod=w.score_mod, softcap=w.softcap, alibi=mod.get("alibi"))
+
         def step():
             fa.attention_bwd(q, k, v, o, lse, do_d, scale=w.scale, causal=w.causal,
                              window_left=w.window_left, window_right=w.window_right,
-                             dq=dq, dk=dk, dv=dv, workspace=ws_b, stream=stream.cuda_stream)
+                             dq=dq, dk=dk, dv=dv, workspace=ws_b, stream=stream.cuda_stream, **bmod)
 
     for _ in range(args.warmup):
         step()

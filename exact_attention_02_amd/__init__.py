@@ -27,7 +27,7 @@ FA_ERR_MOD = 10
 FA_MOD_NONE, FA_MOD_SOFTCAP, FA_MOD_ALIBI = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_mod", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes",
-           "fa_splitkv_num_splits", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class",
+           "fa_splitkv_num_splits", "fa_bwd", "fa_bwd_mod", "fa_bwd_workspace_bytes", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class",
            "fa_plan_window_range", "fa_plan_block_class_window")
 
 _lib = None
@@ -65,6 +65,8 @@ def load(path: str = LIB_PATH):
     lib.fa_splitkv_num_splits.restype = I
     lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, P, LL]
     lib.fa_bwd.restype = I
+    lib.fa_bwd_mod.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, P, LL, I, F, P]
+    lib.fa_bwd_mod.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.fa_bwd_workspace_bytes.restype = LL
     lib.fa_status_str.argtypes = [I]
@@ -125,6 +127,13 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, scale, window_lef
            workspace, workspace_bytes) -> int:
     return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, scale, int(window_left),
                          int(window_right), dtype, stream, workspace, int(workspace_bytes))
+
+
+def fa_bwd_mod(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, scale, window_left, window_right, dtype,
+               stream, workspace, workspace_bytes, score_mod, softcap=0.0, alibi_slopes=None) -> int:
+    return load().fa_bwd_mod(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, scale, int(window_left),
+                             int(window_right), dtype, stream, workspace, int(workspace_bytes), int(score_mod),
+                             float(softcap), alibi_slopes)
 
 
 def bwd_workspace_bytes(B, H, Nq) -> int:
@@ -291,7 +300,7 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
 
 
 def attention_bwd(q, k, v, out, lse, dout, scale=None, causal=False, window_left=None, window_right=None,
-                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+                  dq=None, dk=None, dv=None, workspace=None, stream=None, score_mod=None, softcap=0.0, alibi=None):
     """dQ, dK, dV of O = softmax(scale Q K^T) V contracted with dout, via fa_bwd.
 
     q, out, dout [B,H,Nq,D], k and v [B,H,Nk,D]: contiguous float16 or bfloat16
@@ -300,6 +309,8 @@ def attention_bwd(q, k, v, out, lse, dout, scale=None, causal=False, window_left
     unbounded, window_right 0) or the extents of fa_fwd_window (None or -1:
     unbounded). workspace: a uint8 device tensor of at least
     bwd_workspace_bytes(B, H, Nq) bytes (allocated here when None).
+    score_mod, softcap, alibi: as in attention() (then through fa_bwd_mod; out
+    and lse must come from the forward with the same modifier).
     """
     import torch
     B, H, Nq, D = q.shape
@@ -331,9 +342,24 @@ def attention_bwd(q, k, v, out, lse, dout, scale=None, causal=False, window_left
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, D, float(scale), wl, wr, code, stream,
-                workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    if score_mod is None:
+        st = fa_bwd(*ptrs, B, H, Nq, Nk, D, float(scale), wl, wr, code, stream, *ws)
+        where = "fa_bwd"
+    else:
+        mod = {"softcap": FA_MOD_SOFTCAP, "alibi": FA_MOD_ALIBI, "none": FA_MOD_NONE}[score_mod]
+        slopes_ptr = None
+        if mod == FA_MOD_ALIBI:
+            if alibi is None:
+                alibi = torch.tensor(alibi_slopes(H), dtype=torch.float32, device=q.device)
+            if alibi.dtype != torch.float32 or alibi.numel() != H or not alibi.is_contiguous():
+                raise ValueError("alibi must be a contiguous float32 tensor of H slopes")
+            slopes_ptr = alibi.data_ptr()
+        st = fa_bwd_mod(*ptrs, B, H, Nq, Nk, D, float(scale), wl, wr, code, stream, *ws, mod, float(softcap),
+                        slopes_ptr)
+        where = "fa_bwd_mod"
     if st != FA_OK:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, where)
     return dq, dk, dv

@@ -243,9 +243,14 @@ long long fa_bwd_workspace_bytes(int B, int H, int Nq) {
     return 2 * (long long)B * H * nqp * 4;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
-           void* dk, void* dv, int B, int H, int Nq, int Nk, int D, float scale, int window_left, int window_right,
-           int dtype, void* stream, void* workspace, long long workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+            void* dk, void* dv, int B, int H, int Nq, int Nk, int D, float scale, int window_left, int window_right,
+            int dtype, void* stream, void* workspace, long long workspace_bytes, int mod, float cap,
+            const float* slopes) {
     DtypeInfo di;
     const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
     if (st != FA_OK) return st;
@@ -253,6 +258,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     int wl, wr;
     if (!window_extents(window_left, window_right, Nq, Nk, &wl, &wr)) return FA_ERR_MASK;
     if (!finite_positive(scale)) return FA_ERR_SCALE;
+    if (mod != FA_MOD_NONE && mod != FA_MOD_SOFTCAP && mod != FA_MOD_ALIBI) return FA_ERR_MOD;
+    if (mod == FA_MOD_SOFTCAP && !finite_positive(cap)) return FA_ERR_MOD;
     const long long n_bh = (long long)B * H;
     const long long n_qt = ((long long)Nq + 127) / 128, n_kt = ((long long)Nk + 127) / 128;
     if (n_bh * n_qt > 0x7fffffffLL || n_bh * n_kt > 0x7fffffffLL) return FA_ERR_SHAPE;
@@ -261,8 +268,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     if (n_bh == 0 || (Nq == 0 && Nk == 0)) return FA_OK;  // nothing to write
     if (Nq > 0 && (!q || !o || !dout || !lse || !dq || !workspace)) return FA_ERR_NULL;
     if (Nk > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
+    if (mod == FA_MOD_ALIBI && !slopes) return FA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
-        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16) || !aligned(lse, 4))
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(workspace, 16) || !aligned(lse, 4) ||
+        !aligned(slopes, 4))
         return FA_ERR_ALIGN;
     if (Nq > 0 && workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq)) return FA_ERR_SHAPE;
     const int dst = check_device();
@@ -290,8 +299,32 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     p.n_kt = (int)n_kt;
     p.c = scale * 1.44269504088896341f;
     p.scale = scale;
+    p.H = H;
+    p.mod = mod;
+    p.mk1 = (mod == FA_MOD_SOFTCAP) ? 2.f * p.c / cap : 0.f;
+    p.mk2 = (mod == FA_MOD_SOFTCAP) ? cap * 1.44269504088896341f : 0.f;
+    p.slopes = slopes;
     (void)hipGetLastError();
     return fa::launch_bwd(di.in, D, p, stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int Nq, int Nk, int D, float scale, int window_left, int window_right,
+           int dtype, void* stream, void* workspace, long long workspace_bytes) {
+    return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, scale, window_left, window_right, dtype,
+                   stream, workspace, workspace_bytes, FA_MOD_NONE, 0.f, nullptr);
+}
+
+int fa_bwd_mod(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int D, float scale, int window_left,
+               int window_right, int dtype, void* stream, void* workspace, long long workspace_bytes, int score_mod,
+               float softcap, const float* alibi_slopes) {
+    return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, scale, window_left, window_right, dtype,
+                   stream, workspace, workspace_bytes, score_mod, softcap, alibi_slopes);
 }
 
 const char* fa_status_str(int status) {

@@ -9,7 +9,10 @@
 // P = exp(scale S - LSE):
 //   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - Dvec),
 //   dQ = scale dS K,   dK = scale dS^T Q,
-// where Dvec_i = dO_i . O_i is the row sum of P o dP.
+// where Dvec_i = dO_i . O_i is the row sum of P o dP. With a score modifier f
+// (softcap s <- cap tanh(s / cap), ALiBi s <- s + slope (j - i'); the
+// FLASHLIGHT summary's score_mod variants) P is the softmax of the modified
+// scores and dS picks up f'(s) by the chain rule: 1 - tanh^2 for softcap.
 //
 // Three kernels:
 //   * fa_bwd_rowstat_kernel: -Dvec and the LSE in base-2 units per row;
@@ -112,9 +115,31 @@ __device__ __forceinline__ f32x4v lds_readf4(const lds_u8* a) {
     return *reinterpret_cast<const __attribute__((address_space(3))) f32x4v*>(a);
 }
 
+// The weight 2^(f(s) - LSE) of a score s (base-2 units: the scaled score is
+// c s) and the chain factor g = f'. e is the exponent's additive part: -LSE
+// in base-2 units, plus the ALiBi bias. Softcap: u = e^(2|x|) with
+// x = scale s / cap (k1 = 2 c / cap), tanh|x| = 1 - 2 r with r = 1 / (u + 1),
+// f = cap log2(e) tanh(x) (k2 = cap log2(e)), and 1 - tanh^2 = 4 r (1 - r),
+// which has no cancellation and is 0 where u overflows. A masked score
+// (-inf) has weight 0 under every modifier.
+template <int MOD>
+__device__ __forceinline__ float mod_weight(float s, float c2, float k1, float k2, float e, float& g) {
+    if constexpr (MOD == MOD_SOFTCAP) {
+        const float u = __builtin_amdgcn_exp2f(fabsf(s) * k1);
+        const float r = __builtin_amdgcn_rcpf(u + 1.f);
+        const float t = fmaf(-2.f, r, 1.f);
+        g = 4.f * r * (1.f - r);
+        const float a = fmaf(__builtin_copysignf(t, s), k2, e);
+        return (s == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(a);
+    } else {
+        g = 1.f;
+        return __builtin_amdgcn_exp2f(fmaf(s, c2, e));
+    }
+}
+
 // ---------------------------------------------------------------- dQ
 
-template <int IN, int D>
+template <int IN, int D, int MOD>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
     using T = TileShape<D>;
     constexpr int RB = T::RB, CPR = T::CPR, TILE = T::TILE, SLOT = T::SLOT, NKS = T::NKS, ND = T::ND;
@@ -151,6 +176,9 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
     const float l2 = (row < Nq) ? p.l2[(size_t)bh * p.nqp + row] : INFINITY;
     const float ndv = (row < Nq) ? p.ndvec[(size_t)bh * p.nqp + row] : 0.f;
     const float c2 = p.c;
+    const float k1 = p.mk1, k2 = p.mk2;   // softcap constants
+    float slope2 = 0.f;                   // ALiBi: this head's slope * log2(e)
+    if constexpr (MOD == MOD_ALIBI) slope2 = p.slopes[bh % p.H] * LOG2E;
 #if FA_BWD_DQ_DINIT
     f32x16 dinit;
 #pragma unroll
@@ -233,15 +261,21 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
                     S[r] = (off < a || off >= b) ? -INFINITY : S[r];
                 }
             }
+            // ALiBi: key - i' = 32j + 4hh - i' (per lane) + 8(r/4) + r%4
+            float ab = -l2;
+            if constexpr (MOD == MOD_ALIBI) ab = fmaf(slope2, (float)(32 * j + 4 * hh - (row + Nk - Nq)), -l2);
             float ds[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pr = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -l2));
+                float e = ab, g;
+                if constexpr (MOD == MOD_ALIBI) e = fmaf(slope2, (float)(8 * (r >> 2) + (r & 3)), ab);
+                const float pr = mod_weight<MOD>(S[r], c2, k1, k2, e, g);
 #if FA_BWD_DQ_DINIT
                 ds[r] = pr * dP[r];
 #else
                 ds[r] = pr * (dP[r] + ndv);
 #endif
+                if constexpr (MOD == MOD_SOFTCAP) ds[r] *= g;
             }
             i32x4 dsb[2];
 #pragma unroll
@@ -288,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------- dK, dV
 
 // D = 128 holds 128 accumulator registers for dK^T and dV^T: one wave per SIMD.
-template <int IN, int D>
+template <int IN, int D, int MOD>
 __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(BwdParams p) {
     using T = TileShape<D>;
     constexpr int RB = T::RB, CPR = T::CPR, TILE = T::TILE, SLOT = T::SLOT, NKS = T::NKS, ND = T::ND;
@@ -342,6 +376,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
                                      : rsrc_words(p.l2 + (size_t)bh * p.nqp, (unsigned)(p.nqp * 4));
     const unsigned stat_voff = (lane < 16) ? (unsigned)(16 * lane) : (1u << 30);
     const float c2 = p.c;
+    const float k1 = p.mk1, k2 = p.mk2;   // softcap constants
+    float slope2 = 0.f;                   // ALiBi: this head's slope * log2(e)
+    if constexpr (MOD == MOD_ALIBI) slope2 = p.slopes[bh % p.H] * LOG2E;
     // the lane's key sees the rows [klo_q, khi_q)
     int klo_q = key - wr - dlt, khi_q = key + wl - dlt + 1;
     klo_q = klo_q > 0 ? klo_q : 0;
@@ -423,10 +460,14 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
             S[r] = (off < a || off >= b) ? -INFINITY : S[r];
         }
     };
-    // P = 2^(c S - LSE) and dS = P (dP - Dvec), rounded to the MFMA type
-    auto softmax = [&](auto slot_c, int sub, const f32x16& S, const f32x16& dP, i32x4(&pb)[2], i32x4(&db2)[2])
-        __attribute__((always_inline)) {
+    // P = 2^(f(c S) - LSE) and dS = P (dP - Dvec) f', rounded to the MFMA type;
+    // rows q0 .. q0 + 31 of the sub-tile
+    auto softmax = [&](auto slot_c, int sub, int q0, const f32x16& S, const f32x16& dP, i32x4(&pb)[2],
+                       i32x4(&db2)[2]) __attribute__((always_inline)) {
         constexpr int SB = decltype(slot_c)::value * SLOTK + SLOT;
+        // ALiBi: key - i' = key - q0 - 4hh - (Nk - Nq) (per lane) - 8(r/4) - r%4
+        float bb = 0.f;
+        if constexpr (MOD == MOD_ALIBI) bb = slope2 * (float)(key - q0 - 4 * hh - dlt);
         float pr[16], ds[16];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
@@ -434,8 +475,11 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * gq + e;
-                pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -L[e]));
+                float ex = -L[e], g;
+                if constexpr (MOD == MOD_ALIBI) ex = fmaf(-slope2, (float)(8 * gq + e), bb) - L[e];
+                pr[r] = mod_weight<MOD>(S[r], c2, k1, k2, ex, g);
                 ds[r] = pr[r] * dP[r];
+                if constexpr (MOD == MOD_SOFTCAP) ds[r] *= g;
             }
         }
 #pragma unroll
@@ -490,7 +534,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
             i32x4 pb[2], db2[2];
             scores(slot_c, sub, S, dP);
             if (cls != TILE_FULL) mask(BC * t + 32 * sub, S);
-            softmax(slot_c, sub, S, dP, pb, db2);
+            softmax(slot_c, sub, BC * t + 32 * sub, S, dP, pb, db2);
             accumulate(slot_c, sub, pb, db2);
         }
     };
@@ -522,7 +566,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
 
 // ---------------------------------------------------------------- host side
 
-template <int IN, int D>
+template <int IN, int D, int MOD>
 static int launch_bwd_d(const BwdParams& p, hipStream_t s) {
     const long long rows = (long long)p.n_bh * p.nqp;
     constexpr int RPB = 256 / (D / 8);
@@ -530,17 +574,30 @@ static int launch_bwd_d(const BwdParams& p, hipStream_t s) {
         hipLaunchKernelGGL((fa_bwd_rowstat_kernel<IN, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s,
                            p);
     if (p.n_bh * (long long)p.n_qt > 0)
-        hipLaunchKernelGGL((fa_bwd_dq_kernel<IN, D>), dim3((unsigned)(p.n_bh * (long long)p.n_qt)), dim3(256), 0, s, p);
-    if (p.n_bh * (long long)p.n_kt > 0)
-        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<IN, D>), dim3((unsigned)(p.n_bh * (long long)p.n_kt)), dim3(256), 0, s,
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<IN, D, MOD>), dim3((unsigned)(p.n_bh * (long long)p.n_qt)), dim3(256), 0, s,
                            p);
+    if (p.n_bh * (long long)p.n_kt > 0)
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<IN, D, MOD>), dim3((unsigned)(p.n_bh * (long long)p.n_kt)), dim3(256), 0,
+                           s, p);
     return (int)hipGetLastError();
+}
+
+template <int IN, int MOD>
+static int launch_bwd_m(int D, const BwdParams& p, hipStream_t s) {
+    return D == 64 ? launch_bwd_d<IN, 64, MOD>(p, s) : launch_bwd_d<IN, 128, MOD>(p, s);
+}
+
+template <int IN>
+static int launch_bwd_i(int D, const BwdParams& p, hipStream_t s) {
+    if (p.mod == MOD_SOFTCAP) return launch_bwd_m<IN, MOD_SOFTCAP>(D, p, s);
+    if (p.mod == MOD_ALIBI) return launch_bwd_m<IN, MOD_ALIBI>(D, p, s);
+    return launch_bwd_m<IN, MOD_NONE>(D, p, s);
 }
 
 int launch_bwd(int in, int D, const BwdParams& p, void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (in == IN_BF16) return D == 64 ? launch_bwd_d<IN_BF16, 64>(p, s) : launch_bwd_d<IN_BF16, 128>(p, s);
-    if (in == IN_F16) return D == 64 ? launch_bwd_d<IN_F16, 64>(p, s) : launch_bwd_d<IN_F16, 128>(p, s);
+    if (in == IN_BF16) return launch_bwd_i<IN_BF16>(D, p, s);
+    if (in == IN_F16) return launch_bwd_i<IN_F16>(D, p, s);
     return (int)hipErrorInvalidValue;
 }
 

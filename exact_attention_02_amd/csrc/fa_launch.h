@@ -63,6 +63,10 @@ struct BwdParams {
     int n_kt;       // 128-key blocks per head (dK/dV kernel)
     float c;        // scale * log2(e)
     float scale;
+    int H;          // heads (ALiBi: the head of bh is bh % H)
+    int mod;        // MOD_NONE, MOD_SOFTCAP or MOD_ALIBI
+    float mk1, mk2; // softcap constants: 2 * c / cap and cap * log2(e)
+    const float* slopes;  // ALiBi: [H] device array of per-head slopes
 };
 
 // Enqueues the three backward kernels on `stream`; returns hipGetLastError().

@@ -206,11 +206,27 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  *   or -1 for negative sizes.
  */
 long long fa_bwd_workspace_bytes(int B, int H, int Nq);
+/*
+ * fa_bwd_mod: fa_bwd for the attention of fa_fwd_mod, whose scores pass
+ * through a modifier f before the softmax (score_mod, softcap and
+ * alibi_slopes as in fa_fwd_mod; o and lse must come from fa_fwd_mod with the
+ * same modifier). P is the softmax of the modified scores and dS picks up
+ * f'(s) by the chain rule: 1 - tanh(s / cap)^2 for FA_MOD_SOFTCAP, 1 for
+ * FA_MOD_ALIBI. Errors as fa_bwd, plus FA_ERR_MOD for an unknown modifier or
+ * a softcap that is not finite and positive, FA_ERR_NULL for a NULL
+ * alibi_slopes with FA_MOD_ALIBI, FA_ERR_ALIGN if it is not 4-byte aligned.
+ */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int Nq, int Nk, int D, float scale,
            int window_left, int window_right, int dtype, void* stream,
            void* workspace, long long workspace_bytes);
+int fa_bwd_mod(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv,
+               int B, int H, int Nq, int Nk, int D, float scale,
+               int window_left, int window_right, int dtype, void* stream,
+               void* workspace, long long workspace_bytes,
+               int score_mod, float softcap, const float* alibi_slopes);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -200,6 +200,11 @@ WORKLOADS = {
     # an upstream gradient dO (make_grad_out), O and the LSE.
     "c3bwd": Workload("c3_backward_causal_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, True, 0, "bf16", "bf16", 3,
                       backward=True),
+    # The backward of the softcap and ALiBi workloads.
+    "c3scbwd": Workload("c3_backward_causal_softcap50_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, True, 0, "bf16",
+                        "bf16", 3, score_mod="softcap", softcap=50.0, backward=True),
+    "c3albwd": Workload("c3_backward_causal_alibi_B4H12N8192D64_bf16", 4, 12, 8192, 8192, 64, True, 0, "bf16", "bf16",
+                        3, score_mod="alibi", backward=True),
 }
 
 

@@ -162,6 +162,31 @@ def test_bwd_argument_errors_before_any_device_work(kw, code):
     assert bwd_call(**kw) == code
 
 
+def test_bwd_mod_entry_checks_modifier_and_parameters():
+    a = (P, P, P, P, P, P, P, P, P, 1, 2, 64, 96, 64, 0.125, -1, 0, fa.FA_BF16, None, P,
+         fa.bwd_workspace_bytes(1, 2, 64))
+    assert fa.fa_bwd_mod(*a, 3, 0.0, None) == fa.FA_ERR_MOD
+    assert fa.fa_bwd_mod(*a, -1, 0.0, None) == fa.FA_ERR_MOD
+    assert fa.fa_bwd_mod(*a, fa.FA_MOD_SOFTCAP, 0.0, None) == fa.FA_ERR_MOD
+    assert fa.fa_bwd_mod(*a, fa.FA_MOD_SOFTCAP, float("nan"), None) == fa.FA_ERR_MOD
+    assert fa.fa_bwd_mod(*a, fa.FA_MOD_ALIBI, 0.0, None) == fa.FA_ERR_NULL
+    assert fa.fa_bwd_mod(*a, fa.FA_MOD_ALIBI, 0.0, P + 2) == fa.FA_ERR_ALIGN
+    b = list(a)
+    b[17] = fa.FA_E4M3
+    assert fa.fa_bwd_mod(*b, fa.FA_MOD_SOFTCAP, 30.0, None) == fa.FA_ERR_DTYPE
+    c = list(a)
+    c[9] = 0   # B = 0: nothing to do, no pointer needed
+    assert fa.fa_bwd_mod(*c, fa.FA_MOD_ALIBI, 0.0, None) == fa.FA_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_bwd_mod_valid_call_without_gpu_reports_device_error():
+    a = (P, P, P, P, P, P, P, P, P, 1, 2, 64, 96, 64, 0.125, -1, 0, fa.FA_BF16, None, P,
+         fa.bwd_workspace_bytes(1, 2, 64))
+    assert fa.fa_bwd_mod(*a, fa.FA_MOD_SOFTCAP, 30.0, None) == fa.FA_ERR_DEVICE
+    assert fa.fa_bwd_mod(*a, fa.FA_MOD_ALIBI, 0.0, P) == fa.FA_ERR_DEVICE
+
+
 def test_bwd_empty_problems_need_no_device():
     assert bwd_call(B=0) == fa.FA_OK
     assert bwd_call(H=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, ws=0) == fa.FA_OK

@@ -13,14 +13,24 @@ that matter are:
     O), so |dD_i| <= u A_i with A_i = sum_d |dO_id| ((P|V|)_id + |O_id|); it
     enters dS as P_ij dD_i;
   * the outputs rounded to the input type (relative u).
-To first order, elementwise,
-  |dV - dV_ref| <= u (P^T|dO|) + u |dV_ref|
-  |dQ - dQ_ref| <= u scale (|dS||K| + A o (P|K|)) + u |dQ_ref|
-  |dK - dK_ref| <= u scale (|dS|^T|Q| + (P o A)^T |Q|) + u |dK_ref|
+Below the smallest normal number a rounding is off by up to eta absolute
+instead (half the smallest subnormal: 2^-25 for float16; negligible for
+bfloat16, whose range is float32's); small weights and dS entries reach it
+under steep ALiBi biases. With V_ij = 1 for a visible pair, to first order,
+elementwise,
+  |dV - dV_ref| <= u (P^T|dO|) + eta (V^T|dO|) + u |dV_ref| + eta
+  |dQ - dQ_ref| <= u scale (|dS||K| + A o (P|K|)) + eta scale (V|K|) + u |dQ_ref| + eta
+  |dK - dK_ref| <= u scale (|dS|^T|Q| + (P o A)^T |Q|) + eta scale (V^T|Q|) + u |dK_ref| + eta
 fp32 accumulation and the fp32 exponential add terms below 1e-5 of these.
 The test allows twice the first-order bound plus 1e-6. The magnitude arrays
 P, dS, A are evaluated here in float64 from the inputs; they set the
 tolerance only, the expected values are the oracle's.
+
+With a score modifier f (softcap, ALiBi) P is the softmax of f(scale S) and
+dS carries g = f'(scale S): the same bound holds with |dS| the modified
+gradient and P o g in place of P in the stored-O term. The fp32 tanh and bias
+add exponent errors below 1e-5 relative to the weights at the caps and slopes
+tested, well inside u.
 
 Rows that see no key must give dQ = 0 exactly; keys that no row sees must give
 dK = dV = 0 exactly.
@@ -38,6 +48,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 UNIT = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+ETA = {"bf16": 0.0, "f16": 2.0 ** -25}
 
 
 def visible(Nq, Nk, wl, wr):
@@ -51,11 +62,19 @@ def visible(Nq, Nk, wl, wr):
     return vis
 
 
-def head_tolerance(Q, K, V, O, dO, dQr, dKr, dVr, scale, wl, wr, u):
+def head_tolerance(Q, K, V, O, dO, dQr, dKr, dVr, scale, wl, wr, u, mod=None, cap=0.0, slope=0.0, eta=0.0):
     """Elementwise allowed |error| of dQ, dK, dV for one head (float64 2-D inputs)."""
     Nq, Nk = Q.shape[0], K.shape[0]
     vis = visible(Nq, Nk, wl, wr)
     S = (Q @ K.T) * scale
+    g = torch.ones_like(S)
+    if mod == "softcap":
+        t = torch.tanh(S / cap)
+        S, g = cap * t, 1.0 - t * t
+    elif mod == "alibi":
+        i = torch.arange(Nq, dtype=torch.float64)[:, None] + (Nk - Nq)
+        j = torch.arange(Nk, dtype=torch.float64)[None, :]
+        S = S + slope * (j - i)
     S = S.masked_fill(~vis, -math.inf)
     m = S.max(dim=1, keepdim=True).values
     m = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
@@ -64,20 +83,37 @@ def head_tolerance(Q, K, V, O, dO, dQr, dKr, dVr, scale, wl, wr, u):
     P = E / E.sum(dim=1, keepdim=True).clamp_min(1e-300)
     del E
     dP = dO @ V.T
-    dS = P * (dP - (P * dP).sum(dim=1, keepdim=True))
+    dS = P * (dP - (P * dP).sum(dim=1, keepdim=True)) * g
     del dP
     A = (dO.abs() * (P @ V.abs() + O.abs())).sum(dim=1)
     bV = P.T @ dO.abs()
-    bQ = scale * (dS.abs() @ K.abs() + A[:, None] * (P @ K.abs()))
-    bK = scale * (dS.abs().T @ Q.abs() + (P * A[:, None]).T @ Q.abs())
-    return [2.0 * u * (b + r.abs()) + 1e-6 for b, r in ((bQ, dQr), (bK, dKr), (bV, dVr))]
+    Pg = P * g
+    bQ = scale * (dS.abs() @ K.abs() + A[:, None] * (Pg @ K.abs()))
+    bK = scale * (dS.abs().T @ Q.abs() + (Pg * A[:, None]).T @ Q.abs())
+    Vm = vis.to(torch.float64)
+    fQ = scale * (Vm @ K.abs()) + 1.0
+    fK = scale * (Vm.T @ Q.abs()) + 1.0
+    fV = Vm.T @ dO.abs() + 1.0
+    return [2.0 * (u * (b + r.abs()) + eta * f) + 1e-6
+            for b, r, f in ((bQ, dQr, fQ), (bK, dKr, fK), (bV, dVr, fV))]
+
+
+def mod_args(w):
+    """The score modifier of a workload as attention() / attention_bwd() keyword arguments."""
+    if w.score_mod is None:
+        return {}
+    m = dict(score_mod=w.score_mod, softcap=w.softcap)
+    if w.score_mod == "alibi":
+        m["alibi"] = torch.tensor(synth.alibi_slopes(w.H), dtype=torch.float32, device=DEV)
+    return m
 
 
 def run(w, wl, wr, q, k, v, do):
     """Forward (for O and LSE) then backward on the GPU; returns host tensors."""
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
-    o, lse = fa.attention(qd, kd, vd, scale=w.scale, window_left=wl, window_right=wr)
-    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, window_left=wl, window_right=wr)
+    o, lse = fa.attention(qd, kd, vd, scale=w.scale, window_left=wl, window_right=wr, **mod_args(w))
+    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, lse, dod, scale=w.scale, window_left=wl, window_right=wr,
+                                  **mod_args(w))
     torch.cuda.synchronize()
     return o.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
 
@@ -89,13 +125,20 @@ def check(w, wl, wr, q, k, v, do, o, dq, dk, dv, heads=None, ref=None):
     worst = 0.0
     for b, h in heads:
         sl = (slice(b, b + 1), slice(h, h + 1))
+        om = {}
+        if w.score_mod is not None:
+            om = dict(score_mod=w.score_mod, softcap=w.softcap,
+                      alibi_slopes=[synth.alibi_slopes(w.H)[h]] if w.score_mod == "alibi" else None)
         if ref is None:
-            dQr, dKr, dVr = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], w.scale, wl, wr)
+            dQr, dKr, dVr = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], w.scale, wl, wr, **om)
         else:
             dQr, dKr, dVr = (t[sl] for t in ref)
         dQr, dKr, dVr = dQr[0, 0], dKr[0, 0], dVr[0, 0]
         Q, K, V, dO = (oracle.decode(t[b, h]) for t in (q, k, v, do))
-        tq, tk, tv = head_tolerance(Q, K, V, oracle.decode(o[b, h]), dO, dQr, dKr, dVr, w.scale, wl, wr, u)
+        s32 = float(torch.tensor(w.scale, dtype=torch.float32))
+        slope = synth.alibi_slopes(w.H)[h] if w.score_mod == "alibi" else 0.0
+        tq, tk, tv = head_tolerance(Q, K, V, oracle.decode(o[b, h]), dO, dQr, dKr, dVr, s32, wl, wr, u,
+                                    mod=w.score_mod, cap=w.softcap, slope=slope, eta=ETA[w.in_dtype])
         for name, got, exp, tol in (("dQ", dq[b, h], dQr, tq), ("dK", dk[b, h], dKr, tk),
                                     ("dV", dv[b, h], dVr, tv)):
             err = (got.double() - exp).abs()
@@ -227,3 +270,56 @@ def test_bwd_masked_positions_are_exact(dt):
     pq = grads(q2, inp.k, inp.v, do2)
     for a, b in ((base[1], pq[1]), (base[2], pq[2])):
         assert torch.equal(a[:, :, 100:].view(torch.int16), b[:, :, 100:].view(torch.int16))
+
+
+# (name, B, H, Nq, Nk, D, window_left, window_right, dtype, modifier, cap)
+MOD_CASES = [
+    ("softcap50_causal", 1, 2, 300, 300, 64, -1, 0, "bf16", "softcap", 50.0),
+    ("softcap2_full_f16", 1, 2, 257, 300, 64, -1, -1, "f16", "softcap", 2.0),
+    ("softcap0.5_window_d128", 1, 2, 300, 300, 128, 40, 40, "bf16", "softcap", 0.5),
+    ("softcap3_nq_gt_nk_f16", 1, 1, 333, 200, 64, -1, 0, "f16", "softcap", 3.0),
+    ("alibi_causal", 1, 3, 300, 300, 64, -1, 0, "bf16", "alibi", 0.0),
+    ("alibi_full_f16_d128", 1, 2, 200, 333, 128, -1, -1, "f16", "alibi", 0.0),
+    ("alibi_window", 2, 2, 129, 400, 64, 50, 0, "bf16", "alibi", 0.0),
+    ("alibi_1k_f16", 1, 2, 1100, 1100, 64, -1, 0, "f16", "alibi", 0.0),
+]
+
+
+@pytest.mark.parametrize("case", MOD_CASES, ids=[c[0] for c in MOD_CASES])
+def test_bwd_mod_parity(case):
+    name, B, H, Nq, Nk, D, wl, wr, dt, mod, cap = case
+    w = synth.small_workload("bwd_" + name, B, H, Nq, Nk, D, False, 0, dt, dt, 51 + len(name), score_mod=mod,
+                             softcap=cap, backward=True)
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w)
+    print(f"case {name} B{B} H{H} Nq{Nq} Nk{Nk} D{D} wl{wl} wr{wr} {dt} {mod} {cap}", flush=True)
+    o, dq, dk, dv = run(w, wl, wr, inp.q, inp.k, inp.v, do)
+    check(w, wl, wr, inp.q, inp.k, inp.v, do, o, dq, dk, dv)
+
+
+def test_bwd_alibi_with_zero_slopes_is_bitwise_plain():
+    w = synth.small_workload("bwd_alibi0", 1, 2, 300, 300, 64, True, 0, "bf16", "bf16", 13, backward=True)
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w)
+    q, k, v, dod = (t.to(DEV) for t in (inp.q, inp.k, inp.v, do))
+    o, lse = fa.attention(q, k, v, scale=w.scale, causal=True)
+    plain = fa.attention_bwd(q, k, v, o, lse, dod, scale=w.scale, causal=True)
+    zero = torch.zeros(2, dtype=torch.float32, device=DEV)
+    mod = fa.attention_bwd(q, k, v, o, lse, dod, scale=w.scale, causal=True, score_mod="alibi", alibi=zero)
+    torch.cuda.synchronize()
+    for a, b in zip(plain, mod):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["c3sc", "c3al"])
+def test_bwd_mod_full_size_sampled_heads(name):
+    """The c3 softcap and ALiBi workloads' backward at full size, two heads compared in full
+    (ALiBi: the steepest and the shallowest slope)."""
+    base = synth.WORKLOADS[name]
+    w = synth.Workload(base.name + "_backward", base.B, base.H, base.Nq, base.Nk, base.D, True, 0, base.in_dtype,
+                       base.out_dtype, base.seed, score_mod=base.score_mod, softcap=base.softcap, backward=True)
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w)
+    print(f"full size {w.name}", flush=True)
+    o, dq, dk, dv = run(w, -1, 0, inp.q, inp.k, inp.v, do)
+    check(w, -1, 0, inp.q, inp.k, inp.v, do, o, dq, dk, dv, heads=[(0, 0), (w.B - 1, w.H - 1)])
