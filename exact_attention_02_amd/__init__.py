@@ -363,3 +363,54 @@ def attention_bwd(q, k, v, out, lse, dout, scale=None, causal=False, window_left
     if st != FA_OK:
         raise FaError(st, where)
     return dq, dk, dv
+
+
+_autograd_fn = None
+
+
+def _flash_fn():
+    """The autograd Function (built on first use, so that importing the package does not import torch)."""
+    global _autograd_fn
+    if _autograd_fn is None:
+        import torch
+
+        class FlashAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, scale, window_left, window_right, score_mod, softcap, alibi):
+                o, lse = attention(q, k, v, scale=scale, window_left=window_left, window_right=window_right,
+                                   score_mod=score_mod, softcap=softcap, alibi=alibi)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.args = (scale, window_left, window_right, score_mod, softcap, alibi)
+                return o
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, o, lse = ctx.saved_tensors
+                scale, wl, wr, score_mod, softcap, alibi = ctx.args
+                dq, dk, dv = attention_bwd(q, k, v, o, lse, dout.contiguous(), scale=scale, window_left=wl,
+                                           window_right=wr, score_mod=score_mod, softcap=softcap, alibi=alibi)
+                return dq, dk, dv, None, None, None, None, None, None
+
+        _autograd_fn = FlashAttention
+    return _autograd_fn
+
+
+def flash_attention(q, k, v, scale=None, causal=False, window_left=None, window_right=None, score_mod=None,
+                    softcap=0.0, alibi=None):
+    """O = softmax(f(scale Q K^T)) V as a differentiable torch operation: the
+    forward through fa_fwd_window / fa_fwd_mod, the backward through fa_bwd /
+    fa_bwd_mod with the saved O and LSE. float16 or bfloat16 inputs
+    [B,H,Nq,D], [B,H,Nk,D]; the mask is causal or the extents (None or -1:
+    open side); score_mod, softcap, alibi as in attention()."""
+    import math as _m
+    if scale is None:
+        scale = 1.0 / _m.sqrt(q.shape[-1])
+    if window_left is None and window_right is None:
+        wl, wr = -1, (0 if causal else -1)
+    else:
+        wl = -1 if window_left is None else int(window_left)
+        wr = -1 if window_right is None else int(window_right)
+    if score_mod == "alibi" and alibi is None:
+        import torch
+        alibi = torch.tensor(alibi_slopes(q.shape[1]), dtype=torch.float32, device=q.device)
+    return _flash_fn().apply(q, k, v, float(scale), wl, wr, score_mod, float(softcap), alibi)

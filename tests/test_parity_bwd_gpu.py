@@ -323,3 +323,23 @@ def test_bwd_mod_full_size_sampled_heads(name):
     print(f"full size {w.name}", flush=True)
     o, dq, dk, dv = run(w, -1, 0, inp.q, inp.k, inp.v, do)
     check(w, -1, 0, inp.q, inp.k, inp.v, do, o, dq, dk, dv, heads=[(0, 0), (w.B - 1, w.H - 1)])
+
+
+@pytest.mark.parametrize("mod", [None, "softcap", "alibi"])
+def test_flash_attention_autograd_matches_the_c_calls(mod):
+    """flash_attention's autograd backward is fa_bwd / fa_bwd_mod on the saved O and LSE, bit for bit."""
+    w = synth.small_workload("autograd", 1, 2, 200, 200, 64, True, 0, "bf16", "bf16", 14, score_mod=mod,
+                             softcap=5.0 if mod == "softcap" else 0.0, backward=True)
+    inp = synth.make_inputs(w)
+    do = synth.make_grad_out(w).to(DEV)
+    q, k, v = (t.to(DEV).requires_grad_(True) for t in (inp.q, inp.k, inp.v))
+    m = mod_args(w)
+    o = fa.flash_attention(q, k, v, scale=w.scale, causal=True, **m)
+    o.backward(do)
+    with torch.no_grad():
+        o2, lse = fa.attention(q.detach(), k.detach(), v.detach(), scale=w.scale, window_left=-1, window_right=0, **m)
+        ref = fa.attention_bwd(q.detach(), k.detach(), v.detach(), o2, lse, do, scale=w.scale, causal=True, **m)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach().view(torch.int16), o2.view(torch.int16))
+    for g, r in zip((q.grad, k.grad, v.grad), ref):
+        assert torch.equal(g.view(torch.int16), r.view(torch.int16))
