@@ -187,6 +187,20 @@ def test_bwd_mod_valid_call_without_gpu_reports_device_error():
     assert fa.fa_bwd_mod(*a, fa.FA_MOD_ALIBI, 0.0, P) == fa.FA_ERR_DEVICE
 
 
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU path")
+def test_largest_head_is_accepted_and_one_more_row_is_not():
+    """One head's rows must stay below 2^31 bytes at 4 bytes per element: at D = 64 that is 2^23 - 1 rows."""
+    n = (1 << 23) - 1
+    assert call(Nq=64, Nk=n) == fa.FA_ERR_DEVICE
+    assert call(Nq=64, Nk=n + 1) == fa.FA_ERR_SHAPE
+    assert call(Nq=n, Nk=64) == fa.FA_ERR_DEVICE
+    assert call(Nq=n + 1, Nk=64) == fa.FA_ERR_SHAPE
+    assert call(Nq=64, Nk=(1 << 22) - 1, D=128) == fa.FA_ERR_DEVICE
+    assert call(Nq=64, Nk=1 << 22, D=128) == fa.FA_ERR_SHAPE
+    assert bwd_call(Nq=64, Nk=n) == fa.FA_ERR_DEVICE
+    assert bwd_call(Nq=64, Nk=n + 1) == fa.FA_ERR_SHAPE
+
+
 def test_bwd_empty_problems_need_no_device():
     assert bwd_call(B=0) == fa.FA_OK
     assert bwd_call(H=0, q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, ws=0) == fa.FA_OK
