@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_fwd16.hip", "fa_bwd.hip", "fa_api.hip"]
+SOURCES = ["fa_fwd.hip", "fa_fwd16.hip", "fa_fwd_ks.hip", "fa_bwd.hip", "fa_api.hip"]
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32.
 HIPFLAGS = [

@@ -419,6 +419,9 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
 
 // ---------------------------------------------------------------- host side
 
+#ifndef FA_KS_MAX_WG
+#define FA_KS_MAX_WG 128
+#endif
 Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool pipe16) {
     Plan pl;
     pl.in = in;
@@ -428,11 +431,21 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool pipe1
     const long long n_bh = (long long)B * H;
     // 16-bit inputs use the pipelined kernel: 4 waves at D = 64, 8 waves at
     // D = 128 (its three 32 KiB LDS slots then serve 256 query rows). e4m3
-    // inputs use the 64-key-tile kernel. FA_KERNEL=0|1 forces one (tuning).
+    // inputs use the 64-key-tile kernel. FA_KERNEL=0|1|2 forces one (tuning).
     int kernel = (in == IN_E4M3) ? KERNEL_TILE64 : KERNEL_PIPE16;
+    // 16-bit inputs at D = 64 go to the key-split kernel where the pipelined
+    // kernel would leave waves idle: with at most 64 query rows per head (two
+    // or three of its four waves would hold no row), or when it would launch
+    // at most FA_KS_MAX_WG workgroups (a CU would hold at most one, and the
+    // heaviest tile would walk its keys alone). Elsewhere the key-split
+    // kernel's 32-row workgroups copy each K/V tile into LDS four times as
+    // often and lose (measured: c2, 384 workgroups, 31.4 against 28.3 us;
+    // B8 H32 Nq128, 256 workgroups, 95 against 78 us).
+    const bool ks_ok = in != IN_E4M3 && D == 64 && mod == MOD_NONE && !pipe16;
+    if (ks_ok && (Nq <= 64 || n_bh * ((Nq + 127) / 128) <= FA_KS_MAX_WG)) kernel = KERNEL_KSPLIT;
     if (const char* e = getenv("FA_KERNEL")) {
         const int f = atoi(e);
-        if (f == KERNEL_TILE64 || (f == KERNEL_PIPE16 && in != IN_E4M3)) kernel = f;
+        if (f == KERNEL_TILE64 || (f == KERNEL_PIPE16 && in != IN_E4M3) || (f == KERNEL_KSPLIT && ks_ok)) kernel = f;
     }
     if (mod != MOD_NONE || pipe16) kernel = KERNEL_PIPE16;
     // 64-key-tile kernel: two 32-row query blocks per wave halve LDS traffic
@@ -455,6 +468,11 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool pipe1
     pl.nw = (kernel == KERNEL_PIPE16 && D == 128) ? 8 : WAVES;
     pl.qb = qb;
     pl.br = pl.nw * 32 * qb;
+    if (kernel == KERNEL_KSPLIT) {
+        pl.qb = 1;
+        pl.br = 32;     // one 32-row block per workgroup, its keys split over the waves
+        pl.bc = 128;    // keys per tile: one 32-key sub-tile per wave
+    }
     pl.n_qt = (Nq + pl.br - 1) / pl.br;
     pl.n_wg = n_bh * pl.n_qt;
     return pl;
@@ -481,6 +499,7 @@ static int launch_io(const Plan& pl, const Params& p, hipStream_t s) {
 
 int launch(const Plan& pl, const Params& p, void* stream) {
     if (pl.kernel == KERNEL_PIPE16) return launch16(pl, p, stream);
+    if (pl.kernel == KERNEL_KSPLIT) return launch_ks(pl, p, stream);
     hipStream_t s = (hipStream_t)stream;
     if (pl.in == IN_F16 && pl.out == OUT_F16) return launch_io<IN_F16, OUT_F16>(pl, p, s);
     if (pl.in == IN_F16 && pl.out == OUT_F32) return launch_io<IN_F16, OUT_F32>(pl, p, s);

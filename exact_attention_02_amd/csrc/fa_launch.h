@@ -12,7 +12,9 @@ enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
 // KERNEL_PIPE16: 16-bit inputs, scores of the next 32 keys formed during the
 // softmax of the current 32 (fa_fwd16.hip).
 enum ScoreMod { MOD_NONE = 0, MOD_SOFTCAP = 1, MOD_ALIBI = 2 };
-enum KernelKind { KERNEL_TILE64 = 0, KERNEL_PIPE16 = 1 };
+// KERNEL_KSPLIT: 16-bit inputs at D = 64 on small grids, 32 query rows per
+// workgroup whose waves split the keys (fa_fwd_ks.hip).
+enum KernelKind { KERNEL_TILE64 = 0, KERNEL_PIPE16 = 1, KERNEL_KSPLIT = 2 };
 
 // Everything a workgroup needs; passed by value as the kernel argument.
 struct Params {
@@ -93,6 +95,7 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod = MOD_NONE,
 // value of hipGetLastError() after the launch (0 on success).
 int launch(const Plan& plan, const Params& p, void* stream);
 int launch16(const Plan& plan, const Params& p, void* stream);
+int launch_ks(const Plan& plan, const Params& p, void* stream);
 // The merge of the splits (p.n_split > 1): O and LSE from ws_o and ws_lse.
 int launch_combine(const Plan& plan, const Params& p, void* stream);
 

@@ -199,6 +199,24 @@ def test_tile64_kernel_on_16bit_inputs(monkeypatch, B, H, Nq, Nk, causal, window
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
+@pytest.mark.parametrize("B,H,Nq,Nk", SHAPES)
+@pytest.mark.parametrize("causal,window", MODES)
+@pytest.mark.parametrize("din,dout", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("kernel", ["1", "2"])
+def test_pipelined_and_key_split_kernels_on_small_shapes(monkeypatch, B, H, Nq, Nk, causal, window, din, dout,
+                                                         kernel):
+    # 16-bit D = 64 problems run the key-split kernel on small grids and the
+    # pipelined kernel otherwise; both are forced here on every small shape.
+    monkeypatch.setenv("FA_KERNEL", kernel)
+    seed = 5000 + B * 7 + H * 13 + Nq * 3 + Nk + (17 if causal else 0) + window
+    w = synth.small_workload(f"k{kernel}_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, 64,
+                             causal, window, din, dout, seed)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
 # --------------------------------------- masks given as key extents
 
 EXTENTS = [(1, 1), (16, 16), (100, 100), (0, 0), (5, 40), (40, 5), (-1, 37), (63, -1), (129, 0), (-1, -1)]
@@ -220,7 +238,8 @@ def test_window_extents_small_shapes(B, H, Nq, Nk, wl, wr, D, din, dout):
 
 
 @pytest.mark.parametrize("wl,wr", [(16, 16), (5, 40), (-1, 37), (100, 100)])
-@pytest.mark.parametrize("D,qb,kernel", [(64, "2", "1"), (64, "1", "0"), (64, "2", "0"), (128, "1", "0")])
+@pytest.mark.parametrize("D,qb,kernel", [(64, "2", "1"), (64, "1", "0"), (64, "2", "0"), (128, "1", "0"), (64, "1", "1"),
+                                         (64, "1", "2")])
 def test_window_extents_other_tile_shapes(monkeypatch, wl, wr, D, qb, kernel):
     monkeypatch.setenv("FA_TILE_QB", qb)
     monkeypatch.setenv("FA_KERNEL", kernel)
@@ -304,7 +323,9 @@ def test_score_mods_with_two_query_blocks_per_wave(monkeypatch, mod, cap):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-def test_alibi_with_zero_slopes_is_bitwise_plain_attention():
+def test_alibi_with_zero_slopes_is_bitwise_plain_attention(monkeypatch):
+    # score modifiers run on the pipelined kernel: plain attention is taken on it too
+    monkeypatch.setenv("FA_KERNEL", "1")
     w = synth.small_workload("alibi0", 1, 2, 333, 333, 64, True, 0, "bf16", "bf16", 5600)
     inp = synth.make_inputs(w)
     q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
@@ -376,7 +397,9 @@ def test_splitkv_dtypes(din, dout):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-def test_one_split_is_bitwise_the_plain_call():
+def test_one_split_is_bitwise_the_plain_call(monkeypatch):
+    # split-KV runs on the pipelined kernel: the plain call is taken on it too
+    monkeypatch.setenv("FA_KERNEL", "1")
     w = synth.small_workload("split_one", 2, 3, 5, 3000, 64, True, 0, "bf16", "bf16", 6200)
     inp = synth.make_inputs(w)
     o1, l1 = run_split(w, inp, 1)
