@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_ks_kernel(Params p) {
     const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
 
     int bh, qt;
-    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, &bh, &qt);
+    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, p.hg, &bh, &qt);
     const int r0 = qt * 32, r1 = min(r0 + 32, Nq);
     int kv_lo, kv_hi;
     kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);

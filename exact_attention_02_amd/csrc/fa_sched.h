@@ -118,25 +118,46 @@ FA_HD void mask_extents(int causal, int window, int Nq, int Nk, int* wl, int* wr
     *wl = (window > 0 && window - 1 < big) ? window - 1 : big;
 }
 
+// Heads an XCD interleaves in its workgroup order (decode_wg): as many as keep
+// the K and V of the heads in flight on the 8 XCDs within kv_budget bytes (a
+// share of the chip's 256 MiB last-level cache), at least 1. per_head_kv is
+// one head's K plus V in bytes.
+FA_HD int wg_head_group(long long n_bh, long long per_head_kv, long long kv_budget) {
+    const bool by_xcd = n_bh % 8 == 0;
+    const long long hp = by_xcd ? n_bh / 8 : n_bh;
+    const long long in_flight = by_xcd ? 8 * per_head_kv : per_head_kv;
+    long long g = in_flight > 0 ? kv_budget / in_flight : hp;
+    if (g > hp) g = hp;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
 // Hardware workgroup id -> (batch*head, query tile).
 //
 // Workgroups are handed to the 8 XCDs of the chip round-robin by id, and each
 // XCD has its own L2. When the head count is a multiple of 8, XCD x gets a
-// contiguous block of heads and walks them one head at a time, so the
-// workgroups resident on one XCD share one head's K and V in that L2. Within
-// a head the query tiles go from last to first: under a causal mask the last
-// tiles carry the most key tiles, so the heaviest work starts first and the
-// light tiles fill the tail.
-FA_HD void decode_wg(long long wg, int n_bh, int n_qt, int* bh, int* qt) {
+// contiguous block of heads (otherwise the whole grid is one sequence). It
+// walks them in groups of hg heads (wg_head_group; the last group may be
+// smaller), and within a group takes the query tiles from last to first
+// across the group's heads: under a causal mask the last tiles carry the
+// most key tiles, so the heaviest work of the group starts first and light
+// tiles fill the tail. Interleaving the heads shortens that tail: a long tile
+// dispatched late shares its CU with others for its whole run. Grouping
+// bounds the K and V the resident workgroups stream at once. hg = 1 walks
+// one head at a time.
+FA_HD void decode_wg(long long wg, int n_bh, int n_qt, int hg, int* bh, int* qt) {
+    long long x = 0, s = wg, hp = n_bh;
     if (n_bh % 8 == 0) {
-        const long long x = wg % 8, s = wg / 8;
-        const long long hp = n_bh / 8;
-        *bh = (int)(x * hp + s / n_qt);
-        *qt = n_qt - 1 - (int)(s % n_qt);
-    } else {
-        *bh = (int)(wg / n_qt);
-        *qt = n_qt - 1 - (int)(wg % n_qt);
+        x = wg % 8;
+        s = wg / 8;
+        hp = n_bh / 8;
     }
+    const long long g = hg < 1 ? 1 : (hg > hp ? hp : hg);
+    const long long span = g * n_qt;        // workgroups of a full group
+    const long long gi = s / span, r = s % span;
+    const long long gs = (hp - gi * g < g) ? hp - gi * g : g;   // heads in this group
+    *bh = (int)(x * hp + gi * g + r % gs);
+    *qt = n_qt - 1 - (int)(r / gs);
 }
 
 }  // namespace fa

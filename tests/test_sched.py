@@ -236,3 +236,39 @@ int main() {{
     subprocess.run(["g++", "-O1", "-std=c++17", "-o", str(exe), str(src)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout
+
+
+@pytest.mark.parametrize("B,H,N", [(4, 12, 8192), (1, 12, 1000), (3, 5, 700), (2, 8, 300)])
+@pytest.mark.parametrize("group", ["1", "2", "4", "5", "64"])
+def test_grouped_order_is_a_bijection_heavy_first_per_group(B, H, N, group, monkeypatch):
+    # FA_WG_GROUP forces the heads an XCD interleaves (the last group may be
+    # smaller). Every (head, tile) appears once; heads stay on their XCD when
+    # B*H is a multiple of 8; per XCD the workgroups run group by group, and
+    # within a group the tiles go from last to first across its heads.
+    monkeypatch.setenv("FA_WG_GROUP", group)
+    n_wg, br, qw, bc = fa.plan_grid(B, H, N, N, 64, True, 0, fa.FA_BF16)
+    n_bh = B * H
+    n_qt = (N + br - 1) // br
+    by_xcd = n_bh % 8 == 0
+    hp = n_bh // 8 if by_xcd else n_bh
+    g = min(max(int(group), 1), hp)
+    seen = set()
+    seq = {}
+    for wg in range(n_wg):
+        bh, qt, lo, hi = fa.plan_tile(B, H, N, N, 64, True, 0, fa.FA_BF16, wg)
+        assert (bh, qt) not in seen
+        seen.add((bh, qt))
+        x = wg % 8 if by_xcd else 0
+        if by_xcd:
+            assert x * hp <= bh < (x + 1) * hp
+        seq.setdefault(x, []).append((bh, qt))
+    assert len(seen) == n_bh * n_qt == n_wg
+    for x, items in seq.items():
+        pos = 0
+        for g0 in range(0, hp, g):
+            gs = min(g, hp - g0)
+            chunk = items[pos:pos + gs * n_qt]
+            pos += gs * n_qt
+            assert {bh - x * hp for bh, _ in chunk} == set(range(g0, g0 + gs))
+            qts = [qt for _, qt in chunk]
+            assert qts == sorted(qts, reverse=True)
