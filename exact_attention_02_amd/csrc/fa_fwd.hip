@@ -422,7 +422,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
 #ifndef FA_KS_MAX_WG
 #define FA_KS_MAX_WG 128
 #endif
-Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool pipe16) {
+Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool splitkv) {
     Plan pl;
     pl.in = in;
     pl.out = out;
@@ -441,13 +441,15 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool pipe1
     // kernel's 32-row workgroups copy each K/V tile into LDS four times as
     // often and lose (measured: c2, 384 workgroups, 31.4 against 28.3 us;
     // B8 H32 Nq128, 256 workgroups, 95 against 78 us).
-    const bool ks_ok = in != IN_E4M3 && D == 64 && mod == MOD_NONE && !pipe16;
+    const bool ks_ok = in != IN_E4M3 && D == 64 && mod == MOD_NONE;
     if (ks_ok && (Nq <= 64 || n_bh * ((Nq + 127) / 128) <= FA_KS_MAX_WG)) kernel = KERNEL_KSPLIT;
     if (const char* e = getenv("FA_KERNEL")) {
         const int f = atoi(e);
         if (f == KERNEL_TILE64 || (f == KERNEL_PIPE16 && in != IN_E4M3) || (f == KERNEL_KSPLIT && ks_ok)) kernel = f;
     }
-    if (mod != MOD_NONE || pipe16) kernel = KERNEL_PIPE16;
+    // score modifiers: the pipelined kernel only; split-KV: the pipelined or
+    // the key-split kernel (16-bit inputs)
+    if (mod != MOD_NONE || (splitkv && kernel == KERNEL_TILE64)) kernel = KERNEL_PIPE16;
     // 64-key-tile kernel: two 32-row query blocks per wave halve LDS traffic
     // per MFMA and the K/V re-reads per query; one block keeps the grid large
     // on small problems and keeps D = 128 within the register file.

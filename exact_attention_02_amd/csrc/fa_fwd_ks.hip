@@ -20,6 +20,10 @@
 // of P never reaches O. Skipped sub-tiles cost a wave nothing but the
 // barrier. K and V tiles of 128 keys stream through two LDS slots by
 // direct-to-LDS copies, in the pipelined kernel's swizzled layout.
+//
+// Split-KV (p.n_split > 1): workgroup (tile, split) takes a contiguous share of
+// the tile's 128-key tiles and writes its O (divided by its own sum) and its
+// LSE in fp32 to the workspace, which the merge kernel combines.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,12 +52,24 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_ks_kernel(Params p) {
     const int g = lane >> 4, cl = lane & 15;
     const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
 
-    int bh, qt;
-    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, p.hg, &bh, &qt);
+    int bh, qt, split = 0;
+    long long wgid = blockIdx.x;
+    if (p.n_split > 1) {
+        split = (int)(wgid % p.n_split);
+        wgid /= p.n_split;
+    }
+    decode_wg(wgid, p.n_bh, p.n_qt, p.hg, &bh, &qt);
     const int r0 = qt * 32, r1 = min(r0 + 32, Nq);
     int kv_lo, kv_hi;
     kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
-    const int t_lo = kv_lo / TK, t_hi = (kv_hi > kv_lo) ? (kv_hi + TK - 1) / TK : kv_lo / TK;
+    int t_lo = kv_lo / TK, t_hi = (kv_hi > kv_lo) ? (kv_hi + TK - 1) / TK : kv_lo / TK;
+    if (p.n_split > 1) {
+        // split s takes tiles [t_lo + nt*s/S, t_lo + nt*(s+1)/S) of the range
+        const long long nt = t_hi - t_lo;
+        const int a = t_lo + (int)(nt * split / p.n_split), b = t_lo + (int)(nt * (split + 1) / p.n_split);
+        t_lo = a;
+        t_hi = b;
+    }
     int jf0, jf1, ju0, ju1;
     block_ranges32(r0, r1, Nq, Nk, wl, wr, &jf0, &jf1, &ju0, &ju1);
     const int row = r0 + l32;
@@ -222,17 +238,25 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_ks_kernel(Params p) {
             for (int w = 0; w < 4; ++w) a = fmaf(f[w], wo[(w * D + d0 + e) * 32 + mr], a);
             o8[e] = a * inv;
         }
-        uint8_t* dst = p.o + ((size_t)bh * Nq + orow) * D * Out<OUT>::EB + d0 * Out<OUT>::EB;
-        Out<OUT>::store4(dst, o8[0], o8[1], o8[2], o8[3]);
-        Out<OUT>::store4(dst + 4 * Out<OUT>::EB, o8[4], o8[5], o8[6], o8[7]);
-        if (d0 == 0)
-            p.lse[(size_t)bh * Nq + orow] = (L > 0.f) ? (M + __builtin_amdgcn_logf(L)) * LN2 : -INFINITY;
+        const float lse = (L > 0.f) ? (M + __builtin_amdgcn_logf(L)) * LN2 : -INFINITY;
+        if (p.n_split > 1) {
+            const size_t sl = (size_t)bh * p.n_split + split;
+            uint8_t* dst = (uint8_t*)(p.ws_o + (sl * Nq + orow) * D + d0);
+            Out<OUT_F32>::store4(dst, o8[0], o8[1], o8[2], o8[3]);
+            Out<OUT_F32>::store4(dst + 16, o8[4], o8[5], o8[6], o8[7]);
+            if (d0 == 0) p.ws_lse[sl * Nq + orow] = lse;
+        } else {
+            uint8_t* dst = p.o + ((size_t)bh * Nq + orow) * D * Out<OUT>::EB + d0 * Out<OUT>::EB;
+            Out<OUT>::store4(dst, o8[0], o8[1], o8[2], o8[3]);
+            Out<OUT>::store4(dst + 4 * Out<OUT>::EB, o8[4], o8[5], o8[6], o8[7]);
+            if (d0 == 0) p.lse[(size_t)bh * Nq + orow] = lse;
+        }
     }
 }
 
 template <int IN, int OUT>
 static int launch_ks_io(const Plan& pl, const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((fa_fwd_ks_kernel<IN, OUT>), dim3((unsigned)pl.n_wg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((fa_fwd_ks_kernel<IN, OUT>), dim3((unsigned)(pl.n_wg * p.n_split)), dim3(256), 0, s, p);
     return (int)hipGetLastError();
 }
 

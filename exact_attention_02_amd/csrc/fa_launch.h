@@ -79,7 +79,7 @@ int launch_bwd(int in, int D, const BwdParams& p, void* stream);
 // Tile shape a launch uses.
 struct Plan {
     int in, out, D;
-    int kernel;     // KERNEL_TILE64 or KERNEL_PIPE16
+    int kernel;     // KERNEL_TILE64, KERNEL_PIPE16 or KERNEL_KSPLIT
     int nw;         // waves per workgroup
     int qb;         // 32-row query blocks per wave
     int br;         // query rows per workgroup (nw * 32 * qb)
@@ -89,9 +89,9 @@ struct Plan {
 };
 
 // Picks the tile shape for a problem. Pure host arithmetic.
-// mod != MOD_NONE and pipe16 (split-KV) need the pipelined kernel, the only one
-// with score modifiers and splits.
-Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod = MOD_NONE, bool pipe16 = false);
+// mod != MOD_NONE needs the pipelined kernel, the only one with score
+// modifiers; splitkv (split-KV) runs on the pipelined or the key-split kernel.
+Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod = MOD_NONE, bool splitkv = false);
 
 // Enqueues the kernel chosen by `plan` on `stream`; returns the hipError_t
 // value of hipGetLastError() after the launch (0 on success).

@@ -376,8 +376,12 @@ def run_split(w, inp, num_splits):
 @pytest.mark.parametrize("splits", [1, 2, 7, 16, 64])
 @pytest.mark.parametrize("mask", [(True, 0, None, None), (False, 0, None, None), (True, 500, None, None),
                                   (False, 0, 300, 40)])
-@pytest.mark.parametrize("D", [64, 128])
-def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D):
+@pytest.mark.parametrize("D,kernel", [(64, None), (64, "1"), (64, "2"), (128, None)])
+def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D, kernel, monkeypatch):
+    # split-KV runs on the key-split kernel (16-bit, D = 64, small grids) or
+    # the pipelined kernel; FA_KERNEL forces each
+    if kernel is not None:
+        monkeypatch.setenv("FA_KERNEL", kernel)
     causal, window, wl, wr = mask
     w = synth.small_workload(f"split{splits}_B{B}H{H}q{Nq}k{Nk}D{D}m{mask}", B, H, Nq, Nk, D, causal, window,
                              "bf16", "bf16", 6000 + B + H * 3 + Nq * 7 + Nk + D + splits,
@@ -389,7 +393,10 @@ def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D):
 
 
 @pytest.mark.parametrize("din,dout", [("f16", "f16"), ("f16", "f32"), ("bf16", "f32")])
-def test_splitkv_dtypes(din, dout):
+@pytest.mark.parametrize("kernel", [None, "1"])
+def test_splitkv_dtypes(din, dout, kernel, monkeypatch):
+    if kernel is not None:
+        monkeypatch.setenv("FA_KERNEL", kernel)
     w = synth.small_workload(f"split_dt_{din}_{dout}", 2, 4, 3, 5000, 64, True, 0, din, dout, 6100)
     inp = synth.make_inputs(w)
     o, lse = run_split(w, inp, "auto")
@@ -397,9 +404,11 @@ def test_splitkv_dtypes(din, dout):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-def test_one_split_is_bitwise_the_plain_call(monkeypatch):
-    # split-KV runs on the pipelined kernel: the plain call is taken on it too
-    monkeypatch.setenv("FA_KERNEL", "1")
+@pytest.mark.parametrize("kernel", [None, "1"])
+def test_one_split_is_bitwise_the_plain_call(kernel, monkeypatch):
+    # one split is the plain call, on whichever kernel both pick
+    if kernel is not None:
+        monkeypatch.setenv("FA_KERNEL", kernel)
     w = synth.small_workload("split_one", 2, 3, 5, 3000, 64, True, 0, "bf16", "bf16", 6200)
     inp = synth.make_inputs(w)
     o1, l1 = run_split(w, inp, 1)
@@ -407,7 +416,10 @@ def test_one_split_is_bitwise_the_plain_call(monkeypatch):
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
 
 
-def test_splits_without_keys_give_zero_and_minus_inf():
+@pytest.mark.parametrize("kernel", [None, "1"])
+def test_splits_without_keys_give_zero_and_minus_inf(kernel, monkeypatch):
+    if kernel is not None:
+        monkeypatch.setenv("FA_KERNEL", kernel)
     # window (0, 0) with Nq > Nk: the first rows see nothing, and most splits of a row are empty
     w = synth.small_workload("split_empty", 1, 2, 300, 200, 64, False, 0, "bf16", "bf16", 6300,
                              window_left=0, window_right=0)
