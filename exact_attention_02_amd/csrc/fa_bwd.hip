@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
     const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
 
     int bh, qt;
-    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, p.hg, &bh, &qt);
+    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, p.hg, p.tl, &bh, &qt);
     const int r0 = qt * BR, r1 = min(r0 + BR, Nq);
     int kv_lo, kv_hi;
     kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
     // key blocks in increasing order: under a causal mask the first ones see
     // the most query rows, so the heaviest work starts first
     int bh, kt;
-    decode_wg((long long)blockIdx.x, p.n_bh, p.n_kt, p.hg, &bh, &kt);
+    decode_wg((long long)blockIdx.x, p.n_bh, p.n_kt, p.hg, p.tl, &bh, &kt);
     kt = p.n_kt - 1 - kt;
     const int c0 = kt * BK, c1 = min(c0 + BK, Nk);
     // query rows that see a key of [c0, c1): key j is visible to row i when

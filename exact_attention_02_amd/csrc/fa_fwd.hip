@@ -86,7 +86,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
 
     const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
     int bh, qt;
-    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, p.hg, &bh, &qt);
+    decode_wg((long long)blockIdx.x, p.n_bh, p.n_qt, p.hg, p.tl, &bh, &qt);
     const int r0 = qt * BR;
     const int r1 = min(r0 + BR, Nq);
     int kv_lo, kv_hi;

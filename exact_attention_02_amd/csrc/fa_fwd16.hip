@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
         split = (int)(wgid % p.n_split);
         wgid /= p.n_split;
     }
-    decode_wg(wgid, p.n_bh, p.n_qt, p.hg, &bh, &qt);
+    decode_wg(wgid, p.n_bh, p.n_qt, p.hg, p.tl, &bh, &qt);
     const int r0 = qt * BR;
     const int r1 = min(r0 + BR, Nq);
     int kv_lo, kv_hi;

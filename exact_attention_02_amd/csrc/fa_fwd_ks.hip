@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_ks_kernel(Params p) {
         split = (int)(wgid % p.n_split);
         wgid /= p.n_split;
     }
-    decode_wg(wgid, p.n_bh, p.n_qt, p.hg, &bh, &qt);
+    decode_wg(wgid, p.n_bh, p.n_qt, p.hg, p.tl, &bh, &qt);
     const int r0 = qt * 32, r1 = min(r0 + 32, Nq);
     int kv_lo, kv_hi;
     kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);

@@ -37,7 +37,8 @@ struct Params {
     float* ws_o;
     float* ws_lse;
     int n_qt;       // query tiles per head
-    int hg;         // heads an XCD interleaves in its workgroup order (decode_wg)
+    int hg;         // workgroup order (decode_wg): heads per group in phase 1,
+    int tl;         // and the query tiles below tl that phase 2 interleaves
     float c;        // scale * descale_q * descale_k * log2(e): scores in base-2 units
     float out_mul;  // descale_v (1 unless e4m3)
 };
@@ -64,7 +65,8 @@ struct BwdParams {
     int nqp;        // Nq rounded up to a multiple of 4
     int n_qt;       // 128-row query blocks per head (dQ kernel)
     int n_kt;       // 128-key blocks per head (dK/dV kernel)
-    int hg;         // heads an XCD interleaves in its workgroup order (decode_wg)
+    int hg;         // workgroup order (decode_wg): heads per group in phase 1,
+    int tl;         // and the key blocks below tl that phase 2 interleaves
     float c;        // scale * log2(e)
     float scale;
     int H;          // heads (ALiBi: the head of bh is bh % H)

@@ -118,10 +118,10 @@ FA_HD void mask_extents(int causal, int window, int Nq, int Nk, int* wl, int* wr
     *wl = (window > 0 && window - 1 < big) ? window - 1 : big;
 }
 
-// Heads an XCD interleaves in its workgroup order (decode_wg): as many as keep
-// the K and V of the heads in flight on the 8 XCDs within kv_budget bytes (a
-// share of the chip's 256 MiB last-level cache), at least 1. per_head_kv is
-// one head's K plus V in bytes.
+// Heads per group in phase 1 of the workgroup order (decode_wg): as many as
+// keep the K and V of the heads in flight on the 8 XCDs within kv_budget
+// bytes (the XCDs' L2 caches together), at least 1. per_head_kv is one head's
+// K plus V in bytes.
 FA_HD int wg_head_group(long long n_bh, long long per_head_kv, long long kv_budget) {
     const bool by_xcd = n_bh % 8 == 0;
     const long long hp = by_xcd ? n_bh / 8 : n_bh;
@@ -136,28 +136,40 @@ FA_HD int wg_head_group(long long n_bh, long long per_head_kv, long long kv_budg
 //
 // Workgroups are handed to the 8 XCDs of the chip round-robin by id, and each
 // XCD has its own L2. When the head count is a multiple of 8, XCD x gets a
-// contiguous block of heads (otherwise the whole grid is one sequence). It
-// walks them in groups of hg heads (wg_head_group; the last group may be
-// smaller), and within a group takes the query tiles from last to first
-// across the group's heads: under a causal mask the last tiles carry the
-// most key tiles, so the heaviest work of the group starts first and light
-// tiles fill the tail. Interleaving the heads shortens that tail: a long tile
-// dispatched late shares its CU with others for its whole run. Grouping
-// bounds the K and V the resident workgroups stream at once. hg = 1 walks
-// one head at a time.
-FA_HD void decode_wg(long long wg, int n_bh, int n_qt, int hg, int* bh, int* qt) {
+// contiguous block of heads (otherwise the whole grid is one sequence), and
+// walks them in two phases:
+//   1. the query tiles qt >= tl, in groups of hg heads (the last group may be
+//      smaller): within a group the tiles go from last to first across the
+//      group's heads;
+//   2. the tiles qt < tl of all its heads, from last to first across them.
+// Under a causal mask the last tiles carry the most key tiles, so every phase
+// starts with its heaviest work. Phase 2 keeps long tiles from starting near
+// the end: a long tile dispatched late shares its CU with other workgroups
+// for its whole run, and the launch ends in a tail. Its tiles stream only
+// short K/V prefixes, so interleaving all heads there costs little cache;
+// phase 1 keeps the resident workgroups on few heads, whose K and V the L2
+// then serves. hg = 1 and tl = 0 walk one head at a time.
+FA_HD void decode_wg(long long wg, int n_bh, int n_qt, int hg, int tl, int* bh, int* qt) {
     long long x = 0, s = wg, hp = n_bh;
     if (n_bh % 8 == 0) {
         x = wg % 8;
         s = wg / 8;
         hp = n_bh / 8;
     }
-    const long long g = hg < 1 ? 1 : (hg > hp ? hp : hg);
-    const long long span = g * n_qt;        // workgroups of a full group
-    const long long gi = s / span, r = s % span;
-    const long long gs = (hp - gi * g < g) ? hp - gi * g : g;   // heads in this group
-    *bh = (int)(x * hp + gi * g + r % gs);
-    *qt = n_qt - 1 - (int)(r / gs);
+    const long long T = tl < 0 ? 0 : (tl > n_qt ? n_qt : tl);
+    const long long nh = n_qt - T;          // phase-1 tiles per head
+    if (s < hp * nh) {
+        const long long g = hg < 1 ? 1 : (hg > hp ? hp : hg);
+        const long long span = g * nh;      // workgroups of a full group
+        const long long gi = s / span, r = s % span;
+        const long long gs = (hp - gi * g < g) ? hp - gi * g : g;   // heads in this group
+        *bh = (int)(x * hp + gi * g + r % gs);
+        *qt = n_qt - 1 - (int)(r / gs);
+    } else {
+        const long long s2 = s - hp * nh;
+        *bh = (int)(x * hp + s2 % hp);
+        *qt = (int)(T - 1 - s2 / hp);
+    }
 }
 
 }  // namespace fa

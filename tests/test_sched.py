@@ -246,6 +246,7 @@ def test_grouped_order_is_a_bijection_heavy_first_per_group(B, H, N, group, monk
     # B*H is a multiple of 8; per XCD the workgroups run group by group, and
     # within a group the tiles go from last to first across its heads.
     monkeypatch.setenv("FA_WG_GROUP", group)
+    monkeypatch.setenv("FA_WG_LIGHT", "0")   # no interleaved light phase
     n_wg, br, qw, bc = fa.plan_grid(B, H, N, N, 64, True, 0, fa.FA_BF16)
     n_bh = B * H
     n_qt = (N + br - 1) // br
@@ -272,3 +273,42 @@ def test_grouped_order_is_a_bijection_heavy_first_per_group(B, H, N, group, monk
             assert {bh - x * hp for bh, _ in chunk} == set(range(g0, g0 + gs))
             qts = [qt for _, qt in chunk]
             assert qts == sorted(qts, reverse=True)
+
+
+@pytest.mark.parametrize("B,H,N", [(4, 12, 8192), (3, 5, 700), (2, 8, 300)])
+@pytest.mark.parametrize("group,light", [("1", "3"), ("2", "16"), ("4", "0"), ("1", "1000"), ("3", "1")])
+def test_two_phase_order_is_a_bijection(B, H, N, group, light, monkeypatch):
+    # FA_WG_LIGHT = T: per XCD, the tiles qt >= T go first, group by group
+    # (tiles last-first across a group's heads); then the tiles qt < T of all
+    # the XCD's heads, last-first across them. T is clamped to the tile count.
+    monkeypatch.setenv("FA_WG_GROUP", group)
+    monkeypatch.setenv("FA_WG_LIGHT", light)
+    n_wg, br, qw, bc = fa.plan_grid(B, H, N, N, 64, True, 0, fa.FA_BF16)
+    n_bh = B * H
+    n_qt = (N + br - 1) // br
+    by_xcd = n_bh % 8 == 0
+    hp = n_bh // 8 if by_xcd else n_bh
+    g = min(max(int(group), 1), hp)
+    T = min(int(light), n_qt)
+    seen, seq = set(), {}
+    for wg in range(n_wg):
+        bh, qt, lo, hi = fa.plan_tile(B, H, N, N, 64, True, 0, fa.FA_BF16, wg)
+        assert (bh, qt) not in seen
+        seen.add((bh, qt))
+        x = wg % 8 if by_xcd else 0
+        seq.setdefault(x, []).append((bh - x * hp, qt))
+    assert len(seen) == n_bh * n_qt == n_wg
+    for x, items in seq.items():
+        nh = n_qt - T
+        heavy, rest = items[:hp * nh], items[hp * nh:]
+        assert all(qt >= T for _, qt in heavy) and all(qt < T for _, qt in rest)
+        pos = 0
+        for g0 in range(0, hp if nh else 0, g):
+            gs = min(g, hp - g0)
+            chunk = heavy[pos:pos + gs * nh]
+            pos += gs * nh
+            assert {h for h, _ in chunk} == set(range(g0, g0 + gs))
+            assert [qt for _, qt in chunk] == sorted((qt for _, qt in chunk), reverse=True)
+        assert [qt for _, qt in rest] == sorted((qt for _, qt in rest), reverse=True)
+        for k in range(0, len(rest), hp):
+            assert {h for h, _ in rest[k:k + hp]} == set(range(hp))
