@@ -593,6 +593,43 @@ def test_run_to_run_determinism_and_head_independence():
     assert torch.equal(l3[0, 0], l1[1, 2])
 
 
+ORDERS = [("1", "0"), ("2", "3"), ("3", "1000"), ("64", "0")]
+
+
+@pytest.mark.parametrize("B,H", [(2, 8), (1, 6)])
+@pytest.mark.parametrize("din,kernel", [("bf16", "0"), ("bf16", "1"), ("bf16", "2"), ("e4m3", None)])
+def test_workgroup_order_does_not_change_results(B, H, din, kernel, monkeypatch):
+    # FA_WG_GROUP / FA_WG_LIGHT only reorder which workgroup runs when; every
+    # output must be bitwise the default order's (heads per XCD when B*H is a
+    # multiple of 8, one sequence otherwise)
+    if kernel is not None:
+        monkeypatch.setenv("FA_KERNEL", kernel)
+    w = synth.small_workload(f"order_{din}_{kernel}_B{B}H{H}", B, H, 600, 600, 64, True, 0, din, "bf16", 71)
+    inp = synth.make_inputs(w)
+    o0, l0 = run_gpu(w, inp)
+    for g, tl in ORDERS:
+        monkeypatch.setenv("FA_WG_GROUP", g)
+        monkeypatch.setenv("FA_WG_LIGHT", tl)
+        o1, l1 = run_gpu(w, inp)
+        assert torch.equal(o0.view(torch.uint8), o1.view(torch.uint8)) and torch.equal(l0, l1), (g, tl)
+
+
+def test_workgroup_order_does_not_change_the_backward(monkeypatch):
+    w = synth.small_workload("order_bwd", 2, 8, 500, 500, 64, True, 0, "bf16", "bf16", 72)
+    inp = synth.make_inputs(w)
+    q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
+    o, lse = fa.attention(q, k, v, scale=w.scale, causal=True)
+    do = torch.randn(o.shape, generator=torch.Generator().manual_seed(73)).to(torch.bfloat16).to(DEV)
+    g0 = fa.attention_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True)
+    for g, tl in ORDERS:
+        monkeypatch.setenv("FA_WG_GROUP", g)
+        monkeypatch.setenv("FA_WG_LIGHT", tl)
+        g1 = fa.attention_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True)
+        torch.cuda.synchronize()
+        for a, b in zip(g0, g1):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (g, tl)
+
+
 def test_power_of_two_rescaling_is_bitwise_invariant():
     w = synth.small_workload("pow2", 1, 2, 300, 300, 128, True, 0, "bf16", "bf16", 70)
     inp = synth.make_inputs(w)
