@@ -439,7 +439,7 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     // at most FA_KS_MAX_WG workgroups (a CU would hold at most one, and the
     // heaviest tile would walk its keys alone). Elsewhere the key-split
     // kernel's 32-row workgroups copy each K/V tile into LDS four times as
-    // often and lose (measured: c2, 384 workgroups, 31.4 against 28.3 us;
+    // often and lose (measured: c2, 384 workgroups, 29.7 against 23.3 us;
     // B8 H32 Nq128, 256 workgroups, 95 against 78 us).
     const bool ks_ok = in != IN_E4M3 && D == 64 && mod == MOD_NONE;
     if (ks_ok && (Nq <= 64 || n_bh * ((Nq + 127) / 128) <= FA_KS_MAX_WG)) kernel = KERNEL_KSPLIT;
