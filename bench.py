@@ -21,6 +21,7 @@ visible pair (the recomputed Q K^T, dO V^T, P^T dO, dS K and dS^T Q).
 """
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -77,16 +78,28 @@ def algorithmic_bytes(w):
     return n_bh * (w.Nq * w.D * eb + 2 * w.Nk * w.D * eb + w.Nq * w.D * ob + w.Nq * 4)
 
 
-FWD_SOURCES = ("fa_fwd.hip", "fa_fwd16.hip", "fa_device.h", "fa_sched.h", "fa_launch.h")
-BWD_SOURCES = ("fa_bwd.hip", "fa_device.h", "fa_sched.h", "fa_launch.h")
+# The sources that decide what a workload's kernels do: the kernels, their
+# headers and the launch planning (tile shapes, workgroup order) in fa_api.hip.
+FWD_SOURCES = ("fa_fwd.hip", "fa_fwd16.hip", "fa_fwd_ks.hip", "fa_device.h", "fa_sched.h", "fa_launch.h",
+               "fa_api.hip")
+BWD_SOURCES = ("fa_bwd.hip", "fa_device.h", "fa_sched.h", "fa_launch.h", "fa_api.hip")
+
+
+def _code_only(text):
+    """C++ source without comments, whitespace collapsed: an edit of a comment
+    leaves the kernels, and so the hash, unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
 
 
 def kernel_hash(backward=False):
-    """Hash of the kernel sources a workload runs (the forward's or the backward's)."""
+    """Hash of the code of the kernel sources a workload runs (the forward's or
+    the backward's), comments and layout ignored."""
     h = hashlib.sha256()
     for name in (BWD_SOURCES if backward else FWD_SOURCES):
-        with open(os.path.join(ROOT, "exact_attention_02_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_attention_02_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
