@@ -152,6 +152,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.mod = mod;
     p.mk1 = (mod == FA_MOD_SOFTCAP) ? 2.f * p.c / cap : 0.f;
     p.mk2 = (mod == FA_MOD_SOFTCAP) ? cap * 1.44269504088896341f : 0.f;
+    p.scp = (mod == FA_MOD_SOFTCAP) ? fa::softcap_poly((double)scale * dq * dk / cap) : fa::SoftcapPoly{};
     p.slopes = slopes;
     p.n_split = n_split;
     p.ws_o = (float*)workspace;
@@ -337,6 +338,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     p.mod = mod;
     p.mk1 = (mod == FA_MOD_SOFTCAP) ? 2.f * p.c / cap : 0.f;
     p.mk2 = (mod == FA_MOD_SOFTCAP) ? cap * 1.44269504088896341f : 0.f;
+    p.scp = (mod == FA_MOD_SOFTCAP) ? fa::softcap_poly((double)scale / cap) : fa::SoftcapPoly{};
     p.slopes = slopes;
     (void)hipGetLastError();
     return fa::launch_bwd(di.in, D, p, stream) == 0 ? FA_OK : FA_ERR_LAUNCH;

@@ -122,6 +122,14 @@ __device__ __forceinline__ f32x4v lds_readf4(const lds_u8* a) {
 // f = cap log2(e) tanh(x) (k2 = cap log2(e)), and 1 - tanh^2 = 4 r (1 - r),
 // which has no cancellation and is 0 where u overflows. A masked score
 // (-inf) has weight 0 under every modifier.
+// Softcap on small arguments (all 16 scores of the lane's block within the
+// range of softcap_tanh_poly): the weight and f' from the polynomial's tanh.
+__device__ __forceinline__ float softcap_weight_poly(const SoftcapPoly& P, float s, float k2, float e, float& g) {
+    const float t = softcap_tanh_poly(P, s);
+    g = fmaf(-t, t, 1.f);
+    return __builtin_amdgcn_exp2f(fmaf(t, k2, e));
+}
+
 template <int MOD>
 __device__ __forceinline__ float mod_weight(float s, float c2, float k1, float k2, float e, float& g) {
     if constexpr (MOD == MOD_SOFTCAP) {
@@ -177,6 +185,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
     const float ndv = (row < Nq) ? p.ndvec[(size_t)bh * p.nqp + row] : 0.f;
     const float c2 = p.c;
     const float k1 = p.mk1, k2 = p.mk2;   // softcap constants
+    const SoftcapPoly scp = p.scp;        // softcap on small arguments (fa_device.h)
     float slope2 = 0.f;                   // ALiBi: this head's slope * log2(e)
     if constexpr (MOD == MOD_ALIBI) slope2 = p.slopes[bh % p.H] * LOG2E;
 #if FA_BWD_DQ_DINIT
@@ -265,17 +274,27 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
             float ab = -l2;
             if constexpr (MOD == MOD_ALIBI) ab = fmaf(slope2, (float)(32 * j + 4 * hh - (row + Nk - Nq)), -l2);
             float ds[16];
+            // POLY: softcap by the polynomial (all 16 of the lane's scores in range)
+            auto weights = [&](auto poly_c) __attribute__((always_inline)) {
+                constexpr bool POLY = decltype(poly_c)::value;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float e = ab, g;
-                if constexpr (MOD == MOD_ALIBI) e = fmaf(slope2, (float)(8 * (r >> 2) + (r & 3)), ab);
-                const float pr = mod_weight<MOD>(S[r], c2, k1, k2, e, g);
+                for (int r = 0; r < 16; ++r) {
+                    float e = ab, g;
+                    if constexpr (MOD == MOD_ALIBI) e = fmaf(slope2, (float)(8 * (r >> 2) + (r & 3)), ab);
+                    const float pr = POLY ? softcap_weight_poly(scp, S[r], k2, e, g) : mod_weight<MOD>(S[r], c2, k1, k2, e, g);
 #if FA_BWD_DQ_DINIT
-                ds[r] = pr * dP[r];
+                    ds[r] = pr * dP[r];
 #else
-                ds[r] = pr * (dP[r] + ndv);
+                    ds[r] = pr * (dP[r] + ndv);
 #endif
-                if constexpr (MOD == MOD_SOFTCAP) ds[r] *= g;
+                    if constexpr (MOD == MOD_SOFTCAP) ds[r] *= g;
+                }
+            };
+            if constexpr (MOD == MOD_SOFTCAP) {
+                if (softcap_poly_ok(scp, S)) weights(std::true_type{});
+                else weights(std::false_type{});
+            } else {
+                weights(std::false_type{});
             }
             i32x4 dsb[2];
 #pragma unroll
@@ -377,6 +396,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
     const unsigned stat_voff = (lane < 16) ? (unsigned)(16 * lane) : (1u << 30);
     const float c2 = p.c;
     const float k1 = p.mk1, k2 = p.mk2;   // softcap constants
+    const SoftcapPoly scp = p.scp;        // softcap on small arguments (fa_device.h)
     float slope2 = 0.f;                   // ALiBi: this head's slope * log2(e)
     if constexpr (MOD == MOD_ALIBI) slope2 = p.slopes[bh % p.H] * LOG2E;
     // the lane's key sees the rows [klo_q, khi_q)
@@ -469,18 +489,28 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void fa_bwd_dkdv_kernel(Bwd
         float bb = 0.f;
         if constexpr (MOD == MOD_ALIBI) bb = slope2 * (float)(key - q0 - 4 * hh - dlt);
         float pr[16], ds[16];
+        // POLY: softcap by the polynomial (all 16 of the lane's scores in range)
+        auto weights = [&](auto poly_c) __attribute__((always_inline)) {
+            constexpr bool POLY = decltype(poly_c)::value;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const f32x4v L = lds_readf4(lds + sofs + (SB + 1024 + 4 * (32 * sub + 8 * gq)));
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4v L = lds_readf4(lds + sofs + (SB + 1024 + 4 * (32 * sub + 8 * gq)));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * gq + e;
-                float ex = -L[e], g;
-                if constexpr (MOD == MOD_ALIBI) ex = fmaf(-slope2, (float)(8 * gq + e), bb) - L[e];
-                pr[r] = mod_weight<MOD>(S[r], c2, k1, k2, ex, g);
-                ds[r] = pr[r] * dP[r];
-                if constexpr (MOD == MOD_SOFTCAP) ds[r] *= g;
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * gq + e;
+                    float ex = -L[e], g;
+                    if constexpr (MOD == MOD_ALIBI) ex = fmaf(-slope2, (float)(8 * gq + e), bb) - L[e];
+                    pr[r] = POLY ? softcap_weight_poly(scp, S[r], k2, ex, g) : mod_weight<MOD>(S[r], c2, k1, k2, ex, g);
+                    ds[r] = pr[r] * dP[r];
+                    if constexpr (MOD == MOD_SOFTCAP) ds[r] *= g;
+                }
             }
+        };
+        if constexpr (MOD == MOD_SOFTCAP) {
+            if (softcap_poly_ok(scp, S)) weights(std::true_type{});
+            else weights(std::false_type{});
+        } else {
+            weights(std::false_type{});
         }
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {

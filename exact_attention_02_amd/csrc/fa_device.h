@@ -209,4 +209,27 @@ __device__ __forceinline__ i32x2 read_tr16(const lds_u8* addr) {
     return __builtin_bit_cast(i32x2, v);
 }
 
+// Softcap, s <- cap * tanh(x) with x = scale * s / cap, on small arguments:
+// for |x| <= SC_POLY_X the Taylor polynomial x - x^3/3 + 2x^5/15 - 17x^7/315
+// is within 62 |x|^9 / 2835 <= 1.2e-8 of tanh(x) (the series alternates with
+// decreasing terms there). It costs six FMAs and multiplies where the closed
+// form tanh|x| = 1 - 2 / (e^(2|x|) + 1) costs an exponential and a reciprocal.
+// A lane takes it for its 16 scores of a block when all of them lie in range
+// (softcap_poly_ok); a masked score (-inf) sends the lane to the closed form.
+// tanh(kx * s) for |s| <= smax
+__device__ __forceinline__ float softcap_tanh_poly(const SoftcapPoly& P, float s) {
+    const float s2 = s * s;
+    float q = fmaf(s2, P.d, P.c);
+    q = fmaf(s2, q, P.b);
+    const float sx = s * P.kx;
+    return fmaf(sx * s2, q, sx);
+}
+// every one of the 16 scores within the polynomial's range
+__device__ __forceinline__ bool softcap_poly_ok(const SoftcapPoly& P, const f32x16& S) {
+    float am = fabsf(S[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) am = fmaxf(am, fabsf(S[r]));
+    return am <= P.smax;
+}
+
 }  // namespace fa

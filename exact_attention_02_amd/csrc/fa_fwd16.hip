@@ -74,12 +74,11 @@ constexpr int EARLY_TILES = FA_EARLY_TILES;
 #ifndef FA_WPS_D64
 #define FA_WPS_D64 3
 #endif
-// The score modifiers need more registers. Softcap keeps three waves per
-// SIMD (72 bytes of spill outside the step; 6.6% faster than two on the
-// causal B4 H12 N8192 forward); ALiBi runs two (at three it spills inside the
-// loop and loses 7%).
+// The score modifiers need more registers: two waves per SIMD. (Softcap's
+// polynomial for small arguments spills inside the step at three; ALiBi at
+// three spills inside the loop and loses 7%.)
 #ifndef FA_WPS_SOFTCAP
-#define FA_WPS_SOFTCAP 3
+#define FA_WPS_SOFTCAP 2
 #endif
 #ifndef FA_WPS_ALIBI
 #define FA_WPS_ALIBI 2
@@ -171,6 +170,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
     // Score modifier (MOD_SOFTCAP, MOD_ALIBI): constants in base-2 units.
     const float sc_k1 = p.mk1;   // softcap: e^(2|x|) = 2^(sc_k1 |s|), x = scale * s / cap
     const float sc_k2 = p.mk2;   // softcap: cap * log2(e)
+    const SoftcapPoly scp = p.scp;   // softcap on small arguments (fa_device.h)
     float slope2 = 0.f;          // ALiBi: this head's slope * log2(e)
     if constexpr (MOD == MOD_ALIBI) slope2 = p.slopes[bh % p.H] * LOG2E;
     // ALiBi with a nonzero slope presets the reference (wave-uniform)
@@ -292,6 +292,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
     //            32j + 4hh - i' (in abase, with -ref) plus 8(r/4) + r%4
     //   softcap: cap * log2(e) * tanh(scale * s / cap) - ref, with
     //            tanh|x| = 1 - 2 / (e^(2|x|) + 1); a masked score stays -inf
+    //            (sc_args takes a polynomial instead on small arguments)
     auto alibi_base = [&](int j, int qb, float ref) __attribute__((always_inline)) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
@@ -310,11 +311,29 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
             return fmaf(s, c2, -ref);
         }
     };
+    // Softcap: the 16 exponent arguments of a lane's block against ref, by the
+    // polynomial when all 16 scores are in its range, else the closed form.
+    // The choice depends on the lane's scores alone, so forming a block again
+    // (exact redo, residual) repeats it bit for bit.
+    auto sc_args = [&](const f32x16& S, float ref, float(&a)[16]) __attribute__((always_inline)) {
+        if (softcap_poly_ok(scp, S)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[r] = fmaf(softcap_tanh_poly(scp, S[r]), sc_k2, -ref);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[r] = earg(S[r], r, 0.f, ref);
+        }
+    };
     auto p_phase_pr = [&](const f32x16& S, float ms, float& ts, i32x4(&hi)[2], float(&pr)[16], int j, int qb)
         __attribute__((always_inline)) {
         if constexpr (MOD == MOD_NONE) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+        } else if constexpr (MOD == MOD_SOFTCAP) {
+            float a[16];
+            sc_args(S, ms, a);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(a[r]);
         } else {
             float ab = 0.f;
             if constexpr (MOD == MOD_ALIBI) ab = alibi_base(j, qb, ms);
@@ -451,6 +470,13 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
 #pragma unroll
                     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
                     mx = max_halves(mx);
+                } else if constexpr (MOD == MOD_SOFTCAP) {
+                    float a[16];
+                    sc_args(S, 0.f, a);
+                    mx = a[0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, a[r]);
+                    mx = max_halves(mx);
                 } else {
                     float ab = 0.f;
                     if constexpr (MOD == MOD_ALIBI) ab = alibi_base(j, qb, 0.f);
@@ -479,6 +505,11 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
                     if constexpr (MOD == MOD_NONE) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
+                    } else if constexpr (MOD == MOD_SOFTCAP) {
+                        float a[16];
+                        sc_args(S, ms, a);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) pe[r] = __builtin_amdgcn_exp2f(a[r]);
                     } else {
                         float ab = 0.f;
                         if constexpr (MOD == MOD_ALIBI) ab = alibi_base(j, qb, ms);

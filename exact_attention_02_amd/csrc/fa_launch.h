@@ -12,6 +12,20 @@ enum OutKind { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2 };
 // KERNEL_PIPE16: 16-bit inputs, scores of the next 32 keys formed during the
 // softmax of the current 32 (fa_fwd16.hip).
 enum ScoreMod { MOD_NONE = 0, MOD_SOFTCAP = 1, MOD_ALIBI = 2 };
+// Softcap on small arguments: tanh(kx * s) by an odd polynomial for |s| <=
+// smax (softcap_tanh_poly in fa_device.h). Filled on the host, so that the
+// kernels read the constants from their arguments.
+constexpr double SC_POLY_X = 0.2;   // largest |x| = |kx * s| on the polynomial
+struct SoftcapPoly {
+    float kx;       // scale / cap
+    float b, c, d;  // -kx^2 / 3, 2 kx^4 / 15, -17 kx^6 / 315
+    float smax;     // SC_POLY_X / kx
+};
+inline SoftcapPoly softcap_poly(double kx) {
+    const double x2 = kx * kx;
+    return {(float)kx, (float)(-x2 / 3), (float)(2 * x2 * x2 / 15), (float)(-17 * x2 * x2 * x2 / 315),
+            (float)(SC_POLY_X / kx)};
+}
 // KERNEL_KSPLIT: 16-bit inputs at D = 64 on small grids, 32 query rows per
 // workgroup whose waves split the keys (fa_fwd_ks.hip).
 enum KernelKind { KERNEL_TILE64 = 0, KERNEL_PIPE16 = 1, KERNEL_KSPLIT = 2 };
@@ -29,6 +43,7 @@ struct Params {
     int H;          // heads (ALiBi: the head of bh is bh % H)
     int mod;        // MOD_NONE, MOD_SOFTCAP or MOD_ALIBI (16-bit kernel only)
     float mk1, mk2; // softcap constants: 2 * c / cap and cap * log2(e)
+    SoftcapPoly scp;  // softcap on small arguments (fa_device.h)
     const float* slopes;  // ALiBi: [H] device array of per-head slopes
     // Split-KV: each head's key tiles are split into n_split contiguous ranges,
     // one workgroup each; a split writes its O (divided by its own sum) and its
@@ -72,6 +87,7 @@ struct BwdParams {
     int H;          // heads (ALiBi: the head of bh is bh % H)
     int mod;        // MOD_NONE, MOD_SOFTCAP or MOD_ALIBI
     float mk1, mk2; // softcap constants: 2 * c / cap and cap * log2(e)
+    SoftcapPoly scp;  // softcap on small arguments (fa_device.h)
     const float* slopes;  // ALiBi: [H] device array of per-head slopes
 };
 
