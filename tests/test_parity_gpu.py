@@ -289,7 +289,10 @@ def test_sliding_window_zero_queries_average_the_window():
 
 # ----------------------------------------------------- score modifiers
 
-MOD_CASES = [("softcap", 50.0), ("softcap", 2.0), ("softcap", 0.5), ("alibi", 0.0)]
+# cap 20: scaled scores of N(0, 1) inputs reach about 4, so within one wave
+# some lanes' blocks stay inside the range of the kernels' polynomial for tanh
+# (|score / cap| <= 0.2) and others take the closed form
+MOD_CASES = [("softcap", 50.0), ("softcap", 20.0), ("softcap", 2.0), ("softcap", 0.5), ("alibi", 0.0)]
 
 
 @pytest.mark.parametrize("B,H,Nq,Nk", [(1, 3, 300, 300), (1, 2, 200, 333), (2, 2, 333, 200)])
@@ -307,6 +310,10 @@ def test_score_mods_small_shapes(B, H, Nq, Nk, mask, mod, cap, D, din, dout):
     if mod == "softcap" and cap <= 2.0:
         # larger scores, so the cap bends them
         inp = synth.Inputs((inp.q.double() * 3.0).to(inp.q.dtype), inp.k, inp.v)
+    elif mod == "softcap" and cap == 20.0:
+        # about 5% of the scaled scores past 20 * 0.2: roughly half the lanes'
+        # blocks leave the polynomial's range
+        inp = synth.Inputs((inp.q.double() * 2.0).to(inp.q.dtype), inp.k, inp.v)
     o, lse = run_gpu(w, inp)
     Oref, Lref = reference(w, inp)
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
