@@ -1,28 +1,41 @@
-"""Builds libfa.so (the gfx950 kernels and the C ABI) in-tree with hipcc."""
+"""Builds libfa.so (the gfx950 kernels and the C ABI) in-tree with hipcc.
+
+Each source compiles to its own object in parallel, then one link step."""
 import os
 import subprocess
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_fwd16.hip", "fa_fwd_ks.hip", "fa_bwd.hip", "fa_api.hip"]
+SOURCES = ["fa_fwd.hip", "fa_fwd16.hip", "fa_fwd_ks.hip", "fa_fwd_serial.hip", "fa_bwd.hip", "fa_api.hip"]
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32.
 HIPFLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
 
 
-def build(out: str = LIB, extra=()) -> str:
-    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [hipcc, *HIPFLAGS, *extra, "-o", tmp, *srcs]
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
+
+
+def build(out: str = LIB, extra=()) -> str:
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmpd:
+        objs = [os.path.join(tmpd, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[hipcc, *HIPFLAGS, *extra, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            for f in [ex.submit(_run, c) for c in cmds]:
+                f.result()
+        tmp = out + ".tmp"
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, out)
     return out

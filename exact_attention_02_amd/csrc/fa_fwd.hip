@@ -442,13 +442,19 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     // often and lose (measured: c2, 384 workgroups, 29.7 against 23.3 us;
     // B8 H32 Nq128, 256 workgroups, 95 against 78 us).
     const bool ks_ok = in != IN_E4M3 && D == 64 && mod == MOD_NONE;
+    // 16-bit inputs without a score modifier: the serial kernel (four waves
+    // per SIMD at D = 64), except on the small grids above.
+    const bool sr_ok = in != IN_E4M3 && mod == MOD_NONE;
+    if (sr_ok) kernel = KERNEL_SERIAL;
     if (ks_ok && (Nq <= 64 || n_bh * ((Nq + 127) / 128) <= FA_KS_MAX_WG)) kernel = KERNEL_KSPLIT;
     if (const char* e = getenv("FA_KERNEL")) {
         const int f = atoi(e);
-        if (f == KERNEL_TILE64 || (f == KERNEL_PIPE16 && in != IN_E4M3) || (f == KERNEL_KSPLIT && ks_ok)) kernel = f;
+        if (f == KERNEL_TILE64 || (f == KERNEL_PIPE16 && in != IN_E4M3) || (f == KERNEL_KSPLIT && ks_ok) ||
+            (f == KERNEL_SERIAL && sr_ok))
+            kernel = f;
     }
-    // score modifiers: the pipelined kernel only; split-KV: the pipelined or
-    // the key-split kernel (16-bit inputs)
+    // score modifiers: the pipelined kernel only; split-KV: the serial, the
+    // pipelined or the key-split kernel (16-bit inputs)
     if (mod != MOD_NONE || (splitkv && kernel == KERNEL_TILE64)) kernel = KERNEL_PIPE16;
     // 64-key-tile kernel: two 32-row query blocks per wave halve LDS traffic
     // per MFMA and the K/V re-reads per query; one block keeps the grid large
@@ -467,6 +473,7 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
         if ((f == 1 || f == 2) && (D == 64 || f == 1)) qb = f;
     }
     pl.kernel = kernel;
+    if (kernel == KERNEL_SERIAL) qb = 1;
     pl.nw = (kernel == KERNEL_PIPE16 && D == 128) ? 8 : WAVES;
     pl.qb = qb;
     pl.br = pl.nw * 32 * qb;
@@ -502,6 +509,7 @@ static int launch_io(const Plan& pl, const Params& p, hipStream_t s) {
 int launch(const Plan& pl, const Params& p, void* stream) {
     if (pl.kernel == KERNEL_PIPE16) return launch16(pl, p, stream);
     if (pl.kernel == KERNEL_KSPLIT) return launch_ks(pl, p, stream);
+    if (pl.kernel == KERNEL_SERIAL) return launch_serial(pl, p, stream);
     hipStream_t s = (hipStream_t)stream;
     if (pl.in == IN_F16 && pl.out == OUT_F16) return launch_io<IN_F16, OUT_F16>(pl, p, s);
     if (pl.in == IN_F16 && pl.out == OUT_F32) return launch_io<IN_F16, OUT_F32>(pl, p, s);

@@ -28,7 +28,9 @@ inline SoftcapPoly softcap_poly(double kx) {
 }
 // KERNEL_KSPLIT: 16-bit inputs at D = 64 on small grids, 32 query rows per
 // workgroup whose waves split the keys (fa_fwd_ks.hip).
-enum KernelKind { KERNEL_TILE64 = 0, KERNEL_PIPE16 = 1, KERNEL_KSPLIT = 2 };
+// KERNEL_SERIAL: 16-bit inputs without a score modifier, one 32 x 32 block at
+// a time per wave, four waves per SIMD at D = 64 (fa_fwd_serial.hip).
+enum KernelKind { KERNEL_TILE64 = 0, KERNEL_PIPE16 = 1, KERNEL_KSPLIT = 2, KERNEL_SERIAL = 3 };
 
 // Everything a workgroup needs; passed by value as the kernel argument.
 struct Params {
@@ -116,6 +118,7 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod = MOD_NONE,
 int launch(const Plan& plan, const Params& p, void* stream);
 int launch16(const Plan& plan, const Params& p, void* stream);
 int launch_ks(const Plan& plan, const Params& p, void* stream);
+int launch_serial(const Plan& plan, const Params& p, void* stream);
 // The merge of the splits (p.n_split > 1): O and LSE from ws_o and ws_lse.
 int launch_combine(const Plan& plan, const Params& p, void* stream);
 

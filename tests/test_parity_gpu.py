@@ -202,11 +202,12 @@ def test_tile64_kernel_on_16bit_inputs(monkeypatch, B, H, Nq, Nk, causal, window
 @pytest.mark.parametrize("B,H,Nq,Nk", SHAPES)
 @pytest.mark.parametrize("causal,window", MODES)
 @pytest.mark.parametrize("din,dout", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
-@pytest.mark.parametrize("kernel", ["1", "2"])
+@pytest.mark.parametrize("kernel", ["1", "2", "3"])
 def test_pipelined_and_key_split_kernels_on_small_shapes(monkeypatch, B, H, Nq, Nk, causal, window, din, dout,
                                                          kernel):
     # 16-bit D = 64 problems run the key-split kernel on small grids and the
-    # pipelined kernel otherwise; both are forced here on every small shape.
+    # serial kernel otherwise (the pipelined kernel with a score modifier);
+    # each is forced here on every small shape.
     monkeypatch.setenv("FA_KERNEL", kernel)
     seed = 5000 + B * 7 + H * 13 + Nq * 3 + Nk + (17 if causal else 0) + window
     w = synth.small_workload(f"k{kernel}_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, 64,
@@ -239,7 +240,7 @@ def test_window_extents_small_shapes(B, H, Nq, Nk, wl, wr, D, din, dout):
 
 @pytest.mark.parametrize("wl,wr", [(16, 16), (5, 40), (-1, 37), (100, 100)])
 @pytest.mark.parametrize("D,qb,kernel", [(64, "2", "1"), (64, "1", "0"), (64, "2", "0"), (128, "1", "0"), (64, "1", "1"),
-                                         (64, "1", "2")])
+                                         (64, "1", "2"), (64, "1", "3"), (128, "1", "3"), (128, "1", "1")])
 def test_window_extents_other_tile_shapes(monkeypatch, wl, wr, D, qb, kernel):
     monkeypatch.setenv("FA_TILE_QB", qb)
     monkeypatch.setenv("FA_KERNEL", kernel)
@@ -383,10 +384,10 @@ def run_split(w, inp, num_splits):
 @pytest.mark.parametrize("splits", [1, 2, 7, 16, 64])
 @pytest.mark.parametrize("mask", [(True, 0, None, None), (False, 0, None, None), (True, 500, None, None),
                                   (False, 0, 300, 40)])
-@pytest.mark.parametrize("D,kernel", [(64, None), (64, "1"), (64, "2"), (128, None)])
+@pytest.mark.parametrize("D,kernel", [(64, None), (64, "1"), (64, "2"), (64, "3"), (128, None), (128, "1")])
 def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D, kernel, monkeypatch):
-    # split-KV runs on the key-split kernel (16-bit, D = 64, small grids) or
-    # the pipelined kernel; FA_KERNEL forces each
+    # split-KV runs on the key-split kernel (16-bit, D = 64, small grids), the
+    # serial kernel or the pipelined kernel; FA_KERNEL forces each
     if kernel is not None:
         monkeypatch.setenv("FA_KERNEL", kernel)
     causal, window, wl, wr = mask
@@ -400,7 +401,7 @@ def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D, kernel, monkeypatch
 
 
 @pytest.mark.parametrize("din,dout", [("f16", "f16"), ("f16", "f32"), ("bf16", "f32")])
-@pytest.mark.parametrize("kernel", [None, "1"])
+@pytest.mark.parametrize("kernel", [None, "1", "3"])
 def test_splitkv_dtypes(din, dout, kernel, monkeypatch):
     if kernel is not None:
         monkeypatch.setenv("FA_KERNEL", kernel)
@@ -411,7 +412,7 @@ def test_splitkv_dtypes(din, dout, kernel, monkeypatch):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-@pytest.mark.parametrize("kernel", [None, "1"])
+@pytest.mark.parametrize("kernel", [None, "1", "3"])
 def test_one_split_is_bitwise_the_plain_call(kernel, monkeypatch):
     # one split is the plain call, on whichever kernel both pick
     if kernel is not None:
@@ -423,7 +424,7 @@ def test_one_split_is_bitwise_the_plain_call(kernel, monkeypatch):
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
 
 
-@pytest.mark.parametrize("kernel", [None, "1"])
+@pytest.mark.parametrize("kernel", [None, "1", "3"])
 def test_splits_without_keys_give_zero_and_minus_inf(kernel, monkeypatch):
     if kernel is not None:
         monkeypatch.setenv("FA_KERNEL", kernel)
@@ -604,7 +605,7 @@ ORDERS = [("1", "0"), ("2", "3"), ("3", "1000"), ("64", "0")]
 
 
 @pytest.mark.parametrize("B,H", [(2, 8), (1, 6)])
-@pytest.mark.parametrize("din,kernel", [("bf16", "0"), ("bf16", "1"), ("bf16", "2"), ("e4m3", None)])
+@pytest.mark.parametrize("din,kernel", [("bf16", "0"), ("bf16", "1"), ("bf16", "2"), ("bf16", "3"), ("e4m3", None)])
 def test_workgroup_order_does_not_change_results(B, H, din, kernel, monkeypatch):
     # FA_WG_GROUP / FA_WG_LIGHT only reorder which workgroup runs when; every
     # output must be bitwise the default order's (heads per XCD when B*H is a
