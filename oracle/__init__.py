@@ -11,7 +11,11 @@ plain C implementation in oracle.c of softmax(scale * Q K^T) V and the
 per-row log-sum-exp, with each softmax row materialised.
 
 Parity pins: tests/test_oracle_pins.py (closed forms, invariants, brute force
-at 50 significant digits, an independent library routine, planted mistakes).
+at 50 significant digits, an independent library routine, planted mistakes in
+oracle.c) and tests/test_oracle_sampled_pins.py (the sampled-row path bit for
+bit against the full run under every mask and score modifier, the e4m3 decode
+against exact rational arithmetic, the e4m3 path against torch's SDPA on
+independently dequantised inputs, planted mistakes in this file).
 """
 from __future__ import annotations
 
