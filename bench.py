@@ -115,12 +115,28 @@ def traffic_for(w):
     return e.get("hbm_bytes_per_launch")
 
 
+def host_cores():
+    """The cores this process may run on: sched_getaffinity, capped by a cgroup CPU quota if one is set."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, int(int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
+    return max(1, n)
+
+
 def cpu_baseline(w, inp, target_s=15.0):
     """The oracle, as it is, on random rows of the workload, scaled to TFLOP/s."""
     import torch
     import oracle
     import synth
-    threads = oracle.default_threads()
+    threads = host_cores()
     g = torch.Generator().manual_seed(1234)
     n_rows_total = w.B * w.H * w.Nq
 
@@ -172,7 +188,7 @@ def cpu_baseline_bwd(w, inp, dout, target_s=15.0):
     """The oracle's backward, as it is, on whole heads of the workload, scaled to TFLOP/s."""
     import oracle
     import synth
-    threads = oracle.default_threads()
+    threads = host_cores()
     wl = -1 if w.window_left is None else w.window_left
     wr = -1 if w.window_right is None else w.window_right
     if w.window_left is None and w.window_right is None:
@@ -195,6 +211,65 @@ def cpu_baseline_bwd(w, inp, dout, target_s=15.0):
                       f"{spent:.1f} s wall"}
 
 
+def kernel_label(w):
+    """The kernels one step launches, from the library's launch plan."""
+    import exact_attention_02_amd as fa
+    if w.backward:
+        return "fa_bwd_rowstat_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one call)"
+    code = {("f16", "f16"): fa.FA_F16, ("bf16", "bf16"): fa.FA_BF16, ("f16", "f32"): fa.FA_F16_F32OUT,
+            ("e4m3", "bf16"): fa.FA_E4M3, ("bf16", "f32"): fa.FA_BF16_F32OUT}[(w.in_dtype, w.out_dtype)]
+    mod = {None: fa.FA_MOD_NONE, "softcap": fa.FA_MOD_SOFTCAP, "alibi": fa.FA_MOD_ALIBI}[w.score_mod]
+    name = fa.KERNEL_NAMES[fa.plan_kernel(w.B, w.H, w.Nq, w.Nk, w.D, code, mod, w.splitkv)]
+    if w.splitkv and fa.splitkv_num_splits(w.B, w.H, w.Nq, w.Nk, w.D, code) > 1:
+        name += " + fa_combine_kernel"
+    return name
+
+
+def timed_launches(step, stream, n, between=None):
+    """Per-launch times (ms) of n launches, each bracketed by HIP events on the
+    launch stream; `between` runs before each launch, outside its events."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        if between is not None:
+            between()
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def measured_clock_ghz(step, n_launches, n_wg):
+    """Mean shader clock during the kernel, from its own workgroups: with
+    fa_set_clock_telemetry on, each workgroup records the shader-clock and the
+    100 MHz counters at its start and end. The clock of each launch is the sum
+    of its workgroups' shader-clock advances over the sum of their 100 MHz
+    advances; the median over n_launches launches is returned."""
+    import torch
+    import exact_attention_02_amd as fa
+    dev = torch.device("cuda:0")
+    buf = torch.zeros(n_launches, 4 * n_wg, dtype=torch.int64, device=dev)
+    clocks = []
+    torch.cuda.synchronize()
+    try:
+        for i in range(n_launches):
+            st = fa.fa_set_clock_telemetry(buf[i].data_ptr(), n_wg)
+            if st != fa.FA_OK:
+                raise fa.FaError(st, "fa_set_clock_telemetry")
+            step()
+        torch.cuda.synchronize()
+    finally:
+        fa.fa_set_clock_telemetry(None, 0)
+    v = buf.view(n_launches, n_wg, 4).cpu().double()
+    for i in range(n_launches):
+        cyc, ticks = (v[i, :, 2] - v[i, :, 0]).sum().item(), (v[i, :, 3] - v[i, :, 1]).sum().item()
+        if ticks > 0:
+            clocks.append(cyc / ticks * 0.1)
+    clocks.sort()
+    return clocks[len(clocks) // 2] if clocks else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +280,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c3", help="c1 c2 c3 c4c c4w c5 c3sw c3sc c3al c6 c3bwd c3scbwd c3albwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the shader-clock pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (to scale the FETCH_SIZE/WRITE_SIZE "
                          "counters of a profiler run)")
@@ -286,6 +362,22 @@ def main():
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
 
+    # After the timed region (which alone gives `value`): per-launch times of
+    # as many launches again, a cold-cache pass with a 512 MiB write between
+    # launches, and the shader clock measured beside the kernel.
+    per = timed_launches(step, stream, args.steps)
+    per_sorted = sorted(per)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = sorted(timed_launches(step, stream, max(3, min(args.steps, 20)), between=lambda: scratch.fill_(1)))
+    del scratch
+    clock = None
+    if not args.no_clock and not w.backward:
+        import exact_attention_02_amd as fa_
+        code = fa_.dtype_code(q.dtype, out_t)
+        # records for every workgroup with room to spare (unused records stay zero and add nothing)
+        n_wg = 4 * fa_.plan_grid(w.B, w.H, w.Nq, w.Nk, w.D, True, 0, code)[0] * max(1, n_splits)
+        clock = measured_clock_ghz(step, max(8, min(args.steps, 40)), max(1, n_wg))
+
     fl = flops(w)
     tflops = fl / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.in_dtype]
@@ -310,11 +402,24 @@ def main():
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic_for(w),
-                     "kernel": "fa_fwd_kernel" if w.in_dtype == "e4m3" else "fa_fwd16_kernel", "flop_per_launch": fl,
+                     "kernel": kernel_label(w), "flop_per_launch": fl,
                      "algorithmic_hbm_bytes": algorithmic_bytes(w),
                      "timing": "HIP events on the launch stream, mean over the timed steps"},
         "wall_s_timed_region": round(wall, 4),
+        "per_launch_ms": {"mean": round(sum(per) / len(per), 5), "median": round(per_sorted[len(per) // 2], 5),
+                          "min": round(per_sorted[0], 5), "launches": len(per),
+                          "note": "one event pair per launch, after the timed region"},
+        "cold_cache_ms": {"median": round(cold[len(cold) // 2], 5), "min": round(cold[0], 5), "launches": len(cold),
+                          "note": "a 512 MiB device write before each launch, outside its events"},
     }
+    if clock is not None:
+        peak_at_clock = peak * clock / 2.4
+        res["clock"] = {"shader_ghz": round(clock, 3), "nominal_ghz": 2.4,
+                        "peak_at_clock": round(peak_at_clock, 1),
+                        "frac_at_clock": round(tflops / peak_at_clock, 4),
+                        "note": "median over launches after the timed region; each launch's workgroups record "
+                                "the shader-clock and 100 MHz counters at their start and end "
+                                "(fa_set_clock_telemetry)"}
     if w.splitkv:
         # A decode step reads the whole K/V once for a handful of queries: HBM
         # bound. The time covers both kernels of the call (splits and merge).
@@ -324,11 +429,12 @@ def main():
             "value": round(gbs, 1), "unit": "GB/s", "num_splits": n_splits,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(w),
-                         "kernel": "fa_fwd16_kernel + fa_combine_kernel",
+                         "kernel": kernel_label(w),
                          "algorithmic_hbm_bytes": algorithmic_bytes(w), "flop_per_launch": fl,
                          "timing": "HIP events on the launch stream, mean over the timed steps"},
         })
         res.pop("pct_mfma_peak", None)
+        res.pop("clock", None)
     if w.backward:
         fl = flops_bwd(w)
         tflops = fl / (ms * 1e-3) / 1e12
@@ -337,7 +443,7 @@ def main():
             "value": round(tflops, 2), "pct_mfma_peak": round(100.0 * tflops / peak, 2),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                          "frac": round(tflops / peak, 4), "traffic": traffic_for(w),
-                         "kernel": "fa_bwd_rowstat_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one call)",
+                         "kernel": kernel_label(w),
                          "flop_per_launch": fl,
                          "timing": "HIP events on the launch stream, mean over the timed steps"},
         })

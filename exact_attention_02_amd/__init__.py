@@ -25,10 +25,14 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE = 0, 1, 2, 3, 4
 FA_ERR_MASK, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_DEVICE, FA_ERR_LAUNCH = 5, 6, 7, 8, 9
 FA_ERR_MOD = 10
 FA_MOD_NONE, FA_MOD_SOFTCAP, FA_MOD_ALIBI = 0, 1, 2
+FA_KNOB_KERNEL, FA_KNOB_TILE_QB, FA_KNOB_WG_GROUP, FA_KNOB_WG_LIGHT, FA_KNOB_DEBUG = 1, 2, 3, 4, 5
 
 EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_mod", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes",
            "fa_splitkv_num_splits", "fa_bwd", "fa_bwd_mod", "fa_bwd_workspace_bytes", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class",
-           "fa_plan_window_range", "fa_plan_block_class_window")
+           "fa_plan_window_range", "fa_plan_block_class_window", "fa_plan_kernel", "fa_set_clock_telemetry", "fa_set_knob")
+
+# fa_plan_kernel's kinds and the kernels each runs (split-KV adds the merge kernel).
+KERNEL_NAMES = {0: "fa_fwd_kernel", 1: "fa_fwd16_kernel", 2: "fa_fwd_ks_kernel", 3: "fa_fwd_serial_kernel"}
 
 _lib = None
 
@@ -81,6 +85,12 @@ def load(path: str = LIB_PATH):
     lib.fa_plan_window_range.restype = I
     lib.fa_plan_block_class_window.argtypes = [I, I, I, I, I, I, I, I]
     lib.fa_plan_block_class_window.restype = I
+    lib.fa_plan_kernel.argtypes = [I, I, I, I, I, I, I, I]
+    lib.fa_plan_kernel.restype = I
+    lib.fa_set_clock_telemetry.argtypes = [P, I]
+    lib.fa_set_clock_telemetry.restype = I
+    lib.fa_set_knob.argtypes = [I, I]
+    lib.fa_set_knob.restype = I
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -170,6 +180,25 @@ def plan_tile(B, H, Nq, Nk, D, causal, window, dtype, wg):
     return bh.value, qt.value, lo.value, hi.value
 
 
+def plan_kernel(B, H, Nq, Nk, D, dtype, score_mod=FA_MOD_NONE, splitkv=False) -> int:
+    """The forward kernel kind (KERNEL_NAMES) a call would launch."""
+    k = load().fa_plan_kernel(B, H, Nq, Nk, D, dtype, int(score_mod), int(bool(splitkv)))
+    if k < 0:
+        raise FaError(-k, "fa_plan_kernel")
+    return k
+
+
+def set_knob(knob: int, value: int) -> None:
+    """A tuning override of the launch planning (FA_KNOB_*; -1 restores the default)."""
+    st = load().fa_set_knob(int(knob), int(value))
+    if st != FA_OK:
+        raise FaError(st, "fa_set_knob")
+
+
+def fa_set_clock_telemetry(buf, n) -> int:
+    return load().fa_set_clock_telemetry(buf, int(n))
+
+
 def plan_block_class(w0, w1, c0, c1, Nq, Nk, causal, window) -> int:
     return load().fa_plan_block_class(w0, w1, c0, c1, Nq, Nk, int(causal), int(window))
 
@@ -201,14 +230,105 @@ def dtype_code(in_dtype, out_dtype) -> int:
     return table[(in_dtype, out_dtype)]
 
 
+def _check(t, name, device, shape=None, dtype=None):
+    """One tensor argument: on `device`, contiguous, and of the given shape and dtype."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _device_of(q, require_gpu=True):
+    """q's device, which every other tensor argument must share; a GPU device unless require_gpu is False."""
+    import torch
+    if not isinstance(q, torch.Tensor):
+        raise ValueError("q must be a torch tensor")
+    if require_gpu and q.device.type != "cuda":
+        raise ValueError(f"q is on {q.device}: the kernels take device tensors (a ROCm GPU)")
+    return q.device
+
+
+def check_forward_args(q, k, v, out=None, lse=None, out_dtype=None, alibi=None, workspace=None,
+                       require_gpu=True):
+    """Validates attention()'s tensors before any C call and returns the output dtype.
+
+    Every tensor must be contiguous and on q's device (a GPU device unless
+    require_gpu is False, which the CPU tests use); k and v [B,H,Nk,D] of q's
+    dtype; a given out [B,H,Nq,D], whose dtype is the output type (out_dtype,
+    when also given, must agree); a given lse [B,H,Nq] float32; alibi H float32
+    slopes; workspace a uint8 tensor.
+    """
+    import torch
+    dev = _device_of(q, require_gpu)
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,Nq,D]")
+    B, H, Nq, D = q.shape
+    _check(q, "q", dev)
+    if k.dim() != 4:
+        raise ValueError("k must be [B,H,Nk,D]")
+    Nk = k.shape[2]
+    _check(k, "k", dev, (B, H, Nk, D), q.dtype)
+    _check(v, "v", dev, (B, H, Nk, D), q.dtype)
+    if out is not None:
+        if out_dtype is not None and out_dtype != out.dtype:
+            raise ValueError(f"out_dtype {out_dtype} disagrees with out.dtype {out.dtype}")
+        out_dtype = out.dtype
+        _check(out, "out", dev, (B, H, Nq, D))
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    dtype_code(q.dtype, out_dtype)   # raises on an unsupported pair
+    if lse is not None:
+        _check(lse, "lse", dev, (B, H, Nq), torch.float32)
+    if alibi is not None:
+        _check(alibi, "alibi", dev, (H,), torch.float32)
+    if workspace is not None:
+        _check(workspace, "workspace", dev, None, torch.uint8)
+    return out_dtype
+
+
+def check_backward_args(q, k, v, out, lse, dout, dq=None, dk=None, dv=None, alibi=None, workspace=None,
+                        require_gpu=True):
+    """Validates attention_bwd()'s tensors before any C call (as check_forward_args)."""
+    import torch
+    dev = _device_of(q, require_gpu)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,H,Nq,D] and k [B,H,Nk,D]")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _check(q, "q", dev)
+    for t, name in ((k, "k"), (v, "v")):
+        _check(t, name, dev, (B, H, Nk, D), q.dtype)
+    for t, name in ((out, "out"), (dout, "dout")):
+        _check(t, name, dev, (B, H, Nq, D), q.dtype)
+    _check(lse, "lse", dev, (B, H, Nq), torch.float32)
+    for t, name, shp in ((dq, "dq", (B, H, Nq, D)), (dk, "dk", (B, H, Nk, D)), (dv, "dv", (B, H, Nk, D))):
+        if t is not None:
+            _check(t, name, dev, shp, q.dtype)
+    if alibi is not None:
+        _check(alibi, "alibi", dev, (H,), torch.float32)
+    if workspace is not None:
+        _check(workspace, "workspace", dev, None, torch.uint8)
+
+
 def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, out_dtype=None,
               descales=None, stream=None, window_left=None, window_right=None,
               score_mod=None, softcap=0.0, alibi=None, num_splits=None, workspace=None):
     """O [B,H,Nq,D] and LSE [B,H,Nq] (float32) of softmax(scale Q K^T) V via libfa.
 
     q [B,H,Nq,D], k and v [B,H,Nk,D]: contiguous device tensors of one dtype
-    (float16, bfloat16 or float8_e4m3fn). out_dtype defaults to the input dtype
-    (bfloat16 for e4m3). descales = (dq, dk, dv) for e4m3 inputs.
+    (float16, bfloat16 or float8_e4m3fn). The output dtype is out.dtype when
+    out is given, else out_dtype, else the input dtype (bfloat16 for e4m3).
+    descales = (dq, dk, dv) for e4m3 inputs. Every tensor argument is checked
+    (check_forward_args) before any C call.
     The mask is (causal, window) as in fa_fwd, or, when window_left or
     window_right is given, the key interval [i' - window_left, i' + window_right]
     of fa_fwd_window (None or -1: that side unbounded; causal and window are then
@@ -221,17 +341,9 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
     bytes (allocated here when None).
     """
     import torch
+    out_dtype = check_forward_args(q, k, v, out, lse, out_dtype, alibi, workspace)
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
-    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
-        raise ValueError("k and v must be [B,H,Nk,D] matching q")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k, v must share a dtype")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous")
-    if out_dtype is None:
-        out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     code = dtype_code(q.dtype, out_dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -272,8 +384,6 @@ def attention(q, k, v, scale=None, causal=False, window=0, out=None, lse=None, o
         if mod == FA_MOD_ALIBI:
             if alibi is None:
                 alibi = torch.tensor(alibi_slopes(H), dtype=torch.float32, device=q.device)
-            if alibi.dtype != torch.float32 or alibi.numel() != H or not alibi.is_contiguous():
-                raise ValueError("alibi must be a contiguous float32 tensor of H slopes")
             slopes_ptr = alibi.data_ptr()
         st = fa_fwd_mod(*ptrs, B, H, Nq, Nk, D, float(scale), wl, wr, code, stream, mod, float(softcap), slopes_ptr)
         if st != FA_OK:
@@ -308,25 +418,16 @@ def attention_bwd(q, k, v, out, lse, dout, scale=None, causal=False, window_left
     forward's outputs for the same arguments. The mask is causal (window_left
     unbounded, window_right 0) or the extents of fa_fwd_window (None or -1:
     unbounded). workspace: a uint8 device tensor of at least
-    bwd_workspace_bytes(B, H, Nq) bytes (allocated here when None).
+    bwd_workspace_bytes(B, H, Nq) bytes (allocated here when None). Every
+    tensor argument is checked (check_backward_args) before any C call.
     score_mod, softcap, alibi: as in attention() (then through fa_bwd_mod; out
     and lse must come from the forward with the same modifier).
     """
     import torch
+    check_backward_args(q, k, v, out, lse, dout, dq, dk, dv, alibi, workspace)
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
-    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
-        raise ValueError("k and v must be [B,H,Nk,D] matching q")
-    if out.shape != q.shape or dout.shape != q.shape or lse.shape != (B, H, Nq):
-        raise ValueError("out and dout must be [B,H,Nq,D] and lse [B,H,Nq]")
-    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype) or lse.dtype != torch.float32:
-        raise ValueError("q, k, v, out, dout must share a dtype; lse must be float32")
-    for t in (q, k, v, out, dout, lse):
-        if not t.is_contiguous():
-            raise ValueError("every input must be contiguous")
-    code = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}.get(q.dtype)
-    if code is None:
-        raise ValueError(f"unsupported dtype {q.dtype}")
+    code = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}[q.dtype]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if window_left is not None or window_right is not None:
@@ -354,8 +455,6 @@ def attention_bwd(q, k, v, out, lse, dout, scale=None, causal=False, window_left
         if mod == FA_MOD_ALIBI:
             if alibi is None:
                 alibi = torch.tensor(alibi_slopes(H), dtype=torch.float32, device=q.device)
-            if alibi.dtype != torch.float32 or alibi.numel() != H or not alibi.is_contiguous():
-                raise ValueError("alibi must be a contiguous float32 tensor of H slopes")
             slopes_ptr = alibi.data_ptr()
         st = fa_bwd_mod(*ptrs, B, H, Nq, Nk, D, float(scale), wl, wr, code, stream, *ws, mod, float(softcap),
                         slopes_ptr)

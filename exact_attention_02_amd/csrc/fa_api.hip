@@ -2,7 +2,8 @@
 //
 // Every argument is validated before the first HIP call, so argument errors
 // are reported (and testable) on a machine without a GPU. The library keeps
-// no state besides a per-device cache of "is this a gfx950".
+// no state besides a per-device cache of "is this a gfx950" and the tuning
+// overrides of fa_set_knob (unset unless a caller sets them).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -18,6 +19,20 @@
 
 namespace {
 
+// fa_set_knob's overrides, indexed by FA_KNOB_*; -1: unset.
+std::atomic<int> g_knob[6] = {-1, -1, -1, -1, -1, -1};
+// fa_set_clock_telemetry's buffer (NULL: off) and its record count.
+std::atomic<unsigned long long*> g_clk{nullptr};
+std::atomic<int> g_clk_n{0};
+
+}  // namespace
+
+namespace fa {
+int knob(int which) { return (which >= 1 && which <= 5) ? g_knob[which].load(std::memory_order_relaxed) : -1; }
+}  // namespace fa
+
+namespace {
+
 struct DtypeInfo {
     int in, out;
 };
@@ -29,25 +44,19 @@ struct DtypeInfo {
 #endif
 
 // Heads per group in phase 1 of the workgroup order (decode_wg), for heads of
-// per_head_kv bytes of K and V. FA_WG_GROUP=n forces n (tuning; clamped to
-// the heads per XCD).
+// per_head_kv bytes of K and V. FA_KNOB_WG_GROUP forces it (tuning; clamped
+// to the heads per XCD).
 int head_group(long long n_bh, long long per_head_kv) {
-    if (const char* e = std::getenv("FA_WG_GROUP")) {
-        const int f = std::atoi(e);
-        if (f >= 1) return f;
-    }
+    if (const int f = fa::knob(FA_KNOB_WG_GROUP); f >= 1) return f;
     return fa::wg_head_group(n_bh, per_head_kv, (long long)FA_WG_KV_BUDGET_MB << 20);
 }
 
 // Query tiles (of n_tiles per head) whose workgroups the order interleaves
 // across heads at the end (decode_wg phase 2): the lightest 3/8. Fewer leave
 // a tail; more add L2 misses for no gain (measured on the causal B4 H12
-// N8192 forward and backward). FA_WG_LIGHT=n forces n (tuning).
+// N8192 forward and backward). FA_KNOB_WG_LIGHT forces it (tuning).
 int light_tiles(int n_tiles) {
-    if (const char* e = std::getenv("FA_WG_LIGHT")) {
-        const int f = std::atoi(e);
-        if (f >= 0) return f;
-    }
+    if (const int f = fa::knob(FA_KNOB_WG_LIGHT); f >= 0) return f;
     return (int)((3LL * n_tiles) / 8);
 }
 
@@ -157,7 +166,9 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.n_split = n_split;
     p.ws_o = (float*)workspace;
     p.ws_lse = workspace ? (float*)workspace + (size_t)B * H * n_split * Nq * D : nullptr;
-    if (std::getenv("FA_DEBUG"))
+    p.clk_n = g_clk_n.load(std::memory_order_acquire);
+    p.clk = p.clk_n > 0 ? g_clk.load(std::memory_order_acquire) : nullptr;
+    if (fa::knob(FA_KNOB_DEBUG) > 0)
         std::fprintf(stderr, "fa_fwd: in=%d out=%d D=%d kernel=%d nw=%d qb=%d br=%d bc=%d n_qt=%d n_wg=%lld\n",
                      pl.in, pl.out, pl.D, pl.kernel, pl.nw, pl.qb, pl.br, pl.bc, pl.n_qt, pl.n_wg);
     (void)hipGetLastError();  // clear a stale error left by the caller
@@ -434,6 +445,32 @@ int fa_plan_block_class_window(int w0, int w1, int c0, int c1, int Nq, int Nk, i
     int wl, wr;
     if (!window_extents(window_left, window_right, Nq, Nk, &wl, &wr)) return -1;
     return fa::tile_class(w0, w1, c0, c1, Nq, Nk, wl, wr);
+}
+
+int fa_set_knob(int knob, int value) {
+    if (knob < 1 || knob > 5 || value < -1) return FA_ERR_SHAPE;
+    g_knob[knob].store(value, std::memory_order_relaxed);
+    return FA_OK;
+}
+
+int fa_plan_kernel(int B, int H, int Nq, int Nk, int D, int dtype, int score_mod, int splitkv) {
+    DtypeInfo di;
+    const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
+    if (st != FA_OK) return -st;
+    if (score_mod != FA_MOD_NONE && score_mod != FA_MOD_SOFTCAP && score_mod != FA_MOD_ALIBI) return -FA_ERR_MOD;
+    if (score_mod != FA_MOD_NONE && di.in == fa::IN_E4M3) return -FA_ERR_MOD;
+    if (splitkv && (score_mod != FA_MOD_NONE || di.in == fa::IN_E4M3)) return -FA_ERR_DTYPE;
+    return fa::make_plan(di.in, di.out, D, B, H, Nq, score_mod, splitkv != 0).kernel;
+}
+
+int fa_set_clock_telemetry(unsigned long long* buf, int n) {
+    if ((buf == nullptr) != (n == 0) || n < 0) return buf == nullptr ? FA_ERR_NULL : FA_ERR_SHAPE;
+    if (buf && !aligned(buf, 8)) return FA_ERR_ALIGN;
+    // off first, so that a concurrent launch never pairs the new count with the old buffer
+    g_clk_n.store(0, std::memory_order_release);
+    g_clk.store(buf, std::memory_order_release);
+    g_clk_n.store(n, std::memory_order_release);
+    return FA_OK;
 }
 
 }  // extern "C"

@@ -232,4 +232,17 @@ __device__ __forceinline__ bool softcap_poly_ok(const SoftcapPoly& P, const f32x
     return am <= P.smax;
 }
 
+// Opt-in clock telemetry (fa_set_clock_telemetry in include/fa.h): the first
+// lane of a workgroup writes the shader-clock counter (s_memtime) and the
+// fixed 100 MHz counter (s_memrealtime) to record blockIdx.x mod clk_n, at the
+// workgroup's start (half 0) and at its end (half 1). A kernel argument
+// decides it, so with telemetry off the cost is one scalar branch each time.
+__device__ __forceinline__ void clock_stamp(unsigned long long* clk, int clk_n, int half) {
+    if (clk != nullptr && threadIdx.x == 0) {
+        unsigned long long* o = clk + 4 * (size_t)(blockIdx.x % (unsigned)clk_n) + 2 * half;
+        o[0] = (unsigned long long)__builtin_amdgcn_s_memtime();
+        o[1] = (unsigned long long)__builtin_amdgcn_s_memrealtime();
+    }
+}
+
 }  // namespace fa

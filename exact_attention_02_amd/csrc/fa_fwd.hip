@@ -93,6 +93,7 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
     kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
     const int t_lo = kv_lo / BC;
     const int t_hi = (kv_hi > kv_lo) ? (kv_hi + BC - 1) / BC : t_lo;
+    clock_stamp(p.clk, p.clk_n, 0);
 
     const int w0 = r0 + wave * QW;
     const int w1 = min(w0 + QW, Nq);
@@ -415,12 +416,20 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
             if (hh == 0) lp[i] = (lt > 0.f) ? (m_run[qb] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
         }
     }
+    clock_stamp(p.clk, p.clk_n, 1);
 }
 
 // ---------------------------------------------------------------- host side
 
 #ifndef FA_KS_MAX_WG
 #define FA_KS_MAX_WG 128
+#endif
+// Waves (32 query rows each) per workgroup of the serial kernel.
+#ifndef FA_SR_NW_D64
+#define FA_SR_NW_D64 4
+#endif
+#ifndef FA_SR_NW_D128
+#define FA_SR_NW_D128 4
 #endif
 Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool splitkv) {
     Plan pl;
@@ -431,7 +440,7 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     const long long n_bh = (long long)B * H;
     // 16-bit inputs use the pipelined kernel: 4 waves at D = 64, 8 waves at
     // D = 128 (its three 32 KiB LDS slots then serve 256 query rows). e4m3
-    // inputs use the 64-key-tile kernel. FA_KERNEL=0|1|2 forces one (tuning).
+    // inputs use the 64-key-tile kernel. FA_KNOB_KERNEL forces one (tuning).
     int kernel = (in == IN_E4M3) ? KERNEL_TILE64 : KERNEL_PIPE16;
     // 16-bit inputs at D = 64 go to the key-split kernel where the pipelined
     // kernel would leave waves idle: with at most 64 query rows per head (two
@@ -447,8 +456,8 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     const bool sr_ok = in != IN_E4M3 && mod == MOD_NONE;
     if (sr_ok) kernel = KERNEL_SERIAL;
     if (ks_ok && (Nq <= 64 || n_bh * ((Nq + 127) / 128) <= FA_KS_MAX_WG)) kernel = KERNEL_KSPLIT;
-    if (const char* e = getenv("FA_KERNEL")) {
-        const int f = atoi(e);
+    {
+        const int f = knob(1);   // FA_KNOB_KERNEL
         if (f == KERNEL_TILE64 || (f == KERNEL_PIPE16 && in != IN_E4M3) || (f == KERNEL_KSPLIT && ks_ok) ||
             (f == KERNEL_SERIAL && sr_ok))
             kernel = f;
@@ -466,15 +475,16 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
         const long long wg2 = n_bh * ((Nq + 255) / 256);
         if (wg2 < 512) qb = 1;
     }
-    // Tuning override: FA_TILE_QB=1|2 forces the query blocks per wave (D = 64
-    // only; D = 128 keeps one block to stay within the register file).
-    if (const char* e = getenv("FA_TILE_QB")) {
-        const int f = atoi(e);
+    // Tuning override: FA_KNOB_TILE_QB = 1 or 2 forces the query blocks per
+    // wave (D = 64 only; D = 128 keeps one block within the register file).
+    {
+        const int f = knob(2);   // FA_KNOB_TILE_QB
         if ((f == 1 || f == 2) && (D == 64 || f == 1)) qb = f;
     }
     pl.kernel = kernel;
     if (kernel == KERNEL_SERIAL) qb = 1;
     pl.nw = (kernel == KERNEL_PIPE16 && D == 128) ? 8 : WAVES;
+    if (kernel == KERNEL_SERIAL) pl.nw = D == 64 ? FA_SR_NW_D64 : FA_SR_NW_D128;
     pl.qb = qb;
     pl.br = pl.nw * 32 * qb;
     if (kernel == KERNEL_KSPLIT) {

@@ -91,6 +91,7 @@ constexpr int waves_per_simd() {
 
 template <int IN, int OUT, int D, int NW, int QB, int MOD>
 __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fwd16_kernel(Params p) {
+    clock_stamp(p.clk, p.clk_n, 0);
     constexpr int NT = 64 * NW;
     constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
@@ -768,6 +769,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
                 if (hh == 0) wlp[i] = (lt > 0.f) ? (m[qb] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
             }
         }
+        clock_stamp(p.clk, p.clk_n, 1);
         return;
     }
     uint8_t* op = p.o + (size_t)bh * Nq * D * Out<OUT>::EB;
@@ -791,6 +793,7 @@ __global__ __launch_bounds__(64 * NW, (waves_per_simd<D, QB, MOD>())) void fa_fw
             if (hh == 0) lp[i] = (lt > 0.f) ? (m[qb] + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
         }
     }
+    clock_stamp(p.clk, p.clk_n, 1);
 }
 
 // ---------------------------------------------------------------- host side

@@ -35,6 +35,7 @@ namespace fa {
 
 template <int IN, int OUT>
 __global__ __launch_bounds__(256, 2) void fa_fwd_ks_kernel(Params p) {
+    clock_stamp(p.clk, p.clk_n, 0);
     constexpr int D = 64, RB = 128, CPR = RB / 16, NKS = D / 16, ND = D / 32;
     constexpr int NT = 256, TK = 128;       // threads; keys per tile (4 sub-tiles)
     constexpr int TILE = TK * RB;           // one tensor's tile: 16 KiB
@@ -252,6 +253,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_ks_kernel(Params p) {
             if (d0 == 0) p.lse[(size_t)bh * Nq + orow] = lse;
         }
     }
+    clock_stamp(p.clk, p.clk_n, 1);
 }
 
 template <int IN, int OUT>

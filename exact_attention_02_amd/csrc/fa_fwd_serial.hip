@@ -79,6 +79,7 @@ constexpr int waves_per_simd() {
 
 template <int IN, int OUT, int D, int NW>
 __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_serial_kernel(Params p) {
+    clock_stamp(p.clk, p.clk_n, 0);
     using namespace serial;
     constexpr int NT = 64 * NW;
     constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
@@ -424,6 +425,7 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
                 }
             if (hh == 0) wlp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
         }
+        clock_stamp(p.clk, p.clk_n, 1);
         return;
     }
     uint8_t* op = p.o + (size_t)bh * Nq * D * Out<OUT>::EB;
@@ -442,6 +444,7 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
             }
         if (hh == 0) lp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
     }
+    clock_stamp(p.clk, p.clk_n, 1);
 }
 
 // ---------------------------------------------------------------- host side
@@ -455,13 +458,17 @@ static int launch_serial_one(const Plan& pl, const Params& p, hipStream_t s) {
 
 template <int IN, int OUT>
 static int launch_serial_io(const Plan& pl, const Params& p, hipStream_t s) {
-    if (pl.D == 64) return launch_serial_one<IN, OUT, 64, 4>(pl, p, s);
+    if (pl.D == 64) {
+        if (pl.nw == 8) return launch_serial_one<IN, OUT, 64, 8>(pl, p, s);
+        return launch_serial_one<IN, OUT, 64, 4>(pl, p, s);
+    }
+    if (pl.nw == 8) return launch_serial_one<IN, OUT, 128, 8>(pl, p, s);
     return launch_serial_one<IN, OUT, 128, 4>(pl, p, s);
 }
 
 int launch_serial(const Plan& pl, const Params& p, void* stream) {
     hipStream_t s = (hipStream_t)stream;
-    if (pl.nw != 4) return (int)hipErrorInvalidValue;
+    if (pl.nw != 4 && pl.nw != 8) return (int)hipErrorInvalidValue;
     if (pl.in == IN_F16 && pl.out == OUT_F16) return launch_serial_io<IN_F16, OUT_F16>(pl, p, s);
     if (pl.in == IN_F16 && pl.out == OUT_F32) return launch_serial_io<IN_F16, OUT_F32>(pl, p, s);
     if (pl.in == IN_BF16 && pl.out == OUT_BF16) return launch_serial_io<IN_BF16, OUT_BF16>(pl, p, s);

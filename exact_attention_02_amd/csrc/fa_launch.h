@@ -58,6 +58,10 @@ struct Params {
     int tl;         // and the query tiles below tl that phase 2 interleaves
     float c;        // scale * descale_q * descale_k * log2(e): scores in base-2 units
     float out_mul;  // descale_v (1 unless e4m3)
+    // fa_set_clock_telemetry: NULL, or clk_n records of four 64-bit counters
+    // (shader clock and 100 MHz at a workgroup's start, then at its end)
+    unsigned long long* clk;
+    int clk_n;
 };
 
 // The backward's arguments (16-bit inputs, D = 64 or 128). ndvec and l2 are
@@ -107,6 +111,10 @@ struct Plan {
     int n_qt;
     long long n_wg;
 };
+
+// The current value of a tuning override of fa_set_knob (include/fa.h), -1
+// when unset.
+int knob(int which);
 
 // Picks the tile shape for a problem. Pure host arithmetic.
 // mod != MOD_NONE needs the pipelined kernel, the only one with score

@@ -274,6 +274,55 @@ int fa_plan_window_range(int r0, int r1, int Nq, int Nk, int window_left, int wi
 int fa_plan_block_class_window(int w0, int w1, int c0, int c1, int Nq, int Nk,
                                int window_left, int window_right);
 
+/*
+ * fa_plan_kernel: which forward kernel a call would launch (host only):
+ *   0  the 64-key-tile kernel     (e4m3 inputs)
+ *   1  the pipelined kernel       (16-bit inputs with a score modifier)
+ *   2  the key-split kernel       (16-bit inputs at D = 64 on small grids)
+ *   3  the serial kernel          (other 16-bit inputs)
+ * score_mod != 0 plans fa_fwd_mod, splitkv != 0 fa_fwd_splitkv (which also
+ * launches the merge kernel when its split count exceeds 1), else fa_fwd and
+ * fa_fwd_window. Returns the kind, or minus an argument error code.
+ */
+int fa_plan_kernel(int B, int H, int Nq, int Nk, int D, int dtype, int score_mod, int splitkv);
+
+/*
+ * Tuning and test overrides of the launch planning, process-wide and off by
+ * default: the library reads no environment variable. fa_set_knob sets one
+ * (value -1 restores the planner's own choice) and returns FA_OK, or
+ * FA_ERR_SHAPE for an unknown knob or a value below -1. Results stay within
+ * the parity bounds under every setting; the tests use these to run each
+ * kernel and tile shape on every case.
+ *   FA_KNOB_KERNEL    force a kernel kind of fa_plan_kernel where it applies
+ *                     (1 needs 16-bit inputs; 2 16-bit inputs at D = 64 with
+ *                     no score modifier; 3 16-bit inputs with none)
+ *   FA_KNOB_TILE_QB   query blocks of 32 rows per wave (1 or 2; D = 64) for
+ *                     the 64-key-tile and pipelined kernels
+ *   FA_KNOB_WG_GROUP  heads per group in phase 1 of the workgroup order
+ *   FA_KNOB_WG_LIGHT  query tiles per head interleaved in its phase 2
+ *   FA_KNOB_DEBUG     nonzero: print each launch plan to stderr
+ * Setting a knob while another thread launches gives that launch either
+ * value; the outputs are valid under both.
+ */
+enum { FA_KNOB_KERNEL = 1, FA_KNOB_TILE_QB = 2, FA_KNOB_WG_GROUP = 3, FA_KNOB_WG_LIGHT = 4, FA_KNOB_DEBUG = 5 };
+int fa_set_knob(int knob, int value);
+
+/*
+ * fa_set_clock_telemetry: a measurement aid, off by default. With buf a
+ * caller-owned device buffer of 4 * n 64-bit values (8-byte aligned), every
+ * forward launch after the call has the first lane of each workgroup w write
+ * the shader-clock counter (s_memtime) and the fixed 100 MHz counter
+ * (s_memrealtime) when w starts, to buf[4 * (w mod n)] and the next value, and
+ * both again when w ends, to the two values after. Summed over the workgroups
+ * of one launch, the shader counter's advance over the 100 MHz counter's,
+ * times 100 MHz, is the mean shader clock the kernel ran at. fa_set_clock_
+ * telemetry(NULL, 0) turns it off. The setting is process-wide; launches on
+ * several streams while it is on write the same records. Returns FA_OK,
+ * FA_ERR_NULL (NULL with n > 0), FA_ERR_SHAPE (a buffer with n <= 0) or
+ * FA_ERR_ALIGN. The buffer must stay valid until the launches that use it end.
+ */
+int fa_set_clock_telemetry(unsigned long long* buf, int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,8 @@ def test_enums_match_header():
     for name in ["FA_F16", "FA_BF16", "FA_F16_F32OUT", "FA_E4M3", "FA_BF16_F32OUT", "FA_OK", "FA_ERR_NULL",
                  "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_DTYPE", "FA_ERR_MASK", "FA_ERR_SCALE",
                  "FA_ERR_ALIGN", "FA_ERR_DEVICE", "FA_ERR_LAUNCH", "FA_ERR_MOD", "FA_MOD_NONE", "FA_MOD_SOFTCAP",
-                 "FA_MOD_ALIBI"]:
+                 "FA_MOD_ALIBI", "FA_KNOB_KERNEL", "FA_KNOB_TILE_QB", "FA_KNOB_WG_GROUP", "FA_KNOB_WG_LIGHT",
+                 "FA_KNOB_DEBUG"]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(fa, name), name
 
@@ -230,3 +231,52 @@ def test_valid_call_without_gpu_reports_device_error():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         fa.load(str(tmp_path / "libfa.so"))
+
+
+def test_knobs_reject_unknown_names_and_values_and_restore():
+    lib = fa.load()
+    for knob in (0, 6, -1):
+        assert lib.fa_set_knob(knob, 1) == fa.FA_ERR_SHAPE
+    assert lib.fa_set_knob(fa.FA_KNOB_KERNEL, -2) == fa.FA_ERR_SHAPE
+    try:
+        assert fa.plan_kernel(4, 12, 8192, 8192, 64, fa.FA_BF16) == 3
+        fa.set_knob(fa.FA_KNOB_KERNEL, 1)
+        assert fa.plan_kernel(4, 12, 8192, 8192, 64, fa.FA_BF16) == 1
+        fa.set_knob(fa.FA_KNOB_KERNEL, 2)   # key-split needs D = 64 and no modifier: honoured here
+        assert fa.plan_kernel(4, 12, 8192, 8192, 64, fa.FA_BF16) == 2
+        assert fa.plan_kernel(4, 12, 8192, 8192, 128, fa.FA_BF16) == 3   # ... and ignored here
+    finally:
+        fa.set_knob(fa.FA_KNOB_KERNEL, -1)
+    assert fa.plan_kernel(4, 12, 8192, 8192, 64, fa.FA_BF16) == 3
+
+
+def test_environment_variables_do_not_change_the_plan(monkeypatch):
+    for name in ("FA_KERNEL", "FA_TILE_QB", "FA_WG_GROUP", "FA_WG_LIGHT", "FA_DEBUG"):
+        monkeypatch.setenv(name, "1")
+    assert fa.plan_kernel(4, 12, 8192, 8192, 64, fa.FA_BF16) == 3
+    assert fa.plan_grid(4, 12, 8192, 8192, 64, 1, 0, fa.FA_BF16) == (3072, 128, 32, 64)
+
+
+def test_plan_kernel_choices_and_errors():
+    K = fa.plan_kernel
+    assert K(4, 16, 8192, 8192, 128, fa.FA_E4M3) == 0                         # e4m3: 64-key-tile kernel
+    assert K(4, 12, 8192, 8192, 64, fa.FA_BF16, fa.FA_MOD_SOFTCAP) == 1       # score modifier: pipelined
+    assert K(1, 1, 128, 128, 64, fa.FA_F16_F32OUT) == 2                      # one workgroup: key-split
+    assert K(8, 32, 1, 16384, 64, fa.FA_BF16, splitkv=True) == 2             # decode: key-split splits
+    assert K(1, 32, 32768, 32768, 128, fa.FA_BF16) == 3                      # long context: serial
+    with pytest.raises(fa.FaError):
+        K(1, 1, 128, 128, 96, fa.FA_BF16)
+    with pytest.raises(fa.FaError):
+        K(1, 1, 128, 128, 128, fa.FA_E4M3, fa.FA_MOD_ALIBI)
+    with pytest.raises(fa.FaError):
+        K(1, 1, 128, 128, 128, fa.FA_E4M3, splitkv=True)
+
+
+def test_clock_telemetry_checks_arguments():
+    lib = fa.load()
+    buf = (ctypes.c_ulonglong * 8)()
+    assert lib.fa_set_clock_telemetry(None, 2) == fa.FA_ERR_NULL
+    assert lib.fa_set_clock_telemetry(buf, 0) == fa.FA_ERR_SHAPE
+    assert lib.fa_set_clock_telemetry(buf, -1) == fa.FA_ERR_SHAPE
+    assert lib.fa_set_clock_telemetry(ctypes.addressof(buf) + 4, 1) == fa.FA_ERR_ALIGN
+    assert lib.fa_set_clock_telemetry(None, 0) == fa.FA_OK

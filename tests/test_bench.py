@@ -86,3 +86,26 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_roofline_kernel_label_follows_the_launch_plan(name):
+    import exact_attention_02_amd as fa
+    w = synth.WORKLOADS[name]
+    label = bench.kernel_label(w)
+    if w.backward:
+        assert label.startswith("fa_bwd_")
+        return
+    kinds = {v: k for k, v in fa.KERNEL_NAMES.items()}
+    first = label.split(" + ")[0]
+    assert first in kinds
+    code = {("f16", "f16"): fa.FA_F16, ("bf16", "bf16"): fa.FA_BF16, ("f16", "f32"): fa.FA_F16_F32OUT,
+            ("e4m3", "bf16"): fa.FA_E4M3}[(w.in_dtype, w.out_dtype)]
+    mod = {None: 0, "softcap": 1, "alibi": 2}[w.score_mod]
+    assert kinds[first] == fa.plan_kernel(w.B, w.H, w.Nq, w.Nk, w.D, code, mod, w.splitkv)
+    assert ("fa_combine_kernel" in label) == (w.splitkv and fa.splitkv_num_splits(w.B, w.H, w.Nq, w.Nk, w.D, code) > 1)
+
+
+def test_host_cores_is_positive_and_within_affinity():
+    n = bench.host_cores()
+    assert 1 <= n <= len(os.sched_getaffinity(0))

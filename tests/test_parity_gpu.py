@@ -167,10 +167,10 @@ def test_small_shapes(B, H, Nq, Nk, causal, window, D, din, dout):
                                        (1, 3, 700, 700)])
 @pytest.mark.parametrize("causal,window", MODES)
 @pytest.mark.parametrize("din,dout", DTYPES)
-def test_two_query_blocks_per_wave(monkeypatch, B, H, Nq, Nk, causal, window, din, dout):
+def test_two_query_blocks_per_wave(knobs, B, H, Nq, Nk, causal, window, din, dout):
     # The tile shape with 64 query rows per wave (used for large D = 64
     # problems) on shapes small enough to compare in full.
-    monkeypatch.setenv("FA_TILE_QB", "2")
+    knobs.set("FA_TILE_QB", "2")
     seed = 2000 + B * 7 + H * 13 + Nq * 3 + Nk + (17 if causal else 0) + window
     w = synth.small_workload(f"qb2_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, 64,
                              causal, window, din, dout, seed,
@@ -185,11 +185,11 @@ def test_two_query_blocks_per_wave(monkeypatch, B, H, Nq, Nk, causal, window, di
 @pytest.mark.parametrize("causal,window", MODES)
 @pytest.mark.parametrize("D,qb", [(64, "1"), (64, "2"), (128, "1")])
 @pytest.mark.parametrize("din,dout", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32")])
-def test_tile64_kernel_on_16bit_inputs(monkeypatch, B, H, Nq, Nk, causal, window, D, qb, din, dout):
+def test_tile64_kernel_on_16bit_inputs(knobs, B, H, Nq, Nk, causal, window, D, qb, din, dout):
     # 16-bit inputs run the pipelined kernel by default; the 64-key-tile
     # kernel (the e4m3 kernel) stays selectable for them and must agree too.
-    monkeypatch.setenv("FA_KERNEL", "0")
-    monkeypatch.setenv("FA_TILE_QB", qb)
+    knobs.set("FA_KERNEL", "0")
+    knobs.set("FA_TILE_QB", qb)
     seed = 3000 + B * 7 + H * 13 + Nq * 3 + Nk + D + (17 if causal else 0) + window
     w = synth.small_workload(f"t64_B{B}H{H}q{Nq}k{Nk}D{D}c{int(causal)}w{window}_{din}_{dout}_qb{qb}", B, H, Nq, Nk, D,
                              causal, window, din, dout, seed)
@@ -203,12 +203,12 @@ def test_tile64_kernel_on_16bit_inputs(monkeypatch, B, H, Nq, Nk, causal, window
 @pytest.mark.parametrize("causal,window", MODES)
 @pytest.mark.parametrize("din,dout", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
 @pytest.mark.parametrize("kernel", ["1", "2", "3"])
-def test_pipelined_and_key_split_kernels_on_small_shapes(monkeypatch, B, H, Nq, Nk, causal, window, din, dout,
+def test_pipelined_and_key_split_kernels_on_small_shapes(knobs, B, H, Nq, Nk, causal, window, din, dout,
                                                          kernel):
     # 16-bit D = 64 problems run the key-split kernel on small grids and the
     # serial kernel otherwise (the pipelined kernel with a score modifier);
     # each is forced here on every small shape.
-    monkeypatch.setenv("FA_KERNEL", kernel)
+    knobs.set("FA_KERNEL", kernel)
     seed = 5000 + B * 7 + H * 13 + Nq * 3 + Nk + (17 if causal else 0) + window
     w = synth.small_workload(f"k{kernel}_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, 64,
                              causal, window, din, dout, seed)
@@ -241,9 +241,9 @@ def test_window_extents_small_shapes(B, H, Nq, Nk, wl, wr, D, din, dout):
 @pytest.mark.parametrize("wl,wr", [(16, 16), (5, 40), (-1, 37), (100, 100)])
 @pytest.mark.parametrize("D,qb,kernel", [(64, "2", "1"), (64, "1", "0"), (64, "2", "0"), (128, "1", "0"), (64, "1", "1"),
                                          (64, "1", "2"), (64, "1", "3"), (128, "1", "3"), (128, "1", "1")])
-def test_window_extents_other_tile_shapes(monkeypatch, wl, wr, D, qb, kernel):
-    monkeypatch.setenv("FA_TILE_QB", qb)
-    monkeypatch.setenv("FA_KERNEL", kernel)
+def test_window_extents_other_tile_shapes(knobs, wl, wr, D, qb, kernel):
+    knobs.set("FA_TILE_QB", qb)
+    knobs.set("FA_KERNEL", kernel)
     w = synth.small_workload(f"ext_qb{qb}_k{kernel}_D{D}_l{wl}r{wr}", 1, 2, 457, 457, D, False, 0, "bf16", "bf16",
                              4500 + D + wl + 3 * wr, window_left=wl, window_right=wr)
     inp = synth.make_inputs(w)
@@ -321,8 +321,8 @@ def test_score_mods_small_shapes(B, H, Nq, Nk, mask, mod, cap, D, din, dout):
 
 
 @pytest.mark.parametrize("mod,cap", [("softcap", 1.0), ("alibi", 0.0)])
-def test_score_mods_with_two_query_blocks_per_wave(monkeypatch, mod, cap):
-    monkeypatch.setenv("FA_TILE_QB", "2")
+def test_score_mods_with_two_query_blocks_per_wave(knobs, mod, cap):
+    knobs.set("FA_TILE_QB", "2")
     w = synth.small_workload(f"mod_qb2_{mod}", 1, 3, 700, 700, 64, True, 0, "bf16", "bf16", 5500,
                              score_mod=mod, softcap=cap)
     inp = synth.make_inputs(w)
@@ -331,9 +331,9 @@ def test_score_mods_with_two_query_blocks_per_wave(monkeypatch, mod, cap):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-def test_alibi_with_zero_slopes_is_bitwise_plain_attention(monkeypatch):
+def test_alibi_with_zero_slopes_is_bitwise_plain_attention(knobs):
     # score modifiers run on the pipelined kernel: plain attention is taken on it too
-    monkeypatch.setenv("FA_KERNEL", "1")
+    knobs.set("FA_KERNEL", "1")
     w = synth.small_workload("alibi0", 1, 2, 333, 333, 64, True, 0, "bf16", "bf16", 5600)
     inp = synth.make_inputs(w)
     q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
@@ -385,11 +385,11 @@ def run_split(w, inp, num_splits):
 @pytest.mark.parametrize("mask", [(True, 0, None, None), (False, 0, None, None), (True, 500, None, None),
                                   (False, 0, 300, 40)])
 @pytest.mark.parametrize("D,kernel", [(64, None), (64, "1"), (64, "2"), (64, "3"), (128, None), (128, "1")])
-def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D, kernel, monkeypatch):
+def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D, kernel, knobs):
     # split-KV runs on the key-split kernel (16-bit, D = 64, small grids), the
     # serial kernel or the pipelined kernel; FA_KERNEL forces each
     if kernel is not None:
-        monkeypatch.setenv("FA_KERNEL", kernel)
+        knobs.set("FA_KERNEL", kernel)
     causal, window, wl, wr = mask
     w = synth.small_workload(f"split{splits}_B{B}H{H}q{Nq}k{Nk}D{D}m{mask}", B, H, Nq, Nk, D, causal, window,
                              "bf16", "bf16", 6000 + B + H * 3 + Nq * 7 + Nk + D + splits,
@@ -402,9 +402,9 @@ def test_splitkv_small_shapes(B, H, Nq, Nk, splits, mask, D, kernel, monkeypatch
 
 @pytest.mark.parametrize("din,dout", [("f16", "f16"), ("f16", "f32"), ("bf16", "f32")])
 @pytest.mark.parametrize("kernel", [None, "1", "3"])
-def test_splitkv_dtypes(din, dout, kernel, monkeypatch):
+def test_splitkv_dtypes(din, dout, kernel, knobs):
     if kernel is not None:
-        monkeypatch.setenv("FA_KERNEL", kernel)
+        knobs.set("FA_KERNEL", kernel)
     w = synth.small_workload(f"split_dt_{din}_{dout}", 2, 4, 3, 5000, 64, True, 0, din, dout, 6100)
     inp = synth.make_inputs(w)
     o, lse = run_split(w, inp, "auto")
@@ -413,10 +413,10 @@ def test_splitkv_dtypes(din, dout, kernel, monkeypatch):
 
 
 @pytest.mark.parametrize("kernel", [None, "1", "3"])
-def test_one_split_is_bitwise_the_plain_call(kernel, monkeypatch):
+def test_one_split_is_bitwise_the_plain_call(kernel, knobs):
     # one split is the plain call, on whichever kernel both pick
     if kernel is not None:
-        monkeypatch.setenv("FA_KERNEL", kernel)
+        knobs.set("FA_KERNEL", kernel)
     w = synth.small_workload("split_one", 2, 3, 5, 3000, 64, True, 0, "bf16", "bf16", 6200)
     inp = synth.make_inputs(w)
     o1, l1 = run_split(w, inp, 1)
@@ -425,9 +425,9 @@ def test_one_split_is_bitwise_the_plain_call(kernel, monkeypatch):
 
 
 @pytest.mark.parametrize("kernel", [None, "1", "3"])
-def test_splits_without_keys_give_zero_and_minus_inf(kernel, monkeypatch):
+def test_splits_without_keys_give_zero_and_minus_inf(kernel, knobs):
     if kernel is not None:
-        monkeypatch.setenv("FA_KERNEL", kernel)
+        knobs.set("FA_KERNEL", kernel)
     # window (0, 0) with Nq > Nk: the first rows see nothing, and most splits of a row are empty
     w = synth.small_workload("split_empty", 1, 2, 300, 200, 64, False, 0, "bf16", "bf16", 6300,
                              window_left=0, window_right=0)
@@ -606,23 +606,23 @@ ORDERS = [("1", "0"), ("2", "3"), ("3", "1000"), ("64", "0")]
 
 @pytest.mark.parametrize("B,H", [(2, 8), (1, 6)])
 @pytest.mark.parametrize("din,kernel", [("bf16", "0"), ("bf16", "1"), ("bf16", "2"), ("bf16", "3"), ("e4m3", None)])
-def test_workgroup_order_does_not_change_results(B, H, din, kernel, monkeypatch):
+def test_workgroup_order_does_not_change_results(B, H, din, kernel, knobs):
     # FA_WG_GROUP / FA_WG_LIGHT only reorder which workgroup runs when; every
     # output must be bitwise the default order's (heads per XCD when B*H is a
     # multiple of 8, one sequence otherwise)
     if kernel is not None:
-        monkeypatch.setenv("FA_KERNEL", kernel)
+        knobs.set("FA_KERNEL", kernel)
     w = synth.small_workload(f"order_{din}_{kernel}_B{B}H{H}", B, H, 600, 600, 64, True, 0, din, "bf16", 71)
     inp = synth.make_inputs(w)
     o0, l0 = run_gpu(w, inp)
     for g, tl in ORDERS:
-        monkeypatch.setenv("FA_WG_GROUP", g)
-        monkeypatch.setenv("FA_WG_LIGHT", tl)
+        knobs.set("FA_WG_GROUP", g)
+        knobs.set("FA_WG_LIGHT", tl)
         o1, l1 = run_gpu(w, inp)
         assert torch.equal(o0.view(torch.uint8), o1.view(torch.uint8)) and torch.equal(l0, l1), (g, tl)
 
 
-def test_workgroup_order_does_not_change_the_backward(monkeypatch):
+def test_workgroup_order_does_not_change_the_backward(knobs):
     w = synth.small_workload("order_bwd", 2, 8, 500, 500, 64, True, 0, "bf16", "bf16", 72)
     inp = synth.make_inputs(w)
     q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
@@ -630,8 +630,8 @@ def test_workgroup_order_does_not_change_the_backward(monkeypatch):
     do = torch.randn(o.shape, generator=torch.Generator().manual_seed(73)).to(torch.bfloat16).to(DEV)
     g0 = fa.attention_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True)
     for g, tl in ORDERS:
-        monkeypatch.setenv("FA_WG_GROUP", g)
-        monkeypatch.setenv("FA_WG_LIGHT", tl)
+        knobs.set("FA_WG_GROUP", g)
+        knobs.set("FA_WG_LIGHT", tl)
         g1 = fa.attention_bwd(q, k, v, o, lse, do, scale=w.scale, causal=True)
         torch.cuda.synchronize()
         for a, b in zip(g0, g1):
@@ -665,3 +665,32 @@ def test_no_device_allocation():
     torch.cuda.synchronize()
     free1, _ = torch.cuda.mem_get_info()
     assert free1 == free0 and torch.cuda.max_memory_allocated() == peak0
+
+
+@pytest.mark.parametrize("din,D,kw", [("bf16", 64, {}), ("bf16", 128, {}), ("e4m3", 128, {}),
+                                      ("bf16", 64, dict(score_mod="softcap", softcap=30.0)),
+                                      ("f16", 64, dict(num_splits=4))])
+def test_clock_telemetry_leaves_results_unchanged(din, D, kw):
+    # With fa_set_clock_telemetry on, every workgroup records its start and end
+    # counters; the outputs must be bitwise those of a launch without it.
+    w = synth.small_workload(f"clk_{din}_{D}", 2, 3, 700, 700, D, True, 0, din, "bf16" if din != "f16" else "f16", 81)
+    inp = synth.make_inputs(w)
+    q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
+    ds = (inp.descale_q, inp.descale_k, inp.descale_v) if din == "e4m3" else None
+    o0, l0 = fa.attention(q, k, v, scale=w.scale, causal=True, descales=ds, **kw)
+    n = 4096
+    buf = torch.zeros(4 * n, dtype=torch.int64, device=DEV)
+    assert fa.fa_set_clock_telemetry(buf.data_ptr(), n) == fa.FA_OK
+    try:
+        o1, l1 = fa.attention(q, k, v, scale=w.scale, causal=True, descales=ds, **kw)
+        torch.cuda.synchronize()
+    finally:
+        assert fa.fa_set_clock_telemetry(None, 0) == fa.FA_OK
+    assert torch.equal(o0.view(torch.uint8), o1.view(torch.uint8)) and torch.equal(l0, l1)
+    rec = buf.view(n, 4).cpu()
+    used = rec[:, 1] != 0
+    assert used.any()
+    r = rec[used].double()
+    assert torch.all(r[:, 2] >= r[:, 0]) and torch.all(r[:, 3] >= r[:, 1])
+    ghz = (r[:, 2] - r[:, 0]).sum() / (r[:, 3] - r[:, 1]).sum() * 0.1
+    assert 0.3 < ghz.item() < 3.5, ghz.item()

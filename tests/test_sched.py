@@ -240,13 +240,13 @@ int main() {{
 
 @pytest.mark.parametrize("B,H,N", [(4, 12, 8192), (1, 12, 1000), (3, 5, 700), (2, 8, 300)])
 @pytest.mark.parametrize("group", ["1", "2", "4", "5", "64"])
-def test_grouped_order_is_a_bijection_heavy_first_per_group(B, H, N, group, monkeypatch):
+def test_grouped_order_is_a_bijection_heavy_first_per_group(B, H, N, group, knobs):
     # FA_WG_GROUP forces the heads an XCD interleaves (the last group may be
     # smaller). Every (head, tile) appears once; heads stay on their XCD when
     # B*H is a multiple of 8; per XCD the workgroups run group by group, and
     # within a group the tiles go from last to first across its heads.
-    monkeypatch.setenv("FA_WG_GROUP", group)
-    monkeypatch.setenv("FA_WG_LIGHT", "0")   # no interleaved light phase
+    knobs.set("FA_WG_GROUP", group)
+    knobs.set("FA_WG_LIGHT", "0")   # no interleaved light phase
     n_wg, br, qw, bc = fa.plan_grid(B, H, N, N, 64, True, 0, fa.FA_BF16)
     n_bh = B * H
     n_qt = (N + br - 1) // br
@@ -277,12 +277,12 @@ def test_grouped_order_is_a_bijection_heavy_first_per_group(B, H, N, group, monk
 
 @pytest.mark.parametrize("B,H,N", [(4, 12, 8192), (3, 5, 700), (2, 8, 300)])
 @pytest.mark.parametrize("group,light", [("1", "3"), ("2", "16"), ("4", "0"), ("1", "1000"), ("3", "1")])
-def test_two_phase_order_is_a_bijection(B, H, N, group, light, monkeypatch):
+def test_two_phase_order_is_a_bijection(B, H, N, group, light, knobs):
     # FA_WG_LIGHT = T: per XCD, the tiles qt >= T go first, group by group
     # (tiles last-first across a group's heads); then the tiles qt < T of all
     # the XCD's heads, last-first across them. T is clamped to the tile count.
-    monkeypatch.setenv("FA_WG_GROUP", group)
-    monkeypatch.setenv("FA_WG_LIGHT", light)
+    knobs.set("FA_WG_GROUP", group)
+    knobs.set("FA_WG_LIGHT", light)
     n_wg, br, qw, bc = fa.plan_grid(B, H, N, N, 64, True, 0, fa.FA_BF16)
     n_bh = B * H
     n_qt = (N + br - 1) // br
