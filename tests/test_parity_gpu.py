@@ -3,12 +3,17 @@
 Bounds: max |O - O_ref| <= 2e-3 for float16 inputs and <= 1e-2 for bfloat16
 inputs, relative RMS <= 5e-2 for e4m3 inputs, and |LSE - LSE_ref| /
 max(1, |LSE_ref|) <= 1e-4, where O_ref and LSE_ref are the oracle's unrounded
-float64 results on the very same stored inputs. Rows that see no key must give
+float64 results on the very same stored inputs. Where the output type's own
+rounding of O_ref can exceed what it reaches below |O| = 4 (bf16 values of
+magnitude 4 or more lie 2^-5 apart), that excess is added to the bound
+(o_bound); below 4 the bounds are as stated. Rows that see no key must give
 O = 0 and LSE = -inf exactly.
 
 The five workloads run at full size in the launch configuration the benchmark
-times, compared on sampled rows the oracle computes one by one; smaller
-shapes that span several tiles with ragged tails are compared in full.
+times and are compared on every element (the oracle computes them head by
+head); smaller shapes that span several tiles with ragged tails are compared
+in full too. The relative RMS of the e4m3 workload is taken over the whole
+tensor.
 """
 import json
 import math
@@ -61,6 +66,28 @@ def reference(w, inp, rows=None):
                             descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows, **ext)
 
 
+def half_spacing(x: torch.Tensor, dt: torch.dtype) -> torch.Tensor:
+    """Half the distance between neighbouring values of dt at |x| (normal range)."""
+    mant = {torch.bfloat16: 7, torch.float16: 10}[dt]
+    e = torch.floor(torch.log2(x.abs().clamp(min=2.0 ** -14)))
+    return 2.0 ** (e - mant - 1)
+
+
+def o_bound(w, Oref):
+    """Elementwise bound on |O - O_ref| for 16-bit inputs. The stated bound (1e-2
+    for bf16, 2e-3 for fp16 inputs) is the kernel's allowance; where the output
+    type's own rounding of O_ref can exceed the 2^-7 (bf16) or 2^-10 (fp16) it
+    reaches below |O| = 4, the excess of that rounding is added. For |O_ref| < 4
+    the bound is the stated one; a bf16 output of magnitude in [4, 8) has values
+    2^-5 apart, so its rounding alone can reach 0.0156."""
+    base = O_BOUND[w.in_dtype]
+    odt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(w.out_dtype)
+    if odt is None:
+        return torch.full_like(Oref, base)
+    below4 = half_spacing(torch.tensor(3.9, dtype=torch.float64), odt).item()
+    return base + (half_spacing(Oref, odt) - below4).clamp(min=0.0)
+
+
 def compare(w, O, L, Oref, Lref, label=""):
     """O, L: GPU results as float64 CPU tensors of the same shape as Oref, Lref."""
     O = O.reshape(-1, w.D)
@@ -80,9 +107,21 @@ def compare(w, O, L, Oref, Lref, label=""):
             stats["rel_rms"] = rel
             assert rel <= RMS_BOUND, f"{label}: relative RMS {rel:.3e} > {RMS_BOUND}"
         else:
-            err = d.abs().max().item()
+            ad = d.abs()
+            err = ad.max().item()
             stats["max_abs"] = err
-            assert err <= O_BOUND[w.in_dtype], f"{label}: max abs err {err:.3e} > {O_BOUND[w.in_dtype]}"
+            over = (ad - o_bound(w, Oref[ne])).max().item()
+            stats["max_over_bound"] = over
+            # where the worst element sits, and the floor the output format sets there: the
+            # distance from the unrounded O_ref to its nearest value of the output dtype
+            flat = int(ad.argmax())
+            ref_at = Oref[ne].reshape(-1)[flat].item()
+            got_at = O[ne].reshape(-1)[flat].item()
+            odt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(w.out_dtype)
+            floor = abs(torch.tensor(ref_at, dtype=torch.float64).to(odt).double().item() - ref_at) if odt else 0.0
+            stats.update(worst_ref=ref_at, worst_gpu=got_at, worst_floor=floor)
+            assert over <= 0.0, (f"{label}: max abs err {err:.3e}, {over:.3e} over the bound; worst element "
+                                 f"O_ref {ref_at!r}, O_gpu {got_at!r}, output-rounding floor {floor:.3e}")
         lrel = (L[ne] - Lref[ne]).abs() / Lref[ne].abs().clamp(min=1.0)
         lerr = lrel.max().item()
         stats["lse_rel"] = lerr
@@ -99,19 +138,6 @@ def compare(w, O, L, Oref, Lref, label=""):
     return stats
 
 
-def sample_rows(w, n_random=1500, seed=0):
-    """Row ids: the first 300 and last 64 rows of three heads, plus random rows."""
-    n_bh = w.B * w.H
-    rows = set()
-    for bh in sorted({0, n_bh // 2, n_bh - 1}):
-        base = bh * w.Nq
-        rows.update(base + i for i in range(min(300, w.Nq)))
-        rows.update(base + i for i in range(max(0, w.Nq - 64), w.Nq))
-    g = torch.Generator().manual_seed(seed)
-    rows.update(torch.randint(0, n_bh * w.Nq, (n_random,), generator=g).tolist())
-    return sorted(rows)
-
-
 # ------------------------------------------------------ the five workloads
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c6"])
@@ -123,18 +149,38 @@ def test_workload_full(name):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-@pytest.mark.parametrize("name", ["c3", "c4c", "c4w", "c5", "c3sw", "c3sc", "c3al"])
-def test_workload_full_size_sampled_rows(name):
-    w = synth.WORKLOADS[name]
-    inp = synth.make_inputs(w)
-    o, lse = run_gpu(w, inp)
-    rows = sample_rows(w)
+_FULL = {}
+
+
+def full_size_run(name):
+    """Inputs and GPU outputs of a full-size workload, in the launch configuration
+    the benchmark times; kept for the tests that compare it head range by head range."""
+    if name not in _FULL:
+        _FULL.clear()
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w)
+        o, lse = run_gpu(w, inp)
+        assert torch.all(torch.isfinite(o)) and not torch.any(torch.isnan(lse))
+        _FULL[name] = (w, inp, o.cpu(), lse.cpu())
+    return _FULL[name]
+
+
+# (workload, first and last (batch, head) index): every element of every head
+# is compared; c4c's 32 heads are split so that each test's oracle share stays
+# well under a minute on the box's host cores.
+FULL_SIZE = [("c3", 0, 48), ("c4c", 0, 8), ("c4c", 8, 16), ("c4c", 16, 24), ("c4c", 24, 32), ("c4w", 0, 32),
+             ("c5", 0, 64), ("c3sw", 0, 48), ("c3sc", 0, 48), ("c3al", 0, 48)]
+
+
+@pytest.mark.parametrize("name,h0,h1", FULL_SIZE)
+def test_workload_full_size_every_element(name, h0, h1):
+    w, inp, o, lse = full_size_run(name)
+    rows = torch.arange(h0 * w.Nq, h1 * w.Nq, dtype=torch.int64)
     Oref, Lref = reference(w, inp, rows=rows)
-    idx = torch.tensor(rows)
-    O = o.reshape(-1, w.D)[idx.to(DEV)].double().cpu()
-    L = lse.reshape(-1)[idx.to(DEV)].double().cpu()
-    compare(w, O, L, Oref, Lref, f"{w.name} ({len(rows)} rows)")
-    assert torch.all(torch.isfinite(o)) and not torch.any(torch.isnan(lse))
+    O = o.reshape(-1, w.D)[h0 * w.Nq:h1 * w.Nq].double()
+    L = lse.reshape(-1)[h0 * w.Nq:h1 * w.Nq].double()
+    # c5 takes all 64 heads in one test, so its relative RMS is over the whole tensor
+    compare(w, O, L, Oref, Lref, f"{w.name} heads {h0}-{h1 - 1} (every element)")
 
 
 # ---------------------------------------------- smaller shapes, full compare
