@@ -38,17 +38,23 @@ struct DtypeInfo {
 };
 
 // K and V bytes of the heads in flight across the chip that phase 1 of the
-// workgroup order keeps within: half of the 8 XCDs' 4 MiB L2 caches.
+// workgroup order keeps within: half of the 8 XCDs' 4 MiB L2 caches. The
+// serial kernel, four workgroups per CU, runs best with twice that (two
+// heads of the causal B4 H12 N8192 D64 forward per XCD: +1.7% over one).
 #ifndef FA_WG_KV_BUDGET_MB
 #define FA_WG_KV_BUDGET_MB 16
+#endif
+#ifndef FA_WG_KV_BUDGET_MB_SERIAL
+#define FA_WG_KV_BUDGET_MB_SERIAL 32
 #endif
 
 // Heads per group in phase 1 of the workgroup order (decode_wg), for heads of
 // per_head_kv bytes of K and V. FA_KNOB_WG_GROUP forces it (tuning; clamped
 // to the heads per XCD).
-int head_group(long long n_bh, long long per_head_kv) {
+int head_group(long long n_bh, long long per_head_kv, bool serial = false) {
     if (const int f = fa::knob(FA_KNOB_WG_GROUP); f >= 1) return f;
-    return fa::wg_head_group(n_bh, per_head_kv, (long long)FA_WG_KV_BUDGET_MB << 20);
+    const long long mb = serial ? FA_WG_KV_BUDGET_MB_SERIAL : FA_WG_KV_BUDGET_MB;
+    return fa::wg_head_group(n_bh, per_head_kv, mb << 20);
 }
 
 // Query tiles (of n_tiles per head) whose workgroups the order interleaves
@@ -153,7 +159,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     p.wr = wr;
     p.n_bh = B * H;
     p.n_qt = pl.n_qt;
-    p.hg = head_group(p.n_bh, 2LL * Nk * D * (di.in == fa::IN_E4M3 ? 1 : 2));
+    p.hg = head_group(p.n_bh, 2LL * Nk * D * (di.in == fa::IN_E4M3 ? 1 : 2), pl.kernel == fa::KERNEL_SERIAL);
     p.tl = light_tiles(pl.n_qt);
     p.c = scale * dq * dk * 1.44269504088896341f;
     p.out_mul = dv;
@@ -415,7 +421,9 @@ int fa_plan_tile(int B, int H, int Nq, int Nk, int D, int causal, int window, in
     if (!bh || !qtile || !kv_lo || !kv_hi) return FA_ERR_NULL;
     const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq);
     if (wg < 0 || wg >= pl.n_wg) return FA_ERR_SHAPE;
-    fa::decode_wg(wg, B * H, pl.n_qt, head_group((long long)B * H, 2LL * Nk * D * (di.in == fa::IN_E4M3 ? 1 : 2)),
+    fa::decode_wg(wg, B * H, pl.n_qt,
+                  head_group((long long)B * H, 2LL * Nk * D * (di.in == fa::IN_E4M3 ? 1 : 2),
+                             pl.kernel == fa::KERNEL_SERIAL),
                   light_tiles(pl.n_qt), bh, qtile);
     const int r0 = *qtile * pl.br;
     const int r1 = (r0 + pl.br < Nq) ? r0 + pl.br : Nq;

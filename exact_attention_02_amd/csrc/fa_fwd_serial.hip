@@ -59,10 +59,12 @@ namespace serial {
 // Largest sum of a lane half's 16 weights of one block kept without moving
 // the reference: every weight then stays at most 2^10, within fp16's range.
 constexpr float SUM_LIMIT = 1024.f;
-#ifndef FA_SR_EARLY_TILES
-#define FA_SR_EARLY_TILES 4
+// Keys at the start of a workgroup's range whose blocks always take the
+// residual pass (the running sums are small there, so most rows need it).
+#ifndef FA_SR_EARLY_KEYS
+#define FA_SR_EARLY_KEYS 256
 #endif
-constexpr int EARLY_TILES = FA_SR_EARLY_TILES;
+constexpr int EARLY_KEYS = FA_SR_EARLY_KEYS;
 // Waves per SIMD the register budget is held to.
 #ifndef FA_SR_WPS_D64
 #define FA_SR_WPS_D64 4
@@ -77,7 +79,7 @@ constexpr int waves_per_simd() {
 
 }  // namespace serial
 
-template <int IN, int OUT, int D, int NW>
+template <int IN, int OUT, int D, int NW, int TK>
 __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_serial_kernel(Params p) {
     clock_stamp(p.clk, p.clk_n, 0);
     using namespace serial;
@@ -85,7 +87,9 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
     constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
     constexpr int CPR = RB / 16;           // 16-byte chunks per row
     static_assert(RB == 128 || RB == 256, "row size");
-    constexpr int TILE = BC * RB;          // bytes of one K or V tile
+    static_assert(TK == 64 || TK == 128, "keys per tile");
+    constexpr int SUB = TK / 32;           // 32-key blocks per tile
+    constexpr int TILE = TK * RB;          // bytes of one K or V tile
     constexpr int SLOT = 2 * TILE;         // K tile, then V tile
     constexpr int NKS = D / 16;            // score MFMA steps over D
     constexpr int ND = D / 32;             // 32-row blocks of O^T
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
     const int r1 = min(r0 + BR, Nq);
     int kv_lo, kv_hi;
     kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
-    int t_lo = kv_lo / BC, t_hi = (kv_hi > kv_lo) ? (kv_hi + BC - 1) / BC : kv_lo / BC;
+    int t_lo = kv_lo / TK, t_hi = (kv_hi > kv_lo) ? (kv_hi + TK - 1) / TK : kv_lo / TK;
     if (p.n_split > 1) {
         // split s takes tiles [t_lo + nt*s/S, t_lo + nt*(s+1)/S) of the workgroup's range
         const long long nt = t_hi - t_lo;
@@ -122,7 +126,12 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
         t_lo = a;
         t_hi = b;
     }
-    const int w0 = r0 + wave * 32;
+    // Row block of this wave. Waves w and w + 4 share a SIMD; with eight waves
+    // the second of each pair takes the mirrored block (7 - w), so that under
+    // a causal mask every SIMD carries the same number of the diagonal tiles'
+    // blocks (w + 1 and 8 - w).
+    const int rblk = (NW == 8 && wave >= 4) ? 11 - wave : wave;
+    const int w0 = r0 + rblk * 32;
     const int w1 = min(w0 + 32, Nq);
 
     const uint8_t* qp = p.q + (size_t)bh * Nq * RB;
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
             const int run = 64 * wave + NT * i;
-            const unsigned soff = (unsigned)((t * BC + i * (NT / CPR)) * RB);
+            const unsigned soff = (unsigned)((t * TK + i * (NT / CPR)) * RB);
             dma16(kwords, kb + run * 16, dma_voff, soff);
             dma16(vwords, kb + TILE + run * 16, dma_voff, soff);
         }
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
     }
     const lds_u8* lds0 = (const lds_u8*)smem;
 
-    // S^T of sub-tile jj (0, 1) of the tile in slot PAR.
+    // S^T of sub-tile jj (0 .. SUB-1) of the tile in slot PAR.
     auto scores = [&](auto par, int jj, f32x16& S) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par)::value;
         const lds_u8* kb = lds0 + PAR * SLOT + 32 * jj * RB;
@@ -376,8 +385,8 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
         if (t + 1 < t_hi) issue_tile(t + 1);
-        block(par, mode, 0, 2 * t);
-        block(par, mode, 1, 2 * t + 1);
+#pragma unroll
+        for (int jj = 0; jj < SUB; ++jj) block(par, mode, jj, SUB * t + jj);
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
@@ -394,9 +403,9 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
         if (t < tb) tile(P0{}, mode, t);
     };
 
-    const int tE = min(t_hi, t_lo + EARLY_TILES);
-    const int tS0 = min(t_hi, max(tE, (f0 + 1) / 2));
-    const int tS1 = max(tS0, min(t_hi, f1 / 2));
+    const int tE = min(t_hi, t_lo + (EARLY_KEYS + TK - 1) / TK);
+    const int tS0 = min(t_hi, max(tE, (f0 + SUB - 1) / SUB));
+    const int tS1 = max(tS0, min(t_hi, f1 / SUB));
     if (t_lo < t_hi) issue_tile(t_lo);
     run(std::integral_constant<int, 2>{}, t_lo, tE);
     run(std::integral_constant<int, 1>{}, tE, tS0);
@@ -449,9 +458,9 @@ __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_s
 
 // ---------------------------------------------------------------- host side
 
-template <int IN, int OUT, int D, int NW>
+template <int IN, int OUT, int D, int NW, int TK>
 static int launch_serial_one(const Plan& pl, const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((fa_fwd_serial_kernel<IN, OUT, D, NW>), dim3((unsigned)(pl.n_wg * p.n_split)), dim3(64 * NW), 0,
+    hipLaunchKernelGGL((fa_fwd_serial_kernel<IN, OUT, D, NW, TK>), dim3((unsigned)(pl.n_wg * p.n_split)), dim3(64 * NW), 0,
                        s, p);
     return (int)hipGetLastError();
 }
@@ -459,11 +468,17 @@ static int launch_serial_one(const Plan& pl, const Params& p, hipStream_t s) {
 template <int IN, int OUT>
 static int launch_serial_io(const Plan& pl, const Params& p, hipStream_t s) {
     if (pl.D == 64) {
-        if (pl.nw == 8) return launch_serial_one<IN, OUT, 64, 8>(pl, p, s);
-        return launch_serial_one<IN, OUT, 64, 4>(pl, p, s);
+        if (pl.nw == 8) {
+            if (pl.bc == 128) return launch_serial_one<IN, OUT, 64, 8, 128>(pl, p, s);
+            return launch_serial_one<IN, OUT, 64, 8, 64>(pl, p, s);
+        }
+        return launch_serial_one<IN, OUT, 64, 4, 64>(pl, p, s);
     }
-    if (pl.nw == 8) return launch_serial_one<IN, OUT, 128, 8>(pl, p, s);
-    return launch_serial_one<IN, OUT, 128, 4>(pl, p, s);
+    if (pl.nw == 8) {
+        if (pl.bc == 128) return launch_serial_one<IN, OUT, 128, 8, 128>(pl, p, s);
+        return launch_serial_one<IN, OUT, 128, 8, 64>(pl, p, s);
+    }
+    return launch_serial_one<IN, OUT, 128, 4, 64>(pl, p, s);
 }
 
 int launch_serial(const Plan& pl, const Params& p, void* stream) {

@@ -740,3 +740,19 @@ def test_clock_telemetry_leaves_results_unchanged(din, D, kw):
     assert torch.all(r[:, 2] >= r[:, 0]) and torch.all(r[:, 3] >= r[:, 1])
     ghz = (r[:, 2] - r[:, 0]).sum() / (r[:, 3] - r[:, 1]).sum() * 0.1
     assert 0.3 < ghz.item() < 3.5, ghz.item()
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 256, 300, 300), (2, 128, 257, 400), (1, 128, 520, 333)])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 100)])
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("f16", "f32")])
+def test_eight_wave_workgroups_at_d128(B, H, Nq, Nk, causal, window, din, dout):
+    # D = 128 grids that give every CU a workgroup of 256 query rows run the
+    # serial kernel with eight waves (mirrored row blocks); ragged last tiles.
+    code = fa.dtype_code({"bf16": torch.bfloat16, "f16": torch.float16}[din], OUT_T[dout])
+    assert fa.plan_grid(B, H, Nq, Nk, 128, causal, window, code)[1] == 256
+    w = synth.small_workload(f"nw8_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, 128,
+                             causal, window, din, dout, 7000 + B + H + Nq + Nk + window)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
