@@ -24,10 +24,13 @@ FA_F16, FA_BF16, FA_F16_F32OUT, FA_E4M3, FA_BF16_F32OUT = 1, 2, 3, 4, 5
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE = 0, 1, 2, 3, 4
 FA_ERR_MASK, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_DEVICE, FA_ERR_LAUNCH = 5, 6, 7, 8, 9
 FA_ERR_MOD = 10
+FA_ERR_SCRATCH = 11
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 FA_MOD_NONE, FA_MOD_SOFTCAP, FA_MOD_ALIBI = 0, 1, 2
 FA_KNOB_KERNEL, FA_KNOB_TILE_QB, FA_KNOB_WG_GROUP, FA_KNOB_WG_LIGHT, FA_KNOB_DEBUG = 1, 2, 3, 4, 5
 
-EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_mod", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes",
+EXPORTS = ("fa_fwd", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_mod", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
+           "fa_splitkv_workspace_bytes",
            "fa_splitkv_num_splits", "fa_bwd", "fa_bwd_mod", "fa_bwd_workspace_bytes", "fa_status_str", "fa_plan_grid", "fa_plan_tile", "fa_plan_block_class",
            "fa_plan_window_range", "fa_plan_block_class_window", "fa_plan_kernel", "fa_set_clock_telemetry", "fa_set_knob")
 
@@ -63,6 +66,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_mod.restype = I
     lib.fa_fwd_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, I, P, LL]
     lib.fa_fwd_splitkv.restype = I
+    lib.fa_fwd_splitkv_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, I]
+    lib.fa_fwd_splitkv_noalloc.restype = I
     lib.fa_splitkv_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_splitkv_workspace_bytes.restype = LL
     lib.fa_splitkv_num_splits.argtypes = [I, I, I, I, I, I]
@@ -123,6 +128,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_
                    num_splits, workspace, workspace_bytes) -> int:
     return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(window_left), int(window_right), dtype,
                                  stream, int(num_splits), workspace, int(workspace_bytes))
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_right, dtype, stream,
+                           num_splits) -> int:
+    return load().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, scale, int(window_left),
+                                         int(window_right), dtype, stream, int(num_splits))
 
 
 def splitkv_workspace_bytes(B, H, Nq, D, num_splits) -> int:

@@ -99,6 +99,28 @@ int check_shape(int B, int H, int Nq, int Nk, int D, int dtype, DtypeInfo* di) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// The scratch of fa_fwd_splitkv_noalloc: one array per GPU, in the code
+// object's device memory. In host code `scratch` names a host-side stand-in,
+// not device memory: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[64];
+
+// The current device's address of `scratch`, or NULL if it cannot be had.
+void* scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    g_scratch[dev].store(q, std::memory_order_release);
+    return q;
+}
+
 std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
 
 int check_device() {
@@ -131,7 +153,7 @@ bool window_extents(int window_left, int window_right, int Nq, int Nk, int* wl, 
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
         float scale, int wl, int wr, int dtype, void* stream, float dq, float dk, float dv,
         int mod = FA_MOD_NONE, float cap = 0.f, const float* slopes = nullptr, int n_split = 1,
-        void* workspace = nullptr) {
+        void* workspace = nullptr, bool check_only = false) {
     DtypeInfo di;
     const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
     if (st != FA_OK) return st;
@@ -143,6 +165,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
     if (Nk > 0 && (!k || !v)) return FA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return FA_ERR_ALIGN;
+    if (check_only) return FA_OK;
     const int dst = check_device();
     if (dst != FA_OK) return dst;
 
@@ -264,9 +287,16 @@ int fa_splitkv_num_splits(int B, int H, int Nq, int Nk, int D, int dtype) {
     return s < 1 ? 1 : (int)s;
 }
 
-int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
-                   int D, float scale, int window_left, int window_right, int dtype, void* stream, int num_splits,
-                   void* workspace, long long workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+// fa_fwd_splitkv; with scratch, the workspace is the library's static scratch
+// array (fa_fwd_splitkv_noalloc) and every argument is checked before it is
+// looked up.
+int splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int D,
+            float scale, int window_left, int window_right, int dtype, void* stream, int num_splits, void* workspace,
+            long long workspace_bytes, bool use_scratch) {
     DtypeInfo di;
     const int st = check_shape(B, H, Nq, Nk, D, dtype, &di);
     if (st != FA_OK) return st;
@@ -277,13 +307,44 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
     const fa::Plan pl = fa::make_plan(di.in, di.out, D, B, H, Nq, fa::MOD_NONE, true);
     if (pl.n_wg * num_splits > 0x7fffffffLL) return FA_ERR_SHAPE;
     const long long need = fa_splitkv_workspace_bytes(B, H, Nq, D, num_splits);
-    if ((long long)B * H * Nq > 0 && num_splits > 1) {
+    const bool needs_ws = (long long)B * H * Nq > 0 && num_splits > 1;
+    if (use_scratch) {
+        if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+        const int chk = run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, 1.f, 1.f, 1.f,
+                            FA_MOD_NONE, 0.f, nullptr, num_splits, nullptr, true);
+        if (chk != FA_OK) return chk;
+        if (needs_ws) {
+            const int dst = check_device();
+            if (dst != FA_OK) return dst;
+            workspace = scratch_ptr();
+            if (!workspace) return FA_ERR_SCRATCH;
+            workspace_bytes = FA_NOALLOC_SCRATCH_BYTES;
+        }
+    } else if (needs_ws) {
         if (!workspace) return FA_ERR_NULL;
         if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
         if (workspace_bytes < need) return FA_ERR_SHAPE;
     }
     return run(q, k, v, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, stream, 1.f, 1.f, 1.f, FA_MOD_NONE, 0.f,
                nullptr, num_splits, num_splits > 1 ? workspace : nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                   int D, float scale, int window_left, int window_right, int dtype, void* stream, int num_splits,
+                   void* workspace, long long workspace_bytes) {
+    return splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_right, dtype, stream, num_splits,
+                   workspace, workspace_bytes, false);
+}
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                           int Nk, int D, float scale, int window_left, int window_right, int dtype, void* stream,
+                           int num_splits) {
+    return splitkv(q, k, v, o, lse, B, H, Nq, Nk, D, scale, window_left, window_right, dtype, stream, num_splits,
+                   nullptr, 0, true);
 }
 
 long long fa_bwd_workspace_bytes(int B, int H, int Nq) {
@@ -393,6 +454,7 @@ const char* fa_status_str(int status) {
         case FA_ERR_DEVICE: return "no gfx950 HIP device is current";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_MOD: return "unknown score modifier, a bad modifier parameter, or a modifier with e4m3 inputs";
+        case FA_ERR_SCRATCH: return "the problem needs more than the library's static scratch, or it is unavailable";
         default: return "unknown status";
     }
 }

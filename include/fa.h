@@ -73,8 +73,11 @@ enum {
     FA_ERR_ALIGN = 7,     /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_DEVICE = 8,    /* no HIP device, or the current device is not gfx950 */
     FA_ERR_LAUNCH = 9,    /* the kernel launch failed (hipGetLastError) */
-    FA_ERR_MOD = 10       /* fa_fwd_mod: unknown score modifier, softcap not finite
+    FA_ERR_MOD = 10,      /* fa_fwd_mod: unknown score modifier, softcap not finite
                              and positive, or a modifier with FA_E4M3 inputs */
+    FA_ERR_SCRATCH = 11   /* fa_fwd_splitkv_noalloc: the problem needs more than the
+                             library's static scratch (FA_NOALLOC_SCRATCH_BYTES), or
+                             the scratch's device address could not be obtained */
 };
 
 /* Score modifiers of fa_fwd_mod. */
@@ -178,6 +181,27 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int Nq, int Nk, int D, float scale,
                    int window_left, int window_right, int dtype, void* stream,
                    int num_splits, void* workspace, long long workspace_bytes);
+
+/*
+ * fa_fwd_splitkv_noalloc: fa_fwd_splitkv for callers that cannot allocate
+ * device memory around the call -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The split results go to a
+ * scratch array the library holds in device memory (FA_NOALLOC_SCRATCH_BYTES
+ * on each GPU it runs on, kept until the process ends) instead of a caller's
+ * workspace; the call allocates and frees nothing. Arguments, results and
+ * errors as fa_fwd_splitkv without (workspace, workspace_bytes), plus
+ * FA_ERR_SCRATCH when fa_splitkv_workspace_bytes(B, H, Nq, D, num_splits)
+ * exceeds FA_NOALLOC_SCRATCH_BYTES (checked before any device work). Every
+ * split writes its whole slice of the scratch before the merge reads it, so
+ * nothing is cleared between calls. All calls on one GPU share its array:
+ * calls that may overlap on that GPU (on several streams, or from several
+ * threads) race on it and must be serialised by the caller.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32LL << 20)
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int D, float scale,
+                           int window_left, int window_right, int dtype, void* stream,
+                           int num_splits);
 
 /*
  * Backward pass: the gradients dQ, dK, dV of O = softmax(scale Q K^T) V

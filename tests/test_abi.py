@@ -31,7 +31,7 @@ def test_enums_match_header():
     text = open(HEADER).read()
     for name in ["FA_F16", "FA_BF16", "FA_F16_F32OUT", "FA_E4M3", "FA_BF16_F32OUT", "FA_OK", "FA_ERR_NULL",
                  "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_DTYPE", "FA_ERR_MASK", "FA_ERR_SCALE",
-                 "FA_ERR_ALIGN", "FA_ERR_DEVICE", "FA_ERR_LAUNCH", "FA_ERR_MOD", "FA_MOD_NONE", "FA_MOD_SOFTCAP",
+                 "FA_ERR_ALIGN", "FA_ERR_DEVICE", "FA_ERR_LAUNCH", "FA_ERR_MOD", "FA_ERR_SCRATCH", "FA_MOD_NONE", "FA_MOD_SOFTCAP",
                  "FA_MOD_ALIBI", "FA_KNOB_KERNEL", "FA_KNOB_TILE_QB", "FA_KNOB_WG_GROUP", "FA_KNOB_WG_LIGHT",
                  "FA_KNOB_DEBUG"]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
@@ -280,3 +280,31 @@ def test_clock_telemetry_checks_arguments():
     assert lib.fa_set_clock_telemetry(buf, -1) == fa.FA_ERR_SHAPE
     assert lib.fa_set_clock_telemetry(ctypes.addressof(buf) + 4, 1) == fa.FA_ERR_ALIGN
     assert lib.fa_set_clock_telemetry(None, 0) == fa.FA_OK
+
+
+def test_noalloc_splitkv_checks_arguments_and_the_scratch_limit():
+    lib = fa.load()
+    A = 1 << 20   # a 16-byte-aligned stand-in address; nothing is launched in these cases
+    args = dict(B=2, H=8, Nq=3, Nk=5000, D=64)
+
+    def call(B, H, Nq, Nk, D, scale=0.125, wl=-1, wr=0, dtype=fa.FA_BF16, splits=4, q=A, o=A, lse=A):
+        return lib.fa_fwd_splitkv_noalloc(q, A, A, o, lse, B, H, Nq, Nk, D, scale, wl, wr, dtype, None, splits)
+
+    m = re.search(r"#define\s+FA_NOALLOC_SCRATCH_BYTES\s+\((\d+)LL\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_NOALLOC_SCRATCH_BYTES
+    # the largest decode problem that fits, and one more head than fits
+    per_head = fa.splitkv_workspace_bytes(1, 1, 4, 128, 64)
+    heads = fa.FA_NOALLOC_SCRATCH_BYTES // per_head
+    assert call(1, heads + 1, 4, 8192, 128, splits=64) == fa.FA_ERR_SCRATCH
+    assert call(1, heads, 4, 8192, 128, splits=64) in (fa.FA_ERR_DEVICE, fa.FA_OK)
+    # argument errors come first, before any device work
+    assert call(**args, scale=-1.0) == fa.FA_ERR_SCALE
+    assert call(**{**args, "D": 96}) == fa.FA_ERR_HEADDIM
+    assert call(**args, wl=-2) == fa.FA_ERR_MASK
+    assert call(**args, dtype=fa.FA_E4M3) == fa.FA_ERR_DTYPE
+    assert call(**args, splits=0) == fa.FA_ERR_SHAPE
+    assert call(**args, q=None) == fa.FA_ERR_NULL
+    assert call(**args, lse=A + 2) == fa.FA_ERR_ALIGN
+    assert call(2, 8, 0, 5000, 64) == fa.FA_OK          # empty problem: nothing to do
+    if not torch.cuda.is_available():
+        assert call(**args) == fa.FA_ERR_DEVICE
