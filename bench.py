@@ -80,7 +80,8 @@ def algorithmic_bytes(w):
 
 # The sources that decide what a workload's kernels do: the kernels, their
 # headers and the launch planning (tile shapes, workgroup order) in fa_api.hip.
-FWD_SOURCES = ("fa_fwd.hip", "fa_fwd16.hip", "fa_fwd_ks.hip", "fa_fwd_serial.hip", "fa_device.h", "fa_sched.h", "fa_launch.h",
+FWD_SOURCES = ("fa_fwd.hip", "fa_fwd16.hip", "fa_fwd_ks.hip", "fa_fwd_serial.hip", "fa_serial.h", "fa_fwd_serial_inst.hip",
+               "fa_device.h", "fa_sched.h", "fa_launch.h",
                "fa_api.hip")
 BWD_SOURCES = ("fa_bwd.hip", "fa_device.h", "fa_sched.h", "fa_launch.h", "fa_api.hip")
 

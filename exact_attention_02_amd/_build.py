@@ -10,6 +10,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
 SOURCES = ["fa_fwd.hip", "fa_fwd16.hip", "fa_fwd_ks.hip", "fa_fwd_serial.hip", "fa_bwd.hip", "fa_api.hip"]
+# The serial forward kernel's instantiation sets: fa_fwd_serial_inst.hip once
+# per (input type, score modifier), as FA_SR_IN and FA_SR_MOD (fa_launch.h).
+SERIAL_SETS = [(i, m) for i in (0, 1) for m in (0, 1, 2)]
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32.
 HIPFLAGS = [
@@ -28,10 +31,17 @@ def _run(cmd):
 
 def build(out: str = LIB, extra=()) -> str:
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    jobs = max(1, min(len(SOURCES) + len(SERIAL_SETS), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmpd:
         objs = [os.path.join(tmpd, os.path.splitext(s)[0] + ".o") for s in SOURCES]
         cmds = [[hipcc, *HIPFLAGS, *extra, "-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+        for i, m in SERIAL_SETS:
+            o = os.path.join(tmpd, f"fa_fwd_serial_inst_{i}_{m}.o")
+            objs.append(o)
+            cmds.append([hipcc, *HIPFLAGS, *extra, f"-DFA_SR_IN={i}", f"-DFA_SR_MOD={m}", "-c", "-o", o,
+                         os.path.join(CSRC, "fa_fwd_serial_inst.hip")])
+        # the slowest compiles first
+        cmds.sort(key=lambda c: 0 if "fa_fwd_serial_inst.hip" in c[-1] or c[-1].endswith(("fa_fwd16.hip", "fa_bwd.hip")) else 1)
         with ThreadPoolExecutor(max_workers=jobs) as ex:
             for f in [ex.submit(_run, c) for c in cmds]:
                 f.result()

@@ -424,24 +424,6 @@ __global__ __launch_bounds__(NTHREADS) void fa_fwd_kernel(Params p) {
 #ifndef FA_KS_MAX_WG
 #define FA_KS_MAX_WG 128
 #endif
-// Waves (32 query rows each) per workgroup of the serial kernel. At D = 128
-// eight waves (one workgroup per CU) halve the K/V staging per query row and
-// run at a higher clock: causal B1 H32 N32768 +4%, with a 4096-key window
-// +0.7%; they are used when the grid still gives every CU a workgroup. At
-// D = 64 four waves (four workgroups per CU) are faster on causal problems.
-#ifndef FA_SR_NW_D64
-#define FA_SR_NW_D64 4
-#endif
-#ifndef FA_SR_NW_D128
-#define FA_SR_NW_D128 8
-#endif
-// Keys per K/V tile of the serial kernel (64, or 128 with eight waves).
-#ifndef FA_SR_TK_D64
-#define FA_SR_TK_D64 64
-#endif
-#ifndef FA_SR_TK_D128
-#define FA_SR_TK_D128 64
-#endif
 Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool splitkv) {
     Plan pl;
     pl.in = in;
@@ -462,9 +444,9 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     // often and lose (measured: c2, 384 workgroups, 29.7 against 23.3 us;
     // B8 H32 Nq128, 256 workgroups, 95 against 78 us).
     const bool ks_ok = in != IN_E4M3 && D == 64 && mod == MOD_NONE;
-    // 16-bit inputs without a score modifier: the serial kernel (four waves
-    // per SIMD at D = 64), except on the small grids above.
-    const bool sr_ok = in != IN_E4M3 && mod == MOD_NONE;
+    // 16-bit inputs: the serial kernel (four waves per SIMD at D = 64), with
+    // or without a score modifier, except on the small grids above.
+    const bool sr_ok = in != IN_E4M3;
     if (sr_ok) kernel = KERNEL_SERIAL;
     if (ks_ok && (Nq <= 64 || n_bh * ((Nq + 127) / 128) <= FA_KS_MAX_WG)) kernel = KERNEL_KSPLIT;
     {
@@ -473,9 +455,9 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
             (f == KERNEL_SERIAL && sr_ok))
             kernel = f;
     }
-    // score modifiers: the pipelined kernel only; split-KV: the serial, the
-    // pipelined or the key-split kernel (16-bit inputs)
-    if (mod != MOD_NONE || (splitkv && kernel == KERNEL_TILE64)) kernel = KERNEL_PIPE16;
+    // score modifiers: the serial or the pipelined kernel; split-KV: the
+    // serial, the pipelined or the key-split kernel (16-bit inputs)
+    if ((mod != MOD_NONE && kernel != KERNEL_SERIAL) || (splitkv && kernel == KERNEL_TILE64)) kernel = KERNEL_PIPE16;
     // 64-key-tile kernel: two 32-row query blocks per wave halve LDS traffic
     // per MFMA and the K/V re-reads per query; one block keeps the grid large
     // on small problems and keeps D = 128 within the register file.
@@ -498,8 +480,7 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     if (kernel == KERNEL_SERIAL) {
         pl.nw = D == 64 ? FA_SR_NW_D64 : FA_SR_NW_D128;
         if (pl.nw == 8 && n_bh * ((Nq + 255) / 256) < 256) pl.nw = 4;
-        const int tk = D == 64 ? FA_SR_TK_D64 : FA_SR_TK_D128;
-        pl.bc = (pl.nw == 8 && tk == 128) ? 128 : 64;
+        pl.bc = serial_tile_keys(pl.nw, D == 64 ? FA_SR_TK_D64 : FA_SR_TK_D128);
     }
     pl.qb = qb;
     pl.br = pl.nw * 32 * qb;

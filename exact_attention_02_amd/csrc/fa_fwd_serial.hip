@@ -1,493 +1,24 @@
-// Fused exact-attention forward for 16-bit inputs (fp16, bf16) on gfx950:
-// each wave works through its 32 x 32 blocks one at a time, and several waves
-// share each SIMD.
-//
-// The computation is the block-by-block loop of the aiinarabic.com
-// flash-attention page (load a block of K and V on chip, score it, softmax it,
-// multiply by V, merge; the algorithm paragraph under Figure 4), with the
-// running max and sum of the FLASHLIGHT summary on gist.science (Methodology
-// item 3).
-//
-// Why one block at a time: on gfx950 the matrix core runs one wave's MFMAs
-// while the SIMD issues another wave's VALU work, so the overlap of the two
-// comes from the waves sharing the SIMD. At D = 64 a 32 x 32 block costs 8
-// MFMAs (256 SIMD cycles) and about 55 VALU instructions of softmax, 16 of
-// them exponentials, which take longer than the MFMAs: the VALU is the bound.
-// Each wave therefore runs the plain sequence -- scores on MFMA, softmax on
-// the VALU, P.V on MFMA -- with as few VALU instructions beside the
-// exponentials, sums and conversions as possible, and the register budget is
-// held to four waves per SIMD (two at D = 128, where the MFMAs are the bound)
-// so that the SIMD always finds a wave with work for each unit.
-//
-// Per block (wave rows x 32 keys), lane l holds query l mod 32 and 16 of the
-// 32 keys (S^T = K Q^T on a 32 x 32 MFMA accumulator):
-//   S  = K Q^T                             (D/16 MFMAs)
-//   p  = 2^(c s - m), 16 per lane          (one FMA and one exponential each)
-//   ts = the lane half's sum of p          (a fixed pairwise order)
-//   P  = p rounded to the input type       (8 conversions)
-//   O^T += V^T P^T                         (D/16 MFMAs; V read transposed)
-// m is a reference per row that moves only when needed: a block whose lane-
-// half sum exceeds SUM_LIMIT (a score grew past m), or the row's first block
-// (m = -inf makes ts infinite), is formed again exactly against the row max,
-// rescaling O and the sum by 2^(m_old - m_new). O / l and the log-sum-exp do
-// not depend on which m was used. When a block's sum exceeds a third of the
-// lane half's sum so far (the first blocks of a row, peaked rows), P's
-// rounding residual (p - P, rounded) also multiplies V, so that a dominant
-// weight's rounding does not reach O. Both checks are one compare against
-// thr = min(lh / 3, SUM_LIMIT), and both corrections live off the common path.
-//
-// Tiles of 64 keys go HBM -> LDS by direct-to-LDS buffer loads into two
-// slots: tile t+1 is requested at the start of tile t, one barrier per tile.
-// The key range of a workgroup runs through four phases: the first
-// EARLY_TILES tiles, whose blocks always take the residual pass; tiles with
-// a mask edge or skipped blocks before and after the tiles in which every
-// block of every wave is fully visible; and those steady tiles, whose blocks
-// run with no class checks at all.
+// Launch of the serial forward kernel (fa_serial.h): picks the instantiation
+// set for the input type and the score modifier. Each set is compiled in an
+// object of its own from fa_fwd_serial_inst.hip.
 #include <hip/hip_runtime.h>
-#include <stdint.h>
 
-#include <type_traits>
-
-#include "fa_device.h"
 #include "fa_launch.h"
-#include "fa_sched.h"
 
 namespace fa {
 
-namespace serial {
-
-// Largest sum of a lane half's 16 weights of one block kept without moving
-// the reference: every weight then stays at most 2^10, within fp16's range.
-constexpr float SUM_LIMIT = 1024.f;
-// Keys at the start of a workgroup's range whose blocks always take the
-// residual pass (the running sums are small there, so most rows need it).
-#ifndef FA_SR_EARLY_KEYS
-#define FA_SR_EARLY_KEYS 256
-#endif
-constexpr int EARLY_KEYS = FA_SR_EARLY_KEYS;
-// Waves per SIMD the register budget is held to.
-#ifndef FA_SR_WPS_D64
-#define FA_SR_WPS_D64 4
-#endif
-#ifndef FA_SR_WPS_D128
-#define FA_SR_WPS_D128 2
-#endif
-template <int D>
-constexpr int waves_per_simd() {
-    return D == 64 ? FA_SR_WPS_D64 : FA_SR_WPS_D128;
-}
-
-}  // namespace serial
-
-template <int IN, int OUT, int D, int NW, int TK>
-__global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_serial_kernel(Params p) {
-    clock_stamp(p.clk, p.clk_n, 0);
-    using namespace serial;
-    constexpr int NT = 64 * NW;
-    constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
-    constexpr int CPR = RB / 16;           // 16-byte chunks per row
-    static_assert(RB == 128 || RB == 256, "row size");
-    static_assert(TK == 64 || TK == 128, "keys per tile");
-    constexpr int SUB = TK / 32;           // 32-key blocks per tile
-    constexpr int TILE = TK * RB;          // bytes of one K or V tile
-    constexpr int SLOT = 2 * TILE;         // K tile, then V tile
-    constexpr int NKS = D / 16;            // score MFMA steps over D
-    constexpr int ND = D / 32;             // 32-row blocks of O^T
-    constexpr int BR = 32 * NW;            // query rows per workgroup
-    constexpr int NDMA = TILE / 16 / NT;   // 16-byte copies per thread per tensor per tile
-    static_assert(NDMA >= 1 && TILE % (16 * NT) == 0, "tile staging");
-
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int hh = lane >> 5;
-    const int g = lane >> 4, cl = lane & 15;   // 16-lane group of the transposing reads
-
-    const int Nq = p.Nq, Nk = p.Nk, wl = p.wl, wr = p.wr;
-    int bh, qt, split = 0;
-    long long wgid = blockIdx.x;
-    if (p.n_split > 1) {
-        split = (int)(wgid % p.n_split);
-        wgid /= p.n_split;
-    }
-    decode_wg(wgid, p.n_bh, p.n_qt, p.hg, p.tl, &bh, &qt);
-    const int r0 = qt * BR;
-    const int r1 = min(r0 + BR, Nq);
-    int kv_lo, kv_hi;
-    kv_range(r0, r1, Nq, Nk, wl, wr, &kv_lo, &kv_hi);
-    int t_lo = kv_lo / TK, t_hi = (kv_hi > kv_lo) ? (kv_hi + TK - 1) / TK : kv_lo / TK;
-    if (p.n_split > 1) {
-        // split s takes tiles [t_lo + nt*s/S, t_lo + nt*(s+1)/S) of the workgroup's range
-        const long long nt = t_hi - t_lo;
-        const int a = t_lo + (int)(nt * split / p.n_split), b = t_lo + (int)(nt * (split + 1) / p.n_split);
-        t_lo = a;
-        t_hi = b;
-    }
-    // Row block of this wave. Waves w and w + 4 share a SIMD; with eight waves
-    // the second of each pair takes the mirrored block (7 - w), so that under
-    // a causal mask every SIMD carries the same number of the diagonal tiles'
-    // blocks (w + 1 and 8 - w).
-    const int rblk = (NW == 8 && wave >= 4) ? 11 - wave : wave;
-    const int w0 = r0 + rblk * 32;
-    const int w1 = min(w0 + 32, Nq);
-
-    const uint8_t* qp = p.q + (size_t)bh * Nq * RB;
-    const uint8_t* kp = p.k + (size_t)bh * Nk * RB;
-    const uint8_t* vp = p.v + (size_t)bh * Nk * RB;
-
-    // Q fragments, B operand of S^T = K Q^T: lane holds query w0 + l32,
-    // head-dim elements [16s + 8hh, +8). Rows at or past Nq read as zeros.
-    i32x4 qf[NKS];
-    {
-        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)(Nq * RB));
-#pragma unroll
-        for (int s = 0; s < NKS; ++s)
-            qf[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                qrs, (w0 + l32) * RB + (16 * s + 8 * hh) * 2, 0, 0));
-    }
-
-    f32x16 oacc[ND];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
-    float m = -INFINITY;   // the row's reference (base-2 units); -inf: none yet
-    float lh = 0.f;        // this lane half's weight sum
-    float thr = 0.f;       // min(lh / 3, SUM_LIMIT): a block above it takes the rare path
-    const float c2 = p.c;  // scale * log2(e): scores in base-2 units
-
-    // ---- K/V copies: lane l of a wave fills the l-th 16-byte slot of a 1 KiB
-    // run of the tile, fetching the global chunk that belongs there under the
-    // swizzled layout; rows at or past Nk read as zeros.
-    const i32x4 kwords = rsrc_words(kp, (unsigned)(Nk * RB));
-    const i32x4 vwords = rsrc_words(vp, (unsigned)(Nk * RB));
-    const unsigned smem_base = (unsigned)(unsigned long long)(lds_u8*)smem;
-    static_assert((NT / CPR) % 16 == 0, "copy rows");
-    const unsigned dma_voff = [&] {
-        const int slot = 64 * wave + lane;
-        const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
-        return (unsigned)(x * RB + c * 16);
-    }();
-    auto issue_tile = [&](int t) {
-        const unsigned kb = smem_base + (unsigned)((t & 1) * SLOT);
-#pragma unroll
-        for (int i = 0; i < NDMA; ++i) {
-            const int run = 64 * wave + NT * i;
-            const unsigned soff = (unsigned)((t * TK + i * (NT / CPR)) * RB);
-            dma16(kwords, kb + run * 16, dma_voff, soff);
-            dma16(vwords, kb + TILE + run * 16, dma_voff, soff);
-        }
-    };
-
-    // ---- block classes. Wave: [jf0, jf1) every pair visible, [ju0, ju1) at
-    // least one. Workgroup: tiles [ts0, ts1) in which both blocks are fully
-    // visible to every wave that holds rows.
-    int jf0, jf1, ju0, ju1;
-    block_ranges32(w0, w1, Nq, Nk, wl, wr, &jf0, &jf1, &ju0, &ju1);
-    int f0 = 0, f1 = 1 << 30;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-        const int a0 = r0 + 32 * ww, a1 = min(a0 + 32, Nq);
-        if (a1 <= a0) continue;
-        int x0, x1, y0, y1;
-        block_ranges32(a0, a1, Nq, Nk, wl, wr, &x0, &x1, &y0, &y1);
-        f0 = max(f0, x0);
-        f1 = min(f1, x1);
-    }
-    auto block_skip = [&](int j) { return (unsigned)(j - ju0) >= (unsigned)(ju1 - ju0); };
-    auto block_full = [&](int j) { return (unsigned)(j - jf0) < (unsigned)(jf1 - jf0); };
-
-    // ---- LDS addresses. Element r of lane (l32, hh) in S^T of sub-tile j is
-    // key 32j + 8(r/4) + 4hh + r%4 against query w0 + l32. The per-lane parts
-    // of the addresses are fixed; slot, sub-tile and MFMA step are immediate
-    // offsets (the swizzle depends on the row mod 16, which those multiples
-    // of 16 rows leave unchanged).
-    int kofs[NKS];
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) kofs[s] = lds_pos<RB>(l32, 2 * s + hh);
-    int vofs[ND][2];   // transposing V reads: rows 4hh + cl/4 and 8 rows further
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-        const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
-#pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) vofs[db][h8] = lds_pos<RB>(4 * hh + (cl >> 2) + 8 * h8, ch) + 8 * (cl & 1);
-    }
-    const lds_u8* lds0 = (const lds_u8*)smem;
-
-    // S^T of sub-tile jj (0 .. SUB-1) of the tile in slot PAR.
-    auto scores = [&](auto par, int jj, f32x16& S) __attribute__((always_inline)) {
-        constexpr int PAR = decltype(par)::value;
-        const lds_u8* kb = lds0 + PAR * SLOT + 32 * jj * RB;
-        i32x4 a[NKS];
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) a[s] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(kb + kofs[s]);
-        S = f32x16{};
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) S = mfma16(IN, a[s], qf[s], S);
-    };
-    // V^T operands of sub-tile jj for its two 16-key MFMA steps, in the key
-    // order P has: step sp, lane half hh, k-slot e holds key
-    // 32j + 16sp + 8(e/4) + 4hh + e%4 (two transposing reads of 4 rows).
-    auto v_operands = [&](auto par, int jj, i32x4(&va)[2][ND]) __attribute__((always_inline)) {
-        constexpr int PAR = decltype(par)::value;
-        const lds_u8* vb = lds0 + PAR * SLOT + TILE + 32 * jj * RB;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
-                const i32x2 u0 = read_tr16(vb + 16 * sp * RB + vofs[db][0]);
-                const i32x2 u1 = read_tr16(vb + 16 * sp * RB + vofs[db][1]);
-                va[sp][db] = i32x4{u0[0], u0[1], u1[0], u1[1]};
-            }
-    };
-    auto pv = [&](const i32x4(&va)[2][ND], const i32x4(&P)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-            for (int db = 0; db < ND; ++db) oacc[db] = mfma16(IN, va[sp][db], P[sp], oacc[db]);
-    };
-
-    // Masked scores of sub-tile j become -inf: row i = w0 + l32 sees keys
-    // [klo, khi) (none when i is past the wave's rows).
-    auto mask = [&](int j, f32x16& S) __attribute__((always_inline)) {
-        const int c0 = 32 * j;
-        int ln = lane;
-        asm volatile("" : "+v"(ln));   // recomputed here, not held across the loop
-        const int i = w0 + (ln & 31);
-        const int ip = i + (Nk - Nq);
-        int klo = ip - wl;
-        int khi = ip + wr + 1;
-        klo = klo > 0 ? klo : 0;
-        khi = khi < Nk ? khi : Nk;
-        if (i >= w1) khi = klo;
-        const int a = klo - c0 - 4 * (ln >> 5), b = khi - c0 - 4 * (ln >> 5);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int off = 8 * (r >> 2) + (r & 3);
-            S[r] = (off < a || off >= b) ? -INFINITY : S[r];
-        }
-    };
-
-    // p = 2^(c*s - ms) for the 16 scores, their sum (a fixed pairwise order)
-    // and p rounded to the MFMA type.
-    auto softmax = [&](const f32x16& S, float ms, float(&pr)[16], float& ts, i32x4(&P)[2])
-        __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -ms));
-        float s8[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) s8[r] = pr[2 * r] + pr[2 * r + 1];
-        ts = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            const int o = 8 * sp;
-            P[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
-                          pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
-        }
-    };
-    // The rounding residual of the weights, lo = p - P rounded to the MFMA
-    // type (zero where on is false).
-    auto residual = [&](const float(&pr)[16], const i32x4(&P)[2], bool on, i32x4(&lo)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            const int o = 8 * sp;
-            const i32x4 h = P[sp];
-            const i32x4 d = i32x4{pack2<IN>(pr[o + 0] - unpack_lo<IN>(h[0]), pr[o + 1] - unpack_hi<IN>(h[0])),
-                                  pack2<IN>(pr[o + 2] - unpack_lo<IN>(h[1]), pr[o + 3] - unpack_hi<IN>(h[1])),
-                                  pack2<IN>(pr[o + 4] - unpack_lo<IN>(h[2]), pr[o + 5] - unpack_hi<IN>(h[2])),
-                                  pack2<IN>(pr[o + 6] - unpack_lo<IN>(h[3]), pr[o + 7] - unpack_hi<IN>(h[3]))};
-            lo[sp] = i32x4{on ? d[0] : 0, on ? d[1] : 0, on ? d[2] : 0, on ? d[3] : 0};
-        }
-    };
-
-    // The exact redo of a block for the rows whose reference must move (no
-    // reference yet, or a lane half's sum above SUM_LIMIT): their max over
-    // the block's visible keys becomes the reference, O and the sums are
-    // rescaled, and the weights are formed again. S holds the block's
-    // (masked) scores. Rows whose reference does not move form the same bits
-    // again, so a row's result depends on its own scores alone.
-    auto redo = [&](const f32x16& S, bool trig, float(&pr)[16], float& ts, i32x4(&P)[2]) __attribute__((always_inline)) {
-        const unsigned tr = trig ? 1u : 0u;
-        auto pw = __builtin_amdgcn_permlane32_swap(tr, tr, false, false);
-        const bool row = (pw[0] | pw[1]) != 0;
-        float mx = S[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-        mx = max_halves(mx);
-        const float mnew = row ? fmaxf(m, mx * c2) : m;
-        const bool mv = mnew != m;
-        const float alpha = mv ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
-        m = mnew;
-        if (__builtin_amdgcn_ballot_w64(mv) != 0) {
-            lh *= alpha;
-#pragma unroll
-            for (int db = 0; db < ND; ++db) oacc[db] *= alpha;
-        }
-        softmax(S, (mnew == -INFINITY) ? 0.f : mnew, pr, ts, P);
-    };
-
-    // ---- one block: sub-tile jj of the tile in slot PAR, key block j.
-    // MODE 0: steady (fully visible, no checks but the one compare);
-    // MODE 1: checked (skip / edge classes); MODE 2: checked and early (the
-    // residual pass on every lane).
-    auto block = [&](auto par, auto mode, int jj, int j) __attribute__((always_inline)) {
-        constexpr int MODE = decltype(mode)::value;
-        bool edge = false;
-        if constexpr (MODE != 0) {
-            if (block_skip(j)) return;
-            edge = !block_full(j);
-        }
-        f32x16 S;
-        scores(par, jj, S);
-        if constexpr (MODE != 0) {
-            if (edge) mask(j, S);
-        }
-        i32x4 va[2][ND];
-        v_operands(par, jj, va);
-        float pr[16], ts;
-        i32x4 P[2];
-        // m = -inf (no reference yet) gives ts = inf or NaN: the redo runs
-        softmax(S, m, pr, ts, P);
-        if (__builtin_amdgcn_ballot_w64(!(ts <= thr)) != 0) {
-            const bool trig = !(ts <= SUM_LIMIT);
-            if (__builtin_amdgcn_ballot_w64(trig) != 0) {
-                f32x16 S2;
-                scores(par, jj, S2);
-                if constexpr (MODE != 0) {
-                    if (edge) mask(j, S2);
-                }
-                redo(S2, trig, pr, ts, P);
-            }
-            if constexpr (MODE != 2) {
-                const bool sr = ts * 3.f > lh;
-                if (__builtin_amdgcn_ballot_w64(sr) != 0) {
-                    i32x4 lo[2];
-                    residual(pr, P, sr, lo);
-                    pv(va, lo);
-                }
-            }
-        }
-        if constexpr (MODE == 2) {
-            i32x4 lo[2];
-            residual(pr, P, true, lo);
-            pv(va, lo);
-        }
-        lh += ts;
-        thr = fminf(lh * (1.f / 3.f), SUM_LIMIT);
-        pv(va, P);
-    };
-
-    // ---- tiles: the copies of tile t landed (each wave waits for its own,
-    // the barrier for everyone's), every wave is past tile t-1, so tile t+1
-    // goes into t-1's slot; then the two sub-tiles of tile t.
-    auto tile = [&](auto par, auto mode, int t) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        __syncthreads();
-        if (t + 1 < t_hi) issue_tile(t + 1);
-#pragma unroll
-        for (int jj = 0; jj < SUB; ++jj) block(par, mode, jj, SUB * t + jj);
-    };
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    auto run = [&](auto mode, int ta, int tb) __attribute__((always_inline)) {
-        int t = ta;
-        if (t < tb && (t & 1)) {
-            tile(P1{}, mode, t);
-            ++t;
-        }
-        for (; t + 1 < tb; t += 2) {
-            tile(P0{}, mode, t);
-            tile(P1{}, mode, t + 1);
-        }
-        if (t < tb) tile(P0{}, mode, t);
-    };
-
-    const int tE = min(t_hi, t_lo + (EARLY_KEYS + TK - 1) / TK);
-    const int tS0 = min(t_hi, max(tE, (f0 + SUB - 1) / SUB));
-    const int tS1 = max(tS0, min(t_hi, f1 / SUB));
-    if (t_lo < t_hi) issue_tile(t_lo);
-    run(std::integral_constant<int, 2>{}, t_lo, tE);
-    run(std::integral_constant<int, 1>{}, tE, tS0);
-    run(std::integral_constant<int, 0>{}, tS0, tS1);
-    run(std::integral_constant<int, 1>{}, tS1, t_hi);
-
-    // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l); a split writes both
-    // in fp32 to its slice of the workspace instead
-    const float lt = sum_halves(lh);
-    const int i = w0 + l32;
-    if (p.n_split > 1) {
-        const size_t sl = (size_t)bh * p.n_split + split;
-        float* wo = p.ws_o + sl * Nq * D;
-        float* wlp = p.ws_lse + sl * Nq;
-        if (i < w1) {
-            const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-            uint8_t* orow = (uint8_t*)(wo + (size_t)i * D);
-#pragma unroll
-            for (int db = 0; db < ND; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x16& a = oacc[db];
-                    const int d = 32 * db + 8 * r4 + 4 * hh;
-                    Out<OUT_F32>::store4(orow + d * 4, a[4 * r4] * inv, a[4 * r4 + 1] * inv, a[4 * r4 + 2] * inv,
-                                         a[4 * r4 + 3] * inv);
-                }
-            if (hh == 0) wlp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
-        }
-        clock_stamp(p.clk, p.clk_n, 1);
-        return;
-    }
-    uint8_t* op = p.o + (size_t)bh * Nq * D * Out<OUT>::EB;
-    float* lp = p.lse + (size_t)bh * Nq;
-    if (i < w1) {
-        const float inv = (lt > 0.f) ? p.out_mul / lt : 0.f;
-        uint8_t* orow = op + (size_t)i * D * Out<OUT>::EB;
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x16& a = oacc[db];
-                const int d = 32 * db + 8 * r4 + 4 * hh;
-                Out<OUT>::store4(orow + d * Out<OUT>::EB, a[4 * r4] * inv, a[4 * r4 + 1] * inv, a[4 * r4 + 2] * inv,
-                                 a[4 * r4 + 3] * inv);
-            }
-        if (hh == 0) lp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
-    }
-    clock_stamp(p.clk, p.clk_n, 1);
-}
-
-// ---------------------------------------------------------------- host side
-
-template <int IN, int OUT, int D, int NW, int TK>
-static int launch_serial_one(const Plan& pl, const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((fa_fwd_serial_kernel<IN, OUT, D, NW, TK>), dim3((unsigned)(pl.n_wg * p.n_split)), dim3(64 * NW), 0,
-                       s, p);
-    return (int)hipGetLastError();
-}
-
-template <int IN, int OUT>
-static int launch_serial_io(const Plan& pl, const Params& p, hipStream_t s) {
-    if (pl.D == 64) {
-        if (pl.nw == 8) {
-            if (pl.bc == 128) return launch_serial_one<IN, OUT, 64, 8, 128>(pl, p, s);
-            return launch_serial_one<IN, OUT, 64, 8, 64>(pl, p, s);
-        }
-        return launch_serial_one<IN, OUT, 64, 4, 64>(pl, p, s);
-    }
-    if (pl.nw == 8) {
-        if (pl.bc == 128) return launch_serial_one<IN, OUT, 128, 8, 128>(pl, p, s);
-        return launch_serial_one<IN, OUT, 128, 8, 64>(pl, p, s);
-    }
-    return launch_serial_one<IN, OUT, 128, 4, 64>(pl, p, s);
-}
-
 int launch_serial(const Plan& pl, const Params& p, void* stream) {
-    hipStream_t s = (hipStream_t)stream;
     if (pl.nw != 4 && pl.nw != 8) return (int)hipErrorInvalidValue;
-    if (pl.in == IN_F16 && pl.out == OUT_F16) return launch_serial_io<IN_F16, OUT_F16>(pl, p, s);
-    if (pl.in == IN_F16 && pl.out == OUT_F32) return launch_serial_io<IN_F16, OUT_F32>(pl, p, s);
-    if (pl.in == IN_BF16 && pl.out == OUT_BF16) return launch_serial_io<IN_BF16, OUT_BF16>(pl, p, s);
-    if (pl.in == IN_BF16 && pl.out == OUT_F32) return launch_serial_io<IN_BF16, OUT_F32>(pl, p, s);
+    if (pl.in == IN_F16) {
+        if (p.mod == MOD_NONE) return launch_serial_in<IN_F16, MOD_NONE>(pl, p, stream);
+        if (p.mod == MOD_SOFTCAP) return launch_serial_in<IN_F16, MOD_SOFTCAP>(pl, p, stream);
+        if (p.mod == MOD_ALIBI) return launch_serial_in<IN_F16, MOD_ALIBI>(pl, p, stream);
+    }
+    if (pl.in == IN_BF16) {
+        if (p.mod == MOD_NONE) return launch_serial_in<IN_BF16, MOD_NONE>(pl, p, stream);
+        if (p.mod == MOD_SOFTCAP) return launch_serial_in<IN_BF16, MOD_SOFTCAP>(pl, p, stream);
+        if (p.mod == MOD_ALIBI) return launch_serial_in<IN_BF16, MOD_ALIBI>(pl, p, stream);
+    }
     return (int)hipErrorInvalidValue;
 }
 

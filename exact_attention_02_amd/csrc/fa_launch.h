@@ -28,8 +28,8 @@ inline SoftcapPoly softcap_poly(double kx) {
 }
 // KERNEL_KSPLIT: 16-bit inputs at D = 64 on small grids, 32 query rows per
 // workgroup whose waves split the keys (fa_fwd_ks.hip).
-// KERNEL_SERIAL: 16-bit inputs without a score modifier, one 32 x 32 block at
-// a time per wave, four waves per SIMD at D = 64 (fa_fwd_serial.hip).
+// KERNEL_SERIAL: 16-bit inputs, with or without a score modifier, one 32 x 32
+// block at a time per wave, four waves per SIMD at D = 64 (fa_serial.h).
 enum KernelKind { KERNEL_TILE64 = 0, KERNEL_PIPE16 = 1, KERNEL_KSPLIT = 2, KERNEL_SERIAL = 3 };
 
 // Everything a workgroup needs; passed by value as the kernel argument.
@@ -116,9 +116,31 @@ struct Plan {
 // when unset.
 int knob(int which);
 
+// Waves (32 query rows each) per workgroup of the serial kernel. At D = 128
+// eight waves (one workgroup per CU) halve the K/V staging per query row and
+// run at a higher clock: causal B1 H32 N32768 +4%, with a 4096-key window
+// +0.7%; they are used when the grid still gives every CU a workgroup. At
+// D = 64 four waves (four workgroups per CU) are faster on causal problems.
+#ifndef FA_SR_NW_D64
+#define FA_SR_NW_D64 4
+#endif
+#ifndef FA_SR_NW_D128
+#define FA_SR_NW_D128 8
+#endif
+// Keys per K/V tile of the serial kernel (64, or 128 with eight waves).
+#ifndef FA_SR_TK_D64
+#define FA_SR_TK_D64 64
+#endif
+#ifndef FA_SR_TK_D128
+#define FA_SR_TK_D128 64
+#endif
+// Keys per tile a serial-kernel plan takes for nw waves and tile size tk.
+constexpr int serial_tile_keys(int nw, int tk) { return (nw == 8 && tk == 128) ? 128 : 64; }
+
 // Picks the tile shape for a problem. Pure host arithmetic.
-// mod != MOD_NONE needs the pipelined kernel, the only one with score
-// modifiers; splitkv (split-KV) runs on the pipelined or the key-split kernel.
+// mod != MOD_NONE needs the serial or the pipelined kernel, the ones with
+// score modifiers; splitkv (split-KV) runs on the serial, the pipelined or the
+// key-split kernel.
 Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod = MOD_NONE, bool splitkv = false);
 
 // Enqueues the kernel chosen by `plan` on `stream`; returns the hipError_t
@@ -127,6 +149,11 @@ int launch(const Plan& plan, const Params& p, void* stream);
 int launch16(const Plan& plan, const Params& p, void* stream);
 int launch_ks(const Plan& plan, const Params& p, void* stream);
 int launch_serial(const Plan& plan, const Params& p, void* stream);
+// The serial kernel's launches for one input type and score modifier
+// (fa_serial.h); each set is instantiated in an object of its own
+// (fa_fwd_serial_inst.hip), launch_serial picks the set.
+template <int IN, int MOD>
+int launch_serial_in(const Plan& plan, const Params& p, void* stream);
 // The merge of the splits (p.n_split > 1): O and LSE from ws_o and ws_lse.
 int launch_combine(const Plan& plan, const Params& p, void* stream);
 

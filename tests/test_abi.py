@@ -260,7 +260,10 @@ def test_environment_variables_do_not_change_the_plan(monkeypatch):
 def test_plan_kernel_choices_and_errors():
     K = fa.plan_kernel
     assert K(4, 16, 8192, 8192, 128, fa.FA_E4M3) == 0                         # e4m3: 64-key-tile kernel
-    assert K(4, 12, 8192, 8192, 64, fa.FA_BF16, fa.FA_MOD_SOFTCAP) == 1       # score modifier: pipelined
+    assert K(4, 12, 8192, 8192, 64, fa.FA_BF16, fa.FA_MOD_SOFTCAP) == 3       # score modifiers: serial
+    assert K(4, 12, 8192, 8192, 64, fa.FA_BF16, fa.FA_MOD_ALIBI) == 3
+    assert K(1, 32, 32768, 32768, 128, fa.FA_BF16, fa.FA_MOD_ALIBI) == 3
+    assert K(1, 1, 128, 128, 64, fa.FA_F16_F32OUT, fa.FA_MOD_SOFTCAP) == 3   # ... also where plain goes key-split
     assert K(1, 1, 128, 128, 64, fa.FA_F16_F32OUT) == 2                      # one workgroup: key-split
     assert K(8, 32, 1, 16384, 64, fa.FA_BF16, splitkv=True) == 2             # decode: key-split splits
     assert K(1, 32, 32768, 32768, 128, fa.FA_BF16) == 3                      # long context: serial

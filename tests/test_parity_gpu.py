@@ -15,6 +15,7 @@ head); smaller shapes that span several tiles with ragged tails are compared
 in full too. The relative RMS of the e4m3 workload is taken over the whole
 tensor.
 """
+import dataclasses
 import json
 import math
 import os
@@ -35,7 +36,7 @@ LSE_BOUND = 1e-4
 OUT_T = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
-def run_gpu(w: synth.Workload, inp: synth.Inputs, q=None, k=None, v=None):
+def run_gpu(w: synth.Workload, inp: synth.Inputs, q=None, k=None, v=None, slopes=None):
     q = inp.q.to(DEV) if q is None else q
     k = inp.k.to(DEV) if k is None else k
     v = inp.v.to(DEV) if v is None else v
@@ -44,7 +45,8 @@ def run_gpu(w: synth.Workload, inp: synth.Inputs, q=None, k=None, v=None):
     if w.score_mod is not None:
         mod = dict(score_mod=w.score_mod, softcap=w.softcap)
         if w.score_mod == "alibi":
-            mod["alibi"] = torch.tensor(synth.alibi_slopes(w.H), dtype=torch.float32, device=DEV)
+            sl = synth.alibi_slopes(w.H) if slopes is None else slopes
+            mod["alibi"] = torch.tensor(sl, dtype=torch.float32, device=DEV)
     if w.splitkv:
         mod["num_splits"] = "auto"
     o, lse = fa.attention(q, k, v, scale=w.scale, causal=w.causal, window=w.window,
@@ -54,14 +56,14 @@ def run_gpu(w: synth.Workload, inp: synth.Inputs, q=None, k=None, v=None):
     return o, lse
 
 
-def reference(w, inp, rows=None):
+def reference(w, inp, rows=None, slopes=None):
     ext = {}
     if w.window_left is not None or w.window_right is not None:
         ext = dict(window_left=-1 if w.window_left is None else w.window_left,
                    window_right=-1 if w.window_right is None else w.window_right)
     if w.score_mod is not None:
-        ext.update(score_mod=w.score_mod, softcap=w.softcap,
-                   alibi_slopes=synth.alibi_slopes(w.H) if w.score_mod == "alibi" else None)
+        sl = synth.alibi_slopes(w.H) if slopes is None else slopes
+        ext.update(score_mod=w.score_mod, softcap=w.softcap, alibi_slopes=sl if w.score_mod == "alibi" else None)
     return oracle.attention(inp.q, inp.k, inp.v, w.scale, w.causal, w.window,
                             descales=(inp.descale_q, inp.descale_k, inp.descale_v), rows=rows, **ext)
 
@@ -337,8 +339,10 @@ def test_sliding_window_zero_queries_average_the_window():
 # ----------------------------------------------------- score modifiers
 
 # cap 20: scaled scores of N(0, 1) inputs reach about 4, so within one wave
-# some lanes' blocks stay inside the range of the kernels' polynomial for tanh
-# (|score / cap| <= 0.2) and others take the closed form
+# some lanes' blocks stay inside the range of the pipelined kernel's
+# polynomial for tanh (|score / cap| <= 0.2) and others take the closed form;
+# small caps bend the scores hard. The default plan runs these on the serial
+# kernel, test_score_mods_pipelined_kernel on the pipelined one.
 MOD_CASES = [("softcap", 50.0), ("softcap", 20.0), ("softcap", 2.0), ("softcap", 0.5), ("alibi", 0.0)]
 
 
@@ -366,8 +370,53 @@ def test_score_mods_small_shapes(B, H, Nq, Nk, mask, mod, cap, D, din, dout):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 3, 300, 300), (2, 2, 333, 200)])
+@pytest.mark.parametrize("mask", [(True, 0, None, None), (False, 0, 40, 40)])
+@pytest.mark.parametrize("mod,cap", MOD_CASES)
+@pytest.mark.parametrize("D", [64, 128])
+def test_score_mods_pipelined_kernel(knobs, B, H, Nq, Nk, mask, mod, cap, D):
+    knobs.set("FA_KERNEL", "1")
+    assert fa.plan_kernel(B, H, Nq, Nk, D, fa.FA_BF16, {"softcap": 1, "alibi": 2}[mod]) == 1
+    causal, window, wl, wr = mask
+    seed = 5100 + B * 7 + H * 13 + Nq * 3 + Nk + D + int(cap * 10) + (17 if causal else 0)
+    w = synth.small_workload(f"mod_pipe_{mod}{cap}_B{B}H{H}q{Nq}k{Nk}D{D}m{mask}", B, H, Nq, Nk, D, causal,
+                             window, "bf16", "bf16", seed, window_left=wl, window_right=wr, score_mod=mod,
+                             softcap=cap)
+    inp = synth.make_inputs(w)
+    if mod == "softcap" and cap <= 2.0:
+        inp = synth.Inputs((inp.q.double() * 3.0).to(inp.q.dtype), inp.k, inp.v)
+    elif mod == "softcap" and cap == 20.0:
+        inp = synth.Inputs((inp.q.double() * 2.0).to(inp.q.dtype), inp.k, inp.v)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+# ALiBi slopes of either sign, zero and large. The serial kernel starts the
+# score accumulator at the in-block part of the bias (slope / scale per key);
+# with scale 1e-30 that would not stay finite, and the bias is added to every
+# exponent argument instead (the scores then hardly matter). A negative slope
+# moves the preset reference to the first visible block.
+@pytest.mark.parametrize("scale", [0.125, 1e-30])
+@pytest.mark.parametrize("mask", [(True, 0, None, None), (False, 0, None, None), (False, 0, 100, 30)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kernel", ["3", "1"])
+def test_alibi_slopes_of_either_sign_and_size(knobs, scale, mask, D, kernel):
+    knobs.set("FA_KERNEL", kernel)
+    causal, window, wl, wr = mask
+    slopes = [0.5, -0.25, 0.0, 4.0]
+    w = synth.small_workload(f"alibi_slopes_s{scale}_D{D}_m{mask}_k{kernel}", 1, 4, 260, 300, D, causal, window,
+                             "bf16", "bf16", 5800 + D, window_left=wl, window_right=wr, score_mod="alibi")
+    w = dataclasses.replace(w, scale=float(torch.tensor(scale, dtype=torch.float32)))   # both sides get this fp32 value
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp, slopes=slopes)
+    Oref, Lref = reference(w, inp, slopes=slopes)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
 @pytest.mark.parametrize("mod,cap", [("softcap", 1.0), ("alibi", 0.0)])
 def test_score_mods_with_two_query_blocks_per_wave(knobs, mod, cap):
+    knobs.set("FA_KERNEL", "1")
     knobs.set("FA_TILE_QB", "2")
     w = synth.small_workload(f"mod_qb2_{mod}", 1, 3, 700, 700, 64, True, 0, "bf16", "bf16", 5500,
                              score_mod=mod, softcap=cap)
@@ -377,9 +426,10 @@ def test_score_mods_with_two_query_blocks_per_wave(knobs, mod, cap):
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
 
 
-def test_alibi_with_zero_slopes_is_bitwise_plain_attention(knobs):
-    # score modifiers run on the pipelined kernel: plain attention is taken on it too
-    knobs.set("FA_KERNEL", "1")
+@pytest.mark.parametrize("kernel", ["3", "1"])
+def test_alibi_with_zero_slopes_is_bitwise_plain_attention(knobs, kernel):
+    # both calls forced onto one kernel
+    knobs.set("FA_KERNEL", kernel)
     w = synth.small_workload("alibi0", 1, 2, 333, 333, 64, True, 0, "bf16", "bf16", 5600)
     inp = synth.make_inputs(w)
     q, k, v = inp.q.to(DEV), inp.k.to(DEV), inp.v.to(DEV)
