@@ -11,8 +11,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
 SOURCES = ["fa_fwd.hip", "fa_fwd16.hip", "fa_fwd_ks.hip", "fa_fwd_serial.hip", "fa_bwd.hip", "fa_api.hip"]
 # The serial forward kernel's instantiation sets: fa_fwd_serial_inst.hip once
-# per (input type, score modifier), as FA_SR_IN and FA_SR_MOD (fa_launch.h).
-SERIAL_SETS = [(i, m) for i in (0, 1) for m in (0, 1, 2)]
+# per (input type, score modifier), as FA_SR_IN and FA_SR_MOD (fa_launch.h);
+# e4m3 inputs (2) take no modifier.
+SERIAL_SETS = [(i, m) for i in (0, 1) for m in (0, 1, 2)] + [(2, 0)]
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32.
 HIPFLAGS = [

@@ -431,9 +431,9 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     pl.D = D;
     pl.bc = BC;
     const long long n_bh = (long long)B * H;
-    // 16-bit inputs use the pipelined kernel: 4 waves at D = 64, 8 waves at
-    // D = 128 (its three 32 KiB LDS slots then serve 256 query rows). e4m3
-    // inputs use the 64-key-tile kernel. FA_KNOB_KERNEL forces one (tuning).
+    // The serial kernel (below) takes most problems. Otherwise 16-bit inputs
+    // use the pipelined kernel (4 waves at D = 64, 8 at D = 128) and e4m3
+    // inputs the 64-key-tile kernel. FA_KNOB_KERNEL forces one (tuning).
     int kernel = (in == IN_E4M3) ? KERNEL_TILE64 : KERNEL_PIPE16;
     // 16-bit inputs at D = 64 go to the key-split kernel where the pipelined
     // kernel would leave waves idle: with at most 64 query rows per head (two
@@ -444,9 +444,10 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     // often and lose (measured: c2, 384 workgroups, 29.7 against 23.3 us;
     // B8 H32 Nq128, 256 workgroups, 95 against 78 us).
     const bool ks_ok = in != IN_E4M3 && D == 64 && mod == MOD_NONE;
-    // 16-bit inputs: the serial kernel (four waves per SIMD at D = 64), with
-    // or without a score modifier, except on the small grids above.
-    const bool sr_ok = in != IN_E4M3;
+    // The serial kernel (four waves per SIMD at D = 64): 16-bit inputs with
+    // or without a score modifier, except on the small grids above, and e4m3
+    // inputs without one (not split).
+    const bool sr_ok = in != IN_E4M3 || (mod == MOD_NONE && !splitkv);
     if (sr_ok) kernel = KERNEL_SERIAL;
     if (ks_ok && (Nq <= 64 || n_bh * ((Nq + 127) / 128) <= FA_KS_MAX_WG)) kernel = KERNEL_KSPLIT;
     {

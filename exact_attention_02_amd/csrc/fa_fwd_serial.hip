@@ -14,6 +14,7 @@ int launch_serial(const Plan& pl, const Params& p, void* stream) {
         if (p.mod == MOD_SOFTCAP) return launch_serial_in<IN_F16, MOD_SOFTCAP>(pl, p, stream);
         if (p.mod == MOD_ALIBI) return launch_serial_in<IN_F16, MOD_ALIBI>(pl, p, stream);
     }
+    if (pl.in == IN_E4M3 && p.mod == MOD_NONE) return launch_serial_in<IN_E4M3, MOD_NONE>(pl, p, stream);
     if (pl.in == IN_BF16) {
         if (p.mod == MOD_NONE) return launch_serial_in<IN_BF16, MOD_NONE>(pl, p, stream);
         if (p.mod == MOD_SOFTCAP) return launch_serial_in<IN_BF16, MOD_SOFTCAP>(pl, p, stream);

@@ -70,6 +70,13 @@ namespace serial {
 // Largest sum of a lane half's 16 weights of one block kept without moving
 // the reference: every weight then stays at most 2^10, within fp16's range.
 constexpr float SUM_LIMIT = 1024.f;
+// e4m3 inputs: the weights are formed as p * 2^LOG2_PRESCALE8 (the scale
+// enters the exponent) and stored as e4m3; a lane half's sum of at most
+// SUM_LIMIT8 (scaled) keeps every scaled weight at most 256, below the
+// format's largest value 448, while weights down to 2^-8 of the reference
+// stay in its normal range.
+constexpr float LOG2_PRESCALE8 = 2.f;
+constexpr float SUM_LIMIT8 = 256.f;
 // Keys at the start of a workgroup's range whose blocks always take the
 // residual pass (the running sums are small there, so most rows need it).
 #ifndef FA_SR_EARLY_KEYS
@@ -107,19 +114,30 @@ __device__ __forceinline__ void serial_wg(const Params& p, int* bh, int* qt, int
 template <int IN, int OUT, int D, int NW, int TK, int MOD, bool FOLD>
 __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int bh, int qt, int split) {
     using namespace serial;
+    // e4m3 inputs: Q and K are widened to bf16 (exactly) for the score MFMA,
+    // V stays e4m3 and P.V runs on the 8-bit MFMA, 64 keys per step.
+    constexpr bool FP8 = IN == IN_E4M3;
+    constexpr int QK = FP8 ? IN_BF16 : IN;     // score MFMA operand type
+    constexpr int EB = FP8 ? 1 : 2;            // bytes per stored element
     constexpr int NT = 64 * NW;
-    constexpr int RB = D * 2;              // bytes per K/V/Q row, in HBM and in LDS
-    constexpr int CPR = RB / 16;           // 16-byte chunks per row
+    constexpr int GRB = D * EB;            // bytes per Q/K/V row in HBM
+    constexpr int RB = D * 2;              // bytes per K row in LDS (16-bit)
+    constexpr int VRB = D * EB;            // bytes per V row in LDS
+    constexpr int CPR = RB / 16;           // 16-byte chunks per LDS K row
+    constexpr int VCPR = VRB / 16;         // 16-byte chunks per LDS V row
     static_assert(RB == 128 || RB == 256, "row size");
     static_assert(TK == 64 || TK == 128, "keys per tile");
+    static_assert(!FP8 || (TK == 64 && MOD == MOD_NONE), "e4m3: 64-key tiles, no score modifier");
     constexpr int SUB = TK / 32;           // 32-key blocks per tile
-    constexpr int TILE = TK * RB;          // bytes of one K or V tile
-    constexpr int SLOT = 2 * TILE;         // K tile, then V tile
+    constexpr int KTILE = TK * RB;         // bytes of one K tile in LDS
+    constexpr int VTILE = TK * VRB;        // bytes of one V tile in LDS
+    constexpr int SLOT = KTILE + VTILE;    // K tile, then V tile
     constexpr int NKS = D / 16;            // score MFMA steps over D
     constexpr int ND = D / 32;             // 32-row blocks of O^T
     constexpr int BR = 32 * NW;            // query rows per workgroup
-    constexpr int NDMA = TILE / 16 / NT;   // 16-byte copies per thread per tensor per tile
-    static_assert(NDMA >= 1 && TILE % (16 * NT) == 0, "tile staging");
+    constexpr int NDMA = VTILE / 16 / NT;  // 16-byte copies per thread per tensor per tile
+    static_assert(NDMA >= 1 && VTILE % (16 * NT) == 0, "tile staging");
+    constexpr int NK8 = TK * GRB / 16 / NT;   // e4m3: 16-byte K chunks each thread widens per tile
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,19 +167,28 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
     const int w0 = r0 + rblk * 32;
     const int w1 = min(w0 + 32, Nq);
 
-    const uint8_t* qp = p.q + (size_t)bh * Nq * RB;
-    const uint8_t* kp = p.k + (size_t)bh * Nk * RB;
-    const uint8_t* vp = p.v + (size_t)bh * Nk * RB;
+    const uint8_t* qp = p.q + (size_t)bh * Nq * GRB;
+    const uint8_t* kp = p.k + (size_t)bh * Nk * GRB;
+    const uint8_t* vp = p.v + (size_t)bh * Nk * GRB;
 
     // Q fragments, B operand of S^T = K Q^T: lane holds query w0 + l32,
-    // head-dim elements [16s + 8hh, +8). Rows at or past Nq read as zeros.
+    // head-dim elements [16s + 8hh, +8) (e4m3: widened to bf16). Rows at or
+    // past Nq read as zeros.
     i32x4 qf[NKS];
     {
-        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)(Nq * RB));
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qp, (unsigned)(Nq * GRB));
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
-            qf[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                qrs, (w0 + l32) * RB + (16 * s + 8 * hh) * 2, 0, 0));
+        for (int s = 0; s < NKS; ++s) {
+            if constexpr (!FP8) {
+                qf[s] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    qrs, (w0 + l32) * GRB + (16 * s + 8 * hh) * 2, 0, 0));
+            } else {
+                const i32x2 w8 = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                    qrs, (w0 + l32) * GRB + 16 * s + 8 * hh, 0, 0));
+                const i32x2 a = e4m3x4_to_bf16(w8[0]), b = e4m3x4_to_bf16(w8[1]);
+                qf[s] = i32x4{a[0], a[1], b[0], b[1]};
+            }
+        }
     }
 
     f32x16 oacc[ND];
@@ -198,24 +225,75 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
 
     // ---- K/V copies: lane l of a wave fills the l-th 16-byte slot of a 1 KiB
     // run of the tile, fetching the global chunk that belongs there under the
-    // swizzled layout; rows at or past Nk read as zeros.
-    const i32x4 kwords = rsrc_words(kp, (unsigned)(Nk * RB));
-    const i32x4 vwords = rsrc_words(vp, (unsigned)(Nk * RB));
+    // swizzled layout; rows at or past Nk read as zeros. e4m3: V's rows are
+    // stored permuted (v8_row), so that each lane half's 32 keys are 32
+    // consecutive LDS rows for the 8-bit transposing reads, and K passes
+    // through registers (stk), to be widened to bf16 on its way into LDS
+    // after the tile's blocks (finish_tile).
+    const i32x4 kwords = rsrc_words(kp, (unsigned)(Nk * GRB));
+    const i32x4 vwords = rsrc_words(vp, (unsigned)(Nk * GRB));
     const unsigned smem_base = (unsigned)(unsigned long long)(lds_u8*)smem;
-    static_assert((NT / CPR) % 16 == 0, "copy rows");
+    static_assert((NT / CPR) % 16 == 0 && (NT / VCPR) % 8 == 0, "copy rows");
     const unsigned dma_voff = [&] {
         const int slot = 64 * wave + lane;
         const int x = slot / CPR, c = (slot % CPR) ^ swz16<RB>(x);
         return (unsigned)(x * RB + c * 16);
     }();
+    // e4m3 V: copy i of a lane fills LDS row xv = slot / VCPR + i * NT / VCPR
+    // with key v8_row_inv(xv); the keys of copy i > 0 are those of copy 0
+    // moved by a multiple of 4 (xv moves by a multiple of 32), so one
+    // per-lane offset serves every copy.
+    const unsigned dma_voff8 = [&] {
+        const int slot = 64 * wave + lane;
+        constexpr int VSW = VCPR < 8 ? VCPR : 8;   // the swizzle of lds_off<VRB>
+        const int xv = slot / VCPR, c = (slot % VCPR) ^ (xv & (VSW - 1));
+        return (unsigned)(v8_row_inv(xv) * VRB + c * 16);
+    }();
+    [[maybe_unused]] i32x4 stk[FP8 ? NK8 : 1];
+    const __amdgpu_buffer_rsrc_t krs8 = make_rsrc(kp, (unsigned)(Nk * GRB));
     auto issue_tile = [&](int t) {
         const unsigned kb = smem_base + (unsigned)((t & 1) * SLOT);
+        if constexpr (!FP8) {
 #pragma unroll
-        for (int i = 0; i < NDMA; ++i) {
-            const int run = 64 * wave + NT * i;
-            const unsigned soff = (unsigned)((t * TK + i * (NT / CPR)) * RB);
-            dma16(kwords, kb + run * 16, dma_voff, soff);
-            dma16(vwords, kb + TILE + run * 16, dma_voff, soff);
+            for (int i = 0; i < NDMA; ++i) {
+                const int run = 64 * wave + NT * i;
+                const unsigned soff = (unsigned)((t * TK + i * (NT / CPR)) * RB);
+                dma16(kwords, kb + run * 16, dma_voff, soff);
+                dma16(vwords, kb + KTILE + run * 16, dma_voff, soff);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NK8; ++i) {
+                const int ci = tid + NT * i;
+                const int x = ci / (GRB / 16), c = ci % (GRB / 16);
+                stk[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    krs8, (t * TK + x) * GRB + c * 16, 0, 0));
+            }
+#pragma unroll
+            for (int i = 0; i < NDMA; ++i) {
+                const int run = 64 * wave + NT * i;
+                const int xv0 = i * (NT / VCPR);   // multiple of 32: keys move by xv0 / 8
+                const unsigned soff = (unsigned)((t * TK + (xv0 >> 3)) * VRB);
+                dma16(vwords, kb + KTILE + run * 16, dma_voff8, soff);
+            }
+        }
+    };
+    // e4m3: the K chunks of tile t have landed in registers (with the V
+    // copies issued beside them); widen them and write them to the tile's
+    // slot. Every wave is past tile t-2, the slot's previous tile.
+    auto finish_tile = [&](int t) __attribute__((always_inline)) {
+        if constexpr (FP8) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            uint8_t* kb = smem + (t & 1) * SLOT;
+#pragma unroll
+            for (int i = 0; i < NK8; ++i) {
+                const int ci = tid + NT * i;
+                const int x = ci / (GRB / 16), c = ci % (GRB / 16);
+                const i32x2 a = e4m3x4_to_bf16(stk[i][0]), b = e4m3x4_to_bf16(stk[i][1]);
+                const i32x2 e = e4m3x4_to_bf16(stk[i][2]), f = e4m3x4_to_bf16(stk[i][3]);
+                *reinterpret_cast<i32x4*>(kb + lds_pos<RB>(x, 2 * c)) = i32x4{a[0], a[1], b[0], b[1]};
+                *reinterpret_cast<i32x4*>(kb + lds_pos<RB>(x, 2 * c + 1)) = i32x4{e[0], e[1], f[0], f[1]};
+            }
         }
     };
 
@@ -246,11 +324,20 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
 #pragma unroll
     for (int s = 0; s < NKS; ++s) kofs[s] = lds_pos<RB>(l32, 2 * s + hh);
     int vofs[ND][2];   // transposing V reads: rows 4hh + cl/4 and 8 rows further
+    if constexpr (!FP8) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-        const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
+        for (int db = 0; db < ND; ++db) {
+            const int ch = (2 * (32 * db + 16 * (g & 1)) + 8 * (cl & 3)) >> 4;
 #pragma unroll
-        for (int h8 = 0; h8 < 2; ++h8) vofs[db][h8] = lds_pos<RB>(4 * hh + (cl >> 2) + 8 * h8, ch) + 8 * (cl & 1);
+            for (int h8 = 0; h8 < 2; ++h8) vofs[db][h8] = lds_pos<RB>(4 * hh + (cl >> 2) + 8 * h8, ch) + 8 * (cl & 1);
+        }
+    } else {
+        // e4m3: the 8-bit transposing reads of LDS rows 32hh + 8u + cl/2
+        // (u = 0..3, an immediate offset), head-dim columns 32db + 16(g%2)
+        // + 8(cl%2) .. +8; the swizzle depends on the row mod 8 only
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+            vofs[db][0] = lds_off<VRB>(32 * hh + (cl >> 1), (32 * db + 16 * (g & 1)) >> 4) + 8 * (cl & 1);
     }
     const lds_u8* lds0 = (const lds_u8*)smem;
 
@@ -267,14 +354,14 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
             S = f32x16{};
         }
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) S = mfma16(IN, a[s], qf[s], S);
+        for (int s = 0; s < NKS; ++s) S = mfma16(QK, a[s], qf[s], S);
     };
     // V^T operands of sub-tile jj for its two 16-key MFMA steps, in the key
     // order P has: step sp, lane half hh, k-slot e holds key
     // 32j + 16sp + 8(e/4) + 4hh + e%4 (two transposing reads of 4 rows).
     auto v_operands = [&](auto par, int jj, i32x4(&va)[2][ND]) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par)::value;
-        const lds_u8* vb = lds0 + PAR * SLOT + TILE + 32 * jj * RB;
+        const lds_u8* vb = lds0 + PAR * SLOT + KTILE + 32 * jj * RB;
 #pragma unroll
         for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -289,6 +376,26 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
         for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
             for (int db = 0; db < ND; ++db) oacc[db] = mfma16(IN, va[sp][db], P[sp], oacc[db]);
+    };
+    // e4m3: O^T += V^T P^T over the 64 keys of the tile in slot PAR; word w
+    // of pf holds the e4m3 weights of sub-tile w/4, accumulator elements
+    // 4(w%4) .. +3, and the V^T operand comes from four 8-bit transposing
+    // reads of the lane half's 32 (permuted) rows.
+    auto pv8 = [&](auto par, const i32x8& pf) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par)::value;
+        const lds_u8* vb = lds0 + PAR * SLOT + KTILE;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            i32x8 a;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2*)(vb + vofs[db][0] + 8 * u * VRB));
+                a[2 * u] = r[0];
+                a[2 * u + 1] = r[1];
+            }
+            oacc[db] = mfma_fp8(a, pf, oacc[db]);
+        }
     };
 
     // Masked scores of sub-tile j become -inf: row i = w0 + l32 sees keys
@@ -388,7 +495,7 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
         __attribute__((always_inline)) {
         {
             float a[16];
-            eargs(S, j, ms, edge, a);
+            eargs(S, j, FP8 ? ms - LOG2_PRESCALE8 : ms, edge, a);
 #pragma unroll
             for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(a[r]);
         }
@@ -396,11 +503,22 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
 #pragma unroll
         for (int r = 0; r < 8; ++r) s8[r] = pr[2 * r] + pr[2 * r + 1];
         ts = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+        if constexpr (!FP8) {
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            const int o = 8 * sp;
-            P[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
-                          pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
+            for (int sp = 0; sp < 2; ++sp) {
+                const int o = 8 * sp;
+                P[sp] = i32x4{pack2<IN>(pr[o + 0], pr[o + 1]), pack2<IN>(pr[o + 2], pr[o + 3]),
+                              pack2<IN>(pr[o + 4], pr[o + 5]), pack2<IN>(pr[o + 6], pr[o + 7])};
+            }
+        } else {
+            // e4m3 of the (scaled) weights, four per word, in P[0]
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                int word = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4 * w], pr[4 * w + 1], 0, false);
+                word = __builtin_amdgcn_cvt_pk_fp8_f32(pr[4 * w + 2], pr[4 * w + 3], word, true);
+                P[0][w] = word;
+            }
+            P[1] = i32x4{};
         }
     };
     // The rounding residual of the weights, lo = p - P rounded to the MFMA
@@ -446,6 +564,9 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
     // MODE 0: steady (fully visible, no checks but the one compare);
     // MODE 1: checked (skip / edge classes); MODE 2: checked and early (the
     // residual pass on every lane).
+    // e4m3: the tile's weights (pv8's pf) and whether a block of the tile ran
+    [[maybe_unused]] i32x8 pf8 = {};
+    [[maybe_unused]] bool live8 = false;
     auto block = [&](auto par, auto mode, int jj, int j) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode)::value;
         bool edge = false;
@@ -457,6 +578,34 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
         scores(par, jj, S);
         if constexpr (MODE != 0) {
             if (edge) mask(j, S);
+        }
+        if constexpr (FP8) {
+            // no residual pass; the reference moves when a lane half's sum
+            // exceeds SUM_LIMIT8. Sub-tile 0's weights wait for P.V at the end
+            // of the tile: before sub-tile 1 moves the reference (and rescales
+            // O), they are multiplied in against the reference they were formed
+            // with.
+            live8 = true;
+            float pr[16], ts;
+            i32x4 P[2];
+            softmax(S, j, m, edge, pr, ts, P);
+            const bool trig = !(ts <= SUM_LIMIT8);
+            if (__builtin_amdgcn_ballot_w64(trig) != 0) {
+                f32x16 S2;
+                scores(par, jj, S2);
+                if constexpr (MODE != 0) {
+                    if (edge) mask(j, S2);
+                }
+                if (jj == 1) {
+                    pv8(par, i32x8{pf8[0], pf8[1], pf8[2], pf8[3], 0, 0, 0, 0});
+                    pf8[0] = pf8[1] = pf8[2] = pf8[3] = 0;
+                }
+                redo(S2, j, edge, trig, pr, ts, P);
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) pf8[4 * jj + w] = P[0][w];
+            lh += ts;
+            return;
         }
         i32x4 va[2][ND];
         v_operands(par, jj, va);
@@ -500,8 +649,16 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
         if (t + 1 < t_hi) issue_tile(t + 1);
+        if constexpr (FP8) {
+            pf8 = i32x8{};
+            live8 = false;
+        }
 #pragma unroll
         for (int jj = 0; jj < SUB; ++jj) block(par, mode, jj, SUB * t + jj);
+        if constexpr (FP8) {
+            if (live8) pv8(par, pf8);
+            if (t + 1 < t_hi) finish_tile(t + 1);
+        }
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
@@ -537,17 +694,21 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
                     krs, (32 * jl + l32) * RB + (16 * s + 8 * hh) * 2, 0, 0));
             f32x16 S = sinit;
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) S = mfma16(IN, a[s], qf[s], S);
+            for (int s = 0; s < NKS; ++s) S = mfma16(QK, a[s], qf[s], S);
             mask(jl, S);
             m = row_max(S, jl, true);
         }
     }
 
-    const int tE = min(t_hi, t_lo + (EARLY_KEYS + TK - 1) / TK);
+    // e4m3 takes no residual pass: no early tiles
+    const int tE = FP8 ? t_lo : min(t_hi, t_lo + (EARLY_KEYS + TK - 1) / TK);
     const int tS0 = min(t_hi, max(tE, (f0 + SUB - 1) / SUB));
     const int tS1 = max(tS0, min(t_hi, f1 / SUB));
-    if (t_lo < t_hi) issue_tile(t_lo);
-    run(std::integral_constant<int, 2>{}, t_lo, tE);
+    if (t_lo < t_hi) {
+        issue_tile(t_lo);
+        finish_tile(t_lo);
+    }
+    if constexpr (!FP8) run(std::integral_constant<int, 2>{}, t_lo, tE);
     if constexpr (MOD == MOD_ALIBI && !FOLD) {
         // the ALiBi form without the fold (rare): every tile checked, which
         // keeps this kernel's code small
@@ -578,7 +739,7 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
                     Out<OUT_F32>::store4(orow + d * 4, a[4 * r4] * inv, a[4 * r4 + 1] * inv, a[4 * r4 + 2] * inv,
                                          a[4 * r4 + 3] * inv);
                 }
-            if (hh == 0) wlp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
+            if (hh == 0) wlp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt) - (FP8 ? LOG2_PRESCALE8 : 0.f)) * LN2 : -INFINITY;
         }
         clock_stamp(p.clk, p.clk_n, 1);
         return;
@@ -597,7 +758,7 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
                 Out<OUT>::store4(orow + d * Out<OUT>::EB, a[4 * r4] * inv, a[4 * r4 + 1] * inv, a[4 * r4 + 2] * inv,
                                  a[4 * r4 + 3] * inv);
             }
-        if (hh == 0) lp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt)) * LN2 : -INFINITY;
+        if (hh == 0) lp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt) - (FP8 ? LOG2_PRESCALE8 : 0.f)) * LN2 : -INFINITY;
     }
     clock_stamp(p.clk, p.clk_n, 1);
 }
@@ -615,7 +776,8 @@ __device__ __forceinline__ bool alibi_fold(const Params& p, int bh) {
 // ran measurably slower).
 template <int IN, int OUT, int D, int NW, int TK, int MOD, bool FOLD>
 __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_serial_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * TK * D * 2];   // two slots of a K and a V tile
+    // two slots of a K tile (16-bit in LDS) and a V tile (the input type)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (TK * D * 2 + TK * D * (IN == IN_E4M3 ? 1 : 2))];
     int bh, qt, split;
     serial_wg(p, &bh, &qt, &split);
     if constexpr (MOD == MOD_ALIBI) {
@@ -656,15 +818,17 @@ static int launch_serial_d(const Plan& pl, const Params& p, hipStream_t s) {
 template <int IN, int MOD>
 int launch_serial_in(const Plan& pl, const Params& p, void* stream) {
     hipStream_t s = (hipStream_t)stream;
+    // 16-bit inputs write their own type or fp32, e4m3 inputs bf16
     constexpr int OUT16 = IN == IN_F16 ? OUT_F16 : OUT_BF16;
-    if (pl.out != OUT16 && pl.out != OUT_F32) return (int)hipErrorInvalidValue;
+    constexpr bool F32 = IN != IN_E4M3;
+    if (pl.out != OUT16 && !(F32 && pl.out == OUT_F32)) return (int)hipErrorInvalidValue;
     if (pl.D == 64) {
         if (pl.out == OUT16) return launch_serial_d<IN, OUT16, 64, MOD>(pl, p, s);
-        return launch_serial_d<IN, OUT_F32, 64, MOD>(pl, p, s);
+        if constexpr (F32) return launch_serial_d<IN, OUT_F32, 64, MOD>(pl, p, s);
     }
     if (pl.D == 128) {
         if (pl.out == OUT16) return launch_serial_d<IN, OUT16, 128, MOD>(pl, p, s);
-        return launch_serial_d<IN, OUT_F32, 128, MOD>(pl, p, s);
+        if constexpr (F32) return launch_serial_d<IN, OUT_F32, 128, MOD>(pl, p, s);
     }
     return (int)hipErrorInvalidValue;
 }

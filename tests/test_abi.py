@@ -259,7 +259,8 @@ def test_environment_variables_do_not_change_the_plan(monkeypatch):
 
 def test_plan_kernel_choices_and_errors():
     K = fa.plan_kernel
-    assert K(4, 16, 8192, 8192, 128, fa.FA_E4M3) == 0                         # e4m3: 64-key-tile kernel
+    assert K(4, 16, 8192, 8192, 128, fa.FA_E4M3) == 3                         # e4m3: serial kernel
+    assert K(1, 1, 64, 1000, 64, fa.FA_E4M3) == 3
     assert K(4, 12, 8192, 8192, 64, fa.FA_BF16, fa.FA_MOD_SOFTCAP) == 3       # score modifiers: serial
     assert K(4, 12, 8192, 8192, 64, fa.FA_BF16, fa.FA_MOD_ALIBI) == 3
     assert K(1, 32, 32768, 32768, 128, fa.FA_BF16, fa.FA_MOD_ALIBI) == 3

@@ -216,14 +216,60 @@ def test_small_shapes(B, H, Nq, Nk, causal, window, D, din, dout):
 @pytest.mark.parametrize("causal,window", MODES)
 @pytest.mark.parametrize("din,dout", DTYPES)
 def test_two_query_blocks_per_wave(knobs, B, H, Nq, Nk, causal, window, din, dout):
-    # The tile shape with 64 query rows per wave (used for large D = 64
-    # problems) on shapes small enough to compare in full.
+    # The tile shape with 64 query rows per wave of the pipelined kernel
+    # (16-bit inputs) and of the 64-key-tile kernel (e4m3), on shapes small
+    # enough to compare in full.
+    knobs.set("FA_KERNEL", "0" if din == "e4m3" else "1")
     knobs.set("FA_TILE_QB", "2")
     seed = 2000 + B * 7 + H * 13 + Nq * 3 + Nk + (17 if causal else 0) + window
     w = synth.small_workload(f"qb2_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, 64,
                              causal, window, din, dout, seed,
                              outlier_frac=0.001 if din == "e4m3" else 0.0, outlier_mult=20.0)
     inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", [(2, 3, 300, 300), (1, 2, 200, 333), (1, 2, 333, 200), (1, 1, 64, 1000),
+                                       (1, 4, 129, 65)])
+@pytest.mark.parametrize("causal,window", MODES)
+@pytest.mark.parametrize("D", [64, 128])
+def test_tile64_kernel_on_e4m3_inputs(knobs, B, H, Nq, Nk, causal, window, D):
+    # e4m3 inputs run the serial kernel by default; the 64-key-tile kernel
+    # stays selectable for them and must agree too.
+    knobs.set("FA_KERNEL", "0")
+    assert fa.plan_kernel(B, H, Nq, Nk, D, fa.FA_E4M3) == 0
+    seed = 2500 + B * 7 + H * 13 + Nq * 3 + Nk + D + (17 if causal else 0) + window
+    w = synth.small_workload(f"t64_e4m3_B{B}H{H}q{Nq}k{Nk}D{D}c{int(causal)}w{window}", B, H, Nq, Nk, D, causal,
+                             window, "e4m3", "bf16", seed, outlier_frac=0.001, outlier_mult=20.0)
+    inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+# e4m3 on the serial kernel: the reference moves when a lane half's weights
+# sum past 16, and P.V waits for both 32-key sub-tiles of a 64-key tile, so a
+# move in sub-tile 1 first multiplies sub-tile 0's weights in against the old
+# reference. Keys whose norm grows along the sequence raise the row max on
+# most sub-tiles (both halves of every tile), and large outliers add jumps.
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 2, 200, 640), (2, 1, 333, 517)])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 150)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("ramp", [0.0, 4.0])
+def test_e4m3_serial_reference_moves_within_a_tile(B, H, Nq, Nk, causal, window, D, ramp):
+    assert fa.plan_kernel(B, H, Nq, Nk, D, fa.FA_E4M3) == 3
+    seed = 2700 + B * 7 + H * 13 + Nq * 3 + Nk + D + (17 if causal else 0) + window + int(ramp)
+    w = synth.small_workload(f"e4m3_moves_B{B}H{H}q{Nq}k{Nk}D{D}c{int(causal)}w{window}r{ramp}", B, H, Nq, Nk, D,
+                             causal, window, "e4m3", "bf16", seed, outlier_frac=0.002, outlier_mult=12.0)
+    inp = synth.make_inputs(w)
+    if ramp > 0.0:
+        # key j scaled by 1 + ramp * j / Nk (codes re-rounded, clamped to the format's range)
+        kf = inp.k.to(torch.float32)
+        g = 1.0 + ramp * torch.arange(Nk, dtype=torch.float32).view(1, 1, Nk, 1) / Nk
+        k8 = (kf * g).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        inp = synth.Inputs(inp.q, k8, inp.v, inp.descale_q, inp.descale_k, inp.descale_v)
     o, lse = run_gpu(w, inp)
     Oref, Lref = reference(w, inp)
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
