@@ -589,18 +589,15 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
             float pr[16], ts;
             i32x4 P[2];
             softmax(S, j, m, edge, pr, ts, P);
+            // (the register budget of two waves per SIMD keeps the scores, so
+            // the redo does not form them again)
             const bool trig = !(ts <= SUM_LIMIT8);
             if (__builtin_amdgcn_ballot_w64(trig) != 0) {
-                f32x16 S2;
-                scores(par, jj, S2);
-                if constexpr (MODE != 0) {
-                    if (edge) mask(j, S2);
-                }
                 if (jj == 1) {
                     pv8(par, i32x8{pf8[0], pf8[1], pf8[2], pf8[3], 0, 0, 0, 0});
                     pf8[0] = pf8[1] = pf8[2] = pf8[3] = 0;
                 }
-                redo(S2, j, edge, trig, pr, ts, P);
+                redo(S, j, edge, trig, pr, ts, P);
             }
 #pragma unroll
             for (int w = 0; w < 4; ++w) pf8[4 * jj + w] = P[0][w];
@@ -770,21 +767,32 @@ __device__ __forceinline__ bool alibi_fold(const Params& p, int bh) {
     return fabsf(p.slopes[bh % p.H] * LOG2E) <= p.c * 0x1p64f;
 }
 
-// With ALiBi the kernel is launched twice on the stream, FOLD true and false;
-// each launch's workgroups take the heads of their kind and leave the others
-// at once, so each kernel holds one form of the loop (a kernel holding both
-// ran measurably slower).
+// With ALiBi the kernel is launched twice on the stream, FOLD true and false,
+// so that each kernel holds one form of the loop (a kernel holding both ran
+// measurably slower). The FOLD launch has the usual grid and its workgroups
+// leave heads without the fold at once; the other launch has one workgroup
+// per head, which leaves at once where the head folds (the usual case) and
+// otherwise walks the head's query tiles one after another.
 template <int IN, int OUT, int D, int NW, int TK, int MOD, bool FOLD>
 __global__ __launch_bounds__(64 * NW, serial::waves_per_simd<D>()) void fa_fwd_serial_kernel(Params p) {
     // two slots of a K tile (16-bit in LDS) and a V tile (the input type)
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (TK * D * 2 + TK * D * (IN == IN_E4M3 ? 1 : 2))];
-    int bh, qt, split;
-    serial_wg(p, &bh, &qt, &split);
-    if constexpr (MOD == MOD_ALIBI) {
-        if (alibi_fold(p, bh) != FOLD) return;
+    if constexpr (MOD == MOD_ALIBI && !FOLD) {
+        const int bh = blockIdx.x;
+        if (alibi_fold(p, bh)) return;
+        for (int qt = 0; qt < p.n_qt; ++qt) {
+            serial_body<IN, OUT, D, NW, TK, MOD, FOLD>(p, smem, bh, qt, 0);
+            __syncthreads();   // every wave is done with the LDS slots before the next tile's copies
+        }
+    } else {
+        int bh, qt, split;
+        serial_wg(p, &bh, &qt, &split);
+        if constexpr (MOD == MOD_ALIBI) {
+            if (!alibi_fold(p, bh)) return;
+        }
+        clock_stamp(p.clk, p.clk_n, 0);
+        serial_body<IN, OUT, D, NW, TK, MOD, FOLD>(p, smem, bh, qt, split);
     }
-    clock_stamp(p.clk, p.clk_n, 0);
-    serial_body<IN, OUT, D, NW, TK, MOD, FOLD>(p, smem, bh, qt, split);
 }
 
 // ---------------------------------------------------------------- host side
@@ -793,9 +801,14 @@ template <int IN, int OUT, int D, int NW, int TK, int MOD>
 static int launch_serial_one(const Plan& pl, const Params& p, hipStream_t s) {
     const dim3 grid((unsigned)(pl.n_wg * p.n_split)), block(64 * NW);
     if constexpr (MOD == MOD_ALIBI) {
+        // ALiBi takes no split (the split-KV entry points have no modifier)
+        if (p.n_split != 1) return (int)hipErrorInvalidValue;
         hipLaunchKernelGGL((fa_fwd_serial_kernel<IN, OUT, D, NW, TK, MOD, true>), grid, block, 0, s, p);
         const int e = (int)hipGetLastError();
         if (e != 0) return e;
+        hipLaunchKernelGGL((fa_fwd_serial_kernel<IN, OUT, D, NW, TK, MOD, false>), dim3((unsigned)p.n_bh), block, 0,
+                           s, p);
+        return (int)hipGetLastError();
     }
     hipLaunchKernelGGL((fa_fwd_serial_kernel<IN, OUT, D, NW, TK, MOD, false>), grid, block, 0, s, p);
     return (int)hipGetLastError();
