@@ -300,10 +300,13 @@ int fa_plan_block_class_window(int w0, int w1, int c0, int c1, int Nq, int Nk,
 
 /*
  * fa_plan_kernel: which forward kernel a call would launch (host only):
- *   0  the 64-key-tile kernel     (e4m3 inputs)
- *   1  the pipelined kernel       (16-bit inputs with a score modifier)
- *   2  the key-split kernel       (16-bit inputs at D = 64 on small grids)
- *   3  the serial kernel          (other 16-bit inputs)
+ *   0  the 64-key-tile kernel     (e4m3 inputs split by fa_fwd_splitkv,
+ *                                  which rejects them; else only when forced)
+ *   1  the pipelined kernel       (only when forced)
+ *   2  the key-split kernel       (16-bit inputs at D = 64 with no score
+ *                                  modifier on small grids)
+ *   3  the serial kernel          (every other call: 16-bit inputs with or
+ *                                  without a score modifier, e4m3 inputs)
  * score_mod != 0 plans fa_fwd_mod, splitkv != 0 fa_fwd_splitkv (which also
  * launches the merge kernel when its split count exceeds 1), else fa_fwd and
  * fa_fwd_window. Returns the kind, or minus an argument error code.
@@ -318,8 +321,10 @@ int fa_plan_kernel(int B, int H, int Nq, int Nk, int D, int dtype, int score_mod
  * the parity bounds under every setting; the tests use these to run each
  * kernel and tile shape on every case.
  *   FA_KNOB_KERNEL    force a kernel kind of fa_plan_kernel where it applies
- *                     (1 needs 16-bit inputs; 2 16-bit inputs at D = 64 with
- *                     no score modifier; 3 16-bit inputs with none)
+ *                     (0 any input without a score modifier; 1 16-bit
+ *                     inputs; 2 16-bit inputs at D = 64 with no score
+ *                     modifier; 3 any input, e4m3 without a modifier or a
+ *                     split)
  *   FA_KNOB_TILE_QB   query blocks of 32 rows per wave (1 or 2; D = 64) for
  *                     the 64-key-tile and pipelined kernels
  *   FA_KNOB_WG_GROUP  heads per group in phase 1 of the workgroup order
