@@ -34,7 +34,9 @@
 // lane half's sum so far (the first blocks of a row, peaked rows), P's
 // rounding residual (p - P, rounded) also multiplies V, so that a dominant
 // weight's rounding does not reach O. Both checks are one compare against
-// thr = min(lh / 3, SUM_LIMIT), and both corrections live off the common path.
+// thr = min(lh / 3, SUM_LIMIT), and both corrections live off the common path;
+// the lane half's sum is kept in thirds (one FMA per block), so thr is one
+// min.
 //
 // Score modifiers (the score_mod of fa_fwd_mod in include/fa.h) change only
 // the exponent argument. ALiBi adds slope * (key - i') to the scaled score:
@@ -195,7 +197,7 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
 #pragma unroll
     for (int db = 0; db < ND; ++db) oacc[db] = f32x16{};
     float m = -INFINITY;   // the row's reference (base-2 units); -inf: none yet
-    float lh = 0.f;        // this lane half's weight sum
+    float lh = 0.f;        // this lane half's weight sum (16-bit inputs: a third of it)
     const float c2 = p.c;  // scale * log2(e): scores in base-2 units
 
     // ---- score modifiers, in base-2 units
@@ -218,9 +220,10 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
     // the largest bias (below), and the blocks before it may hold weights that
     // round to zero against it. A row's final sum is at least 1 against its
     // reference, so the residual pass then compares against max(lh, 1).
+    // res_floor is a third of that floor (lh is kept in thirds).
     const bool floor1 = (MOD == MOD_ALIBI) && slope2 != 0.f;
-    auto res_floor = [&]() __attribute__((always_inline)) { return floor1 ? fmaxf(lh, 1.f) : lh; };
-    // min(floor / 3, SUM_LIMIT): a block whose lane-half sum exceeds it takes the rare path
+    auto res_floor = [&]() __attribute__((always_inline)) { return floor1 ? fmaxf(lh, 1.f / 3.f) : lh; };
+    // min(res_floor, SUM_LIMIT): a block whose lane-half sum exceeds it takes the rare path
     float thr = floor1 ? (1.f / 3.f) : 0.f;
 
     // ---- K/V copies: lane l of a wave fills the l-th 16-byte slot of a 1 KiB
@@ -621,7 +624,7 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
                 redo(S2, j, edge, trig, pr, ts, P);
             }
             if constexpr (MODE != 2) {
-                const bool sr = ts * 3.f > res_floor();
+                const bool sr = ts > res_floor();
                 if (__builtin_amdgcn_ballot_w64(sr) != 0) {
                     i32x4 lo[2];
                     residual(pr, P, sr, lo);
@@ -634,8 +637,8 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
             residual(pr, P, true, lo);
             pv(va, lo);
         }
-        lh += ts;
-        thr = fminf(res_floor() * (1.f / 3.f), SUM_LIMIT);
+        lh = fmaf(ts, 1.f / 3.f, lh);
+        thr = fminf(res_floor(), SUM_LIMIT);
         pv(va, P);
     };
 
@@ -718,7 +721,7 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
 
     // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l); a split writes both
     // in fp32 to its slice of the workspace instead
-    const float lt = sum_halves(lh);
+    const float lt = FP8 ? sum_halves(lh) : sum_halves(lh) * 3.f;
     const int i = w0 + l32;
     if (p.n_split > 1) {
         const size_t sl = (size_t)bh * p.n_split + split;
