@@ -106,14 +106,20 @@ template <> struct Out<OUT_F32> {
 };
 template <> struct Out<OUT_BF16> {
     static constexpr int EB = 2;
+    __device__ static i32x2 pack4(float a, float b, float c, float d) {
+        return i32x2{pack2<IN_BF16>(a, b), pack2<IN_BF16>(c, d)};
+    }
     __device__ static void store4(uint8_t* dst, float a, float b, float c, float d) {
-        *reinterpret_cast<i32x2*>(dst) = i32x2{pack2<IN_BF16>(a, b), pack2<IN_BF16>(c, d)};
+        *reinterpret_cast<i32x2*>(dst) = pack4(a, b, c, d);
     }
 };
 template <> struct Out<OUT_F16> {
     static constexpr int EB = 2;
+    __device__ static i32x2 pack4(float a, float b, float c, float d) {
+        return i32x2{pack2<IN_F16>(a, b), pack2<IN_F16>(c, d)};
+    }
     __device__ static void store4(uint8_t* dst, float a, float b, float c, float d) {
-        *reinterpret_cast<i32x2*>(dst) = i32x2{pack2<IN_F16>(a, b), pack2<IN_F16>(c, d)};
+        *reinterpret_cast<i32x2*>(dst) = pack4(a, b, c, d);
     }
 };
 

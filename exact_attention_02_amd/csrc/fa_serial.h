@@ -749,15 +749,35 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
     if (i < w1) {
         const float inv = (lt > 0.f) ? p.out_mul / lt : 0.f;
         uint8_t* orow = op + (size_t)i * D * Out<OUT>::EB;
+        if constexpr (Out<OUT>::EB == 2) {
+            // 16-byte stores: element r of oacc[db] is column 32db + 8(r/4) +
+            // 4hh + r%4 of row i, so lanes l and l ^ 32 hold the two 4-column
+            // halves of each 8 columns. One exchange of 8 bytes gives lane hh
+            // the 8 columns 32db + 16k + 8hh .. +7 of each 16 (k = 0, 1).
 #pragma unroll
-        for (int db = 0; db < ND; ++db)
+            for (int db = 0; db < ND; ++db)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x16& a = oacc[db];
-                const int d = 32 * db + 8 * r4 + 4 * hh;
-                Out<OUT>::store4(orow + d * Out<OUT>::EB, a[4 * r4] * inv, a[4 * r4 + 1] * inv, a[4 * r4 + 2] * inv,
-                                 a[4 * r4 + 3] * inv);
-            }
+                for (int k = 0; k < 2; ++k) {
+                    const f32x16& a = oacc[db];
+                    const int ra = 8 * k, rb = 8 * k + 4;
+                    const i32x2 A = Out<OUT>::pack4(a[ra] * inv, a[ra + 1] * inv, a[ra + 2] * inv, a[ra + 3] * inv);
+                    const i32x2 B = Out<OUT>::pack4(a[rb] * inv, a[rb + 1] * inv, a[rb + 2] * inv, a[rb + 3] * inv);
+                    // lane hh = 0 takes the other half's A, lane hh = 1 the other half's B
+                    const int x0 = __shfl_xor(hh ? A[0] : B[0], 32), x1 = __shfl_xor(hh ? A[1] : B[1], 32);
+                    const i32x4 v = hh ? i32x4{x0, x1, B[0], B[1]} : i32x4{A[0], A[1], x0, x1};
+                    *reinterpret_cast<i32x4*>(orow + (32 * db + 16 * k + 8 * hh) * 2) = v;
+                }
+        } else {
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x16& a = oacc[db];
+                    const int d = 32 * db + 8 * r4 + 4 * hh;
+                    Out<OUT>::store4(orow + d * Out<OUT>::EB, a[4 * r4] * inv, a[4 * r4 + 1] * inv,
+                                     a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv);
+                }
+        }
         if (hh == 0) lp[i] = (lt > 0.f) ? (m + __builtin_amdgcn_logf(lt) - (FP8 ? LOG2_PRESCALE8 : 0.f)) * LN2 : -INFINITY;
     }
     clock_stamp(p.clk, p.clk_n, 1);
