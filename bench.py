@@ -271,6 +271,46 @@ def measured_clock_ghz(step, n_launches, n_wg):
     return clocks[len(clocks) // 2] if clocks else None
 
 
+def launch_trace(step, stream, n, w, in_t, out_t, n_splits):
+    """The first n launches of the process, one event pair each, with the
+    shader clock of each from the kernel's own telemetry (the clock records
+    of measured_clock_ghz). Under sustained load the part's power management
+    moves the clock over the first launches; this shows where and by how much."""
+    import torch
+    import exact_attention_02_amd as fa
+    dev = torch.device("cuda:0")
+    code = fa.dtype_code(in_t, out_t)
+    n_wg = max(1, 4 * fa.plan_grid(w.B, w.H, w.Nq, w.Nk, w.D, True, 0, code)[0] * max(1, n_splits))
+    buf = torch.zeros(n, 4 * n_wg, dtype=torch.int64, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    try:
+        for i in range(n):
+            st = fa.fa_set_clock_telemetry(buf[i].data_ptr(), n_wg)
+            if st != fa.FA_OK:
+                raise fa.FaError(st, "fa_set_clock_telemetry")
+            evs[i][0].record(stream)
+            step()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+    finally:
+        fa.fa_set_clock_telemetry(None, 0)
+    v = buf.view(n, n_wg, 4).cpu().double()
+    us, ghz = [], []
+    for i in range(n):
+        us.append(round(evs[i][0].elapsed_time(evs[i][1]) * 1000.0, 1))
+        cyc, ticks = (v[i, :, 2] - v[i, :, 0]).sum().item(), (v[i, :, 3] - v[i, :, 1]).sum().item()
+        ghz.append(round(cyc / ticks * 0.1, 3) if ticks > 0 else None)
+
+    def mean(a, b):
+        x = us[a:b]
+        return round(sum(x) / len(x), 1) if x else None
+    return {"workload": w.name, "launches": n, "us": us, "shader_ghz": ghz,
+            "mean_us": {"1-5": mean(0, 5), "6-25": mean(5, 25), "26-45": mean(25, 45), "46-": mean(45, n)},
+            "note": "launch i of a fresh process: HIP event pair on the launch stream; clock from the kernel's "
+                    "per-workgroup clock records (fa_set_clock_telemetry)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +325,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (to scale the FETCH_SIZE/WRITE_SIZE "
                          "counters of a profiler run)")
+    ap.add_argument("--launch-trace", type=int, default=0, metavar="N",
+                    help="instead of the bench line: time each of the first N launches of this process "
+                         "(an event pair each) with the shader clock each ran at, and print them (forward "
+                         "workloads)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 "
@@ -348,6 +392,10 @@ def main():
             fa.attention_bwd(q, k, v, o, lse, do_d, scale=w.scale, causal=w.causal,
                              window_left=w.window_left, window_right=w.window_right,
                              dq=dq, dk=dk, dv=dv, workspace=ws_b, stream=stream.cuda_stream, **bmod)
+
+    if args.launch_trace > 0 and not w.backward:
+        print(json.dumps(launch_trace(step, stream, args.launch_trace, w, q.dtype, out_t, n_splits)), flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

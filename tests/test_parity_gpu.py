@@ -840,15 +840,38 @@ def test_clock_telemetry_leaves_results_unchanged(din, D, kw):
 
 @pytest.mark.parametrize("B,H,Nq,Nk", [(1, 256, 300, 300), (2, 128, 257, 400), (1, 128, 520, 333)])
 @pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 100)])
-@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("f16", "f32")])
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("f16", "f32"), ("e4m3", "bf16")])
 def test_eight_wave_workgroups_at_d128(B, H, Nq, Nk, causal, window, din, dout):
     # D = 128 grids that give every CU a workgroup of 256 query rows run the
     # serial kernel with eight waves (mirrored row blocks); ragged last tiles.
-    code = fa.dtype_code({"bf16": torch.bfloat16, "f16": torch.float16}[din], OUT_T[dout])
+    code = fa.FA_E4M3 if din == "e4m3" else fa.dtype_code({"bf16": torch.bfloat16, "f16": torch.float16}[din],
+                                                           OUT_T[dout])
     assert fa.plan_grid(B, H, Nq, Nk, 128, causal, window, code)[1] == 256
     w = synth.small_workload(f"nw8_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}_{din}_{dout}", B, H, Nq, Nk, 128,
                              causal, window, din, dout, 7000 + B + H + Nq + Nk + window)
     inp = synth.make_inputs(w)
+    o, lse = run_gpu(w, inp)
+    Oref, Lref = reference(w, inp)
+    compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", [(1, 128, 300, 517), (2, 64, 260, 640)])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 150)])
+@pytest.mark.parametrize("ramp", [0.0, 4.0])
+def test_e4m3_eight_waves_reference_moves(B, H, Nq, Nk, causal, window, ramp):
+    # Eight-wave e4m3 workgroups (mirrored row blocks) on inputs whose row max
+    # keeps rising (outliers, and keys whose norm grows along the sequence), so
+    # that the reference moves within tiles of every wave.
+    assert fa.plan_grid(B, H, Nq, Nk, 128, causal, window, fa.FA_E4M3)[1] == 256
+    seed = 7700 + B * 7 + H * 13 + Nq * 3 + Nk + (17 if causal else 0) + window + int(ramp)
+    w = synth.small_workload(f"e4m3_nw8_moves_B{B}H{H}q{Nq}k{Nk}c{int(causal)}w{window}r{ramp}", B, H, Nq, Nk, 128,
+                             causal, window, "e4m3", "bf16", seed, outlier_frac=0.002, outlier_mult=12.0)
+    inp = synth.make_inputs(w)
+    if ramp > 0.0:
+        kf = inp.k.to(torch.float32)
+        g = 1.0 + ramp * torch.arange(Nk, dtype=torch.float32).view(1, 1, Nk, 1) / Nk
+        k8 = (kf * g).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        inp = synth.Inputs(inp.q, k8, inp.v, inp.descale_q, inp.descale_k, inp.descale_v)
     o, lse = run_gpu(w, inp)
     Oref, Lref = reference(w, inp)
     compare(w, o.double().cpu(), lse.double().cpu(), Oref, Lref, w.name)
