@@ -53,6 +53,12 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+    # torch's ROCm build carries its own HIP runtime under a file name other
+    # than ROCm's. Loaded first, libfa.so would bring in ROCm's runtime, and
+    # torch would then load its own beside it: two runtimes in one process, and
+    # the library's calls would not see the device and streams torch set up.
+    # With torch loaded first, libfa.so's libamdhip64.so.7 resolves to torch's.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I, F, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
     pI, pLL = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_longlong)
