@@ -463,12 +463,21 @@ def main():
     }
     if clock is not None:
         peak_at_clock = peak * clock / 2.4
+        # A launch takes the same number of shader cycles whatever the clock
+        # (--launch-trace), so the timed region's mean clock follows from the
+        # cycles of a launch after it and the timed mean duration.
+        timed_ghz = clock * res["per_launch_ms"]["median"] / ms
         res["clock"] = {"shader_ghz": round(clock, 3), "nominal_ghz": 2.4,
                         "peak_at_clock": round(peak_at_clock, 1),
                         "frac_at_clock": round(tflops / peak_at_clock, 4),
                         "note": "median over launches after the timed region; each launch's workgroups record "
                                 "the shader-clock and 100 MHz counters at their start and end "
-                                "(fa_set_clock_telemetry)"}
+                                "(fa_set_clock_telemetry)",
+                        "timed_region_ghz_est": round(timed_ghz, 3),
+                        "frac_at_timed_region_clock_est": round(tflops / (peak * timed_ghz / 2.4), 4),
+                        "timed_region_note": "shader_ghz x the per-launch median duration / ms_per_step: the "
+                                             "cycles of one launch after the timed region over the timed "
+                                             "region's mean launch time"}
     if w.splitkv:
         # A decode step reads the whole K/V once for a handful of queries: HBM
         # bound. The time covers both kernels of the call (splits and merge).
