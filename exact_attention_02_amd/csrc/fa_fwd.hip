@@ -481,7 +481,7 @@ Plan make_plan(int in, int out, int D, int B, int H, int Nq, int mod, bool split
     if (kernel == KERNEL_SERIAL) {
         pl.nw = D == 64 ? FA_SR_NW_D64 : FA_SR_NW_D128;
         if (pl.nw == 8 && n_bh * ((Nq + 255) / 256) < 256) pl.nw = 4;
-        pl.bc = serial_tile_keys(pl.nw, D == 64 ? FA_SR_TK_D64 : FA_SR_TK_D128);
+        pl.bc = serial_tile_keys(in, D, pl.nw);
     }
     pl.qb = qb;
     pl.br = pl.nw * 32 * qb;

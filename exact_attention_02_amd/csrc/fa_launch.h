@@ -134,8 +134,17 @@ int knob(int which);
 #ifndef FA_SR_TK_D128
 #define FA_SR_TK_D128 64
 #endif
+// e4m3 inputs at D = 128 with eight waves: keys per tile.
+#ifndef FA_SR_TK_E4M3_D128
+#define FA_SR_TK_E4M3_D128 128
+#endif
 // Keys per tile a serial-kernel plan takes for nw waves and tile size tk.
 constexpr int serial_tile_keys(int nw, int tk) { return (nw == 8 && tk == 128) ? 128 : 64; }
+// ... for input type in (InKind) at head size D.
+constexpr int serial_tile_keys(int in, int D, int nw) {
+    return serial_tile_keys(nw, in == IN_E4M3 && D == 128 ? FA_SR_TK_E4M3_D128
+                                                                  : (D == 64 ? FA_SR_TK_D64 : FA_SR_TK_D128));
+}
 
 // Picks the tile shape for a problem. Pure host arithmetic.
 // mod != MOD_NONE needs the serial or the pipelined kernel, the ones with

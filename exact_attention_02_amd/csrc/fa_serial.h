@@ -129,7 +129,7 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
     constexpr int VCPR = VRB / 16;         // 16-byte chunks per LDS V row
     static_assert(RB == 128 || RB == 256, "row size");
     static_assert(TK == 64 || TK == 128, "keys per tile");
-    static_assert(!FP8 || (TK == 64 && MOD == MOD_NONE), "e4m3: 64-key tiles, no score modifier");
+    static_assert(!FP8 || MOD == MOD_NONE, "e4m3: no score modifier");
     constexpr int SUB = TK / 32;           // 32-key blocks per tile
     constexpr int KTILE = TK * RB;         // bytes of one K tile in LDS
     constexpr int VTILE = TK * VRB;        // bytes of one V tile in LDS
@@ -275,8 +275,11 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
 #pragma unroll
             for (int i = 0; i < NDMA; ++i) {
                 const int run = 64 * wave + NT * i;
-                const int xv0 = i * (NT / VCPR);   // multiple of 32: keys move by xv0 / 8
-                const unsigned soff = (unsigned)((t * TK + (xv0 >> 3)) * VRB);
+                // copy i fills LDS rows xv0 + (0 .. NT / VCPR - 1), xv0 a
+                // multiple of 32: whole 64-key groups move the keys by 64 each,
+                // and 32 rows within a group by 4 (v8_row_inv)
+                const int xv0 = i * (NT / VCPR);
+                const unsigned soff = (unsigned)((t * TK + ((xv0 >> 6) << 6) + (((xv0 >> 5) & 1) << 2)) * VRB);
                 dma16(vwords, kb + KTILE + run * 16, dma_voff8, soff);
             }
         }
@@ -384,9 +387,9 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
     // of pf holds the e4m3 weights of sub-tile w/4, accumulator elements
     // 4(w%4) .. +3, and the V^T operand comes from four 8-bit transposing
     // reads of the lane half's 32 (permuted) rows.
-    auto pv8 = [&](auto par, const i32x8& pf) __attribute__((always_inline)) {
+    auto pv8 = [&](auto par, int grp, const i32x8& pf) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par)::value;
-        const lds_u8* vb = lds0 + PAR * SLOT + KTILE;
+        const lds_u8* vb = lds0 + PAR * SLOT + KTILE + 64 * grp * VRB;
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
             i32x8 a;
@@ -596,14 +599,14 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
             // the redo does not form them again)
             const bool trig = !(ts <= SUM_LIMIT8);
             if (__builtin_amdgcn_ballot_w64(trig) != 0) {
-                if (jj == 1) {
-                    pv8(par, i32x8{pf8[0], pf8[1], pf8[2], pf8[3], 0, 0, 0, 0});
+                if (jj & 1) {
+                    pv8(par, jj >> 1, i32x8{pf8[0], pf8[1], pf8[2], pf8[3], 0, 0, 0, 0});
                     pf8[0] = pf8[1] = pf8[2] = pf8[3] = 0;
                 }
                 redo(S, j, edge, trig, pr, ts, P);
             }
 #pragma unroll
-            for (int w = 0; w < 4; ++w) pf8[4 * jj + w] = P[0][w];
+            for (int w = 0; w < 4; ++w) pf8[4 * (jj & 1) + w] = P[0][w];
             lh += ts;
             return;
         }
@@ -654,9 +657,18 @@ __device__ __forceinline__ void serial_body(const Params& p, uint8_t* smem, int 
             live8 = false;
         }
 #pragma unroll
-        for (int jj = 0; jj < SUB; ++jj) block(par, mode, jj, SUB * t + jj);
+        for (int jj = 0; jj < SUB; ++jj) {
+            block(par, mode, jj, SUB * t + jj);
+            if constexpr (FP8) {
+                // P.V of each 64-key group once both its sub-tiles have weights
+                if (jj & 1) {
+                    if (live8) pv8(par, jj >> 1, pf8);
+                    pf8 = i32x8{};
+                    live8 = false;
+                }
+            }
+        }
         if constexpr (FP8) {
-            if (live8) pv8(par, pf8);
             if (t + 1 < t_hi) finish_tile(t + 1);
         }
     };
@@ -843,7 +855,7 @@ static int launch_serial_one(const Plan& pl, const Params& p, hipStream_t s) {
 template <int IN, int OUT, int D, int MOD>
 static int launch_serial_d(const Plan& pl, const Params& p, hipStream_t s) {
     constexpr int NWD = D == 64 ? FA_SR_NW_D64 : FA_SR_NW_D128;
-    constexpr int TKD = serial_tile_keys(NWD, D == 64 ? FA_SR_TK_D64 : FA_SR_TK_D128);
+    constexpr int TKD = serial_tile_keys(IN, D, NWD);
     if (pl.nw == NWD && pl.bc == TKD) return launch_serial_one<IN, OUT, D, NWD, TKD, MOD>(pl, p, s);
     if constexpr (NWD == 8) {
         if (pl.nw == 4 && pl.bc == 64) return launch_serial_one<IN, OUT, D, 4, 64, MOD>(pl, p, s);
